@@ -1,0 +1,243 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the decode hot path over one batch: scatter the step's
+new K/V tokens into the block pool (pa_reshape_and_cache), then paged decode
+attention over every sequence's full context (pa_decode, with automatic
+split-K).  The default workload is one Llama-3.1-8B-shaped layer: 64
+sequences, context lengths U[128, 4096], 32 q / 8 kv heads, head_dim 128,
+bf16, 16-token blocks shuffled over a pool 1.25x the need.  All inputs are
+seeded synthetic data resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is KV GB/s over the timed steps (the K/V
+bytes attention must read, one read per kv head, divided by step time);
+tokens/s and the HBM fraction are reported beside it.  ``roofline`` refers
+to the decode call (partition kernel + split-K merge), timed with HIP events
+on the launch stream.  ``cpu_baseline`` times the fp64 CPU oracle on a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: KV GB/s and % of MI355X HBM peak; decode tokens/s"
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+WORKLOADS = {
+    "llama3_8b_b64": 2,
+    "llama2_70b_b256": 3,
+    "shared_prefix_32x4": 4,
+    "long_mixed_decode": 5,
+    "tiny_f32": 1,
+}
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_{name}_pmc.json")
+
+
+def _source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "pa_device.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_396_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(name, decode_launch_bytes):
+    """HBM bytes per decode call from committed rocprofv3 counter runs, if
+    they were taken on the current decode source; else None."""
+    path = PMC_SUMMARY.format(name=name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != _source_hash():
+        return None
+    return d.get("hbm_bytes_per_call")
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """The oracle, untouched, on the host: whole batches until ``budget_s``."""
+    import oracle
+    from workloads import poison_bits
+
+    try:
+        from threadpoolctl import threadpool_limits
+
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    pk = oracle.new_pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype, poison_bits(wl.dtype))
+    pv = pk.copy()
+    oracle.reshape_and_cache_fast(pk, pv, wl.hist_k, wl.hist_v, wl.hist_slots)
+    oracle.reshape_and_cache_fast(pk, pv, wl.new_k, wl.new_v, wl.new_slots)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.decode(wl.q, pk, pv, wl.block_tables, wl.context_lens, wl.scale, wl.dtype)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {
+        "value": round(wl.kv_bytes * n / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n} full decode batch(es) of {wl.name} ({wl.num_seqs} seqs, "
+                  f"{int(wl.context_lens.sum())} tokens) in {el:.1f} s, numpy fp64, BLAS 1 thread",
+        "tokens_per_s": round(wl.num_seqs * n / el, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_b64", choices=sorted(WORKLOADS))
+    ap.add_argument("--partition", type=int, default=0, help="0 auto, <0 no split, >0 tokens")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calib-copy", type=int, default=0,
+                    help="instead of the bench, run N plain 1 GiB device copies (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the paged-attention path has no multi-GPU part in this library)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_396_amd as pa
+    from workloads import make_decode
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import GpuPool, to_dev  # noqa: E402
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calib_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(args.calib_copy):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "copies": args.calib_copy}))
+        return
+
+    cfg = WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    wl = make_decode(cfg)
+    print(f"[bench] workload {args.workload}: {wl.num_seqs} seqs, ctx sum {int(wl.context_lens.sum())}, "
+          f"generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    pool = GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
+    pool.write(wl.hist_k, wl.hist_v, wl.hist_slots)
+    new_k = to_dev(wl.new_k, wl.dtype)
+    new_v = to_dev(wl.new_v, wl.dtype)
+    new_slots = torch.from_numpy(wl.new_slots).to(dev)
+    q = to_dev(wl.q, wl.dtype)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    S, Hq, D = wl.q.shape
+    max_ctx = int(wl.context_lens.max())
+    part = pa.pa_decode_partition_size(S, wl.num_kv_heads, max_ctx, args.partition)
+    ws_bytes = pa.pa_decode_workspace_bytes(S, Hq, wl.num_kv_heads, D, max_ctx, args.partition)
+    ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        pa.pa_reshape_and_cache(new_k, new_v, new_slots, pool.k, pool.v, pool.desc)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_decode(out, q, pool.k, pool.v, bt, cl, max_ctx, float(wl.scale), pool.desc,
+                     partition_size=args.partition, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    kv = wl.kv_bytes
+    value = kv / (ms_step * 1e-3) / 1e9
+    achieved = kv / (dec_avg_ms * 1e-3) / 1e9
+    traffic = _traffic(args.workload, kv)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": wl.num_kv_heads, "head_dim": D,
+            "block_size": 16, "context_lens": "U[128,4096]" if cfg == 2 else "per config",
+            "ctx_sum": int(wl.context_lens.sum()), "num_blocks": wl.num_blocks,
+            "partition_tokens": part, "new_tokens_per_step": int(len(wl.new_slots)),
+            "parallelism": "single GPU",
+        },
+        "tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": kv,
+        "decode_call_ms": round(dec_avg_ms, 5),
+        "wall_s": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * pa.h — C ABI of the MI355X (gfx950) paged-attention library libpa.so.
+ *
+ * The library implements the data-parallel hot path of PagedAttention as the
+ * pages describe it:
+ *   - the KV cache is cut into fixed blocks of 16 tokens that need not be
+ *     contiguous, and a per-sequence block table maps logical to physical
+ *     blocks ("vLLM: from PagedAttention to Speculative Decoding", 3.2;
+ *     zihan-zhang.net vLLM study, 3.2);
+ *   - kernels reach the scattered blocks through block_table (reads) and
+ *     slot_mapping (writes); logical token i is in block block_table[i / 16]
+ *     at offset i % 16 ("vLLM: from PagedAttention ...", 3.3);
+ *   - attention is softmax(Q K^T / sqrt(d)) V under a causal mask
+ *     (zihan-zhang.net vLLM study, 1.1.1), evaluated block by block with the
+ *     online-softmax rescaling of FlashAttention (same page, 4.3.1).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers.  The caller owns every buffer;
+ *     the library never allocates, frees or synchronizes.  Work is enqueued
+ *     on `stream` (a hipStream_t, NULL = the null stream) and the call returns
+ *     before the GPU finishes.
+ *   - q, k, v and out are dense row-major [tokens][heads][head_dim] in the
+ *     cache dtype (fp32 or bf16); out has the dtype of q.
+ *   - Block tables are int32 [rows][max_blocks_per_seq]; entries past a
+ *     sequence's ceil(len / 16) blocks are never read.
+ *   - Argument errors detected on the host return a negative pa_status and
+ *     launch nothing; pa_last_error() then holds a description (per thread).
+ *   - Values that live on the device (slots, block ids, lengths) are not
+ *     checked on the host.  Kernels ignore slots outside the pool, treat
+ *     block ids outside [0, num_blocks) as empty blocks and clamp lengths to
+ *     what the table row and max_context_len cover, so a bad value gives a
+ *     wrong result but never touches memory outside the caller's buffers.
+ *
+ * Pool layout (owned by the library; size it with pa_cache_bytes):
+ *   K pool element (block b, kv head g, token offset o, dim x) at element index
+ *       ((b * Hkv + g) * 16 + o) * D + x
+ *   V pool element (b, g, o, x) at element index
+ *       (((b * Hkv + g) * 8 + o / 2) * D + x) * 2 + o % 2
+ *   i.e. every (block, kv head) tile is one contiguous run (4 KiB for bf16
+ *   with D = 128); K rows are token-major, V stores two consecutive tokens of
+ *   one dim side by side.  The pages print three different block-internal
+ *   orders; this one is chosen for full 128-byte reads on gfx950.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+#define PA_BLOCK_SIZE 16
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+  PA_ERR_DTYPE = -3,       /* unknown dtype */
+  PA_ERR_UNSUPPORTED = -4, /* valid but not built: head_dim, GQA group, block size */
+  PA_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  PA_ERR_OVERFLOW = -6,    /* a size product does not fit the index types */
+  PA_ERR_HIP = -7          /* the HIP runtime reported an error */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Describes one layer's K and V pools (both have the same shape). */
+typedef struct {
+  int32_t num_blocks;   /* physical blocks in the pool, >= 1 */
+  int32_t block_size;   /* must be PA_BLOCK_SIZE (16) */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t dtype;        /* a pa_dtype */
+} pa_cache_desc;
+
+/* PA_ABI_VERSION of the built library. */
+int pa_abi_version(void);
+
+/* Bytes of ONE pool (K or V) for `desc`; 0 if desc is invalid. */
+size_t pa_cache_bytes(const pa_cache_desc* desc);
+
+/*
+ * pa_reshape_and_cache — scatter new K/V rows into the pools
+ * ("vLLM: from PagedAttention ...", 3.3: kernels address scattered blocks
+ * through slot_mapping).
+ *
+ *   k, v          device, [num_tokens][Hkv][D] in the cache dtype
+ *   slot_mapping  device int64 [num_tokens]; token i goes to block
+ *                 slot / 16, offset slot % 16.  A negative slot marks a
+ *                 padding token and writes nothing.  Slots at or beyond
+ *                 num_blocks * 16 are ignored.  Two tokens with the same slot
+ *                 in one call give an unspecified winner.
+ *   k_cache, v_cache  device pools laid out as described above.
+ * The copy is bit-exact (no value conversion).  num_tokens == 0 is a no-op.
+ */
+int pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
+                         int32_t num_tokens, void* k_cache, void* v_cache,
+                         const pa_cache_desc* desc, void* stream);
+
+/*
+ * Partition size pa_decode uses for `partition_size_request`
+ * (0 = automatic, < 0 = one partition per sequence, > 0 = that many tokens,
+ * a multiple of 16).  Returns the resolved size in tokens, or a negative
+ * pa_status.  The automatic choice depends on the current device's compute
+ * unit count and on the shape.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                 int32_t partition_size_request);
+
+/*
+ * Workspace bytes pa_decode needs for these sizes and this partition request
+ * (the same request later passed to pa_decode).  0 means no workspace is
+ * needed (every sequence fits one partition).
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size_request);
+
+/*
+ * pa_decode — one query token per sequence attends to its whole paged context
+ * (zihan-zhang.net vLLM study, 1.1.1 and 3.2: per block, look up the physical
+ * block, score the 16 keys, then weight the 16 values; 4.3.1: online softmax).
+ *
+ *   out            device [num_seqs][num_q_heads][D], dtype of the cache
+ *   q              device [num_seqs][num_q_heads][D]
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens   device int32 [num_seqs]; counts the newest token, whose K/V
+ *                  must already be in the pools (write it with
+ *                  pa_reshape_and_cache earlier on the same stream).  A length
+ *                  of 0 yields a zero output row.
+ *   max_context_len  host bound on every context_lens entry (sizes the grid)
+ *   scale          multiplies Q.K (normally 1/sqrt(D)), fp32
+ *   partition_size 0 = automatic split-K, < 0 = no split, > 0 = tokens per
+ *                  partition (multiple of 16).  Long contexts are split into
+ *                  partitions whose partial softmax states are merged by a
+ *                  second kernel with the same rescaling identity.
+ *   workspace      device scratch of pa_decode_workspace_bytes(...) bytes
+ *                  (may be NULL when that is 0).  Contents need no
+ *                  initialisation and are overwritten.
+ * Query head h reads kv head h / (num_q_heads / Hkv).  Supported:
+ * D in {64, 128}, num_q_heads / Hkv in {1, 2, 4, 8}.  Accumulation is fp32.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+              int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
+              size_t workspace_bytes, const pa_cache_desc* desc, void* stream);
+
+/*
+ * pa_prefill_chunk — causal attention of query chunks against paged KV
+ * (zihan-zhang.net vLLM study, 3.5: a long prompt is processed chunk by chunk;
+ * batch metadata flattens all requests' tokens into one launch).
+ *
+ *   q, out           device [total_q_tokens][num_q_heads][D] (bf16 only)
+ *   query_start_loc  device int32 [num_reqs + 1]; request r owns query rows
+ *                    query_start_loc[r] .. query_start_loc[r+1]-1 (n_r rows)
+ *   context_lens     device int32 [num_reqs]; ctx_r counts the chunk, whose
+ *                    K/V must already be in the pools.  Query i of request r
+ *                    sits at position ctx_r - n_r + i and sees keys 0..that
+ *                    position.
+ *   block_tables     device int32 [num_reqs][max_blocks_per_seq]
+ *   max_q_len        host bound on every n_r (sizes the grid)
+ * Uses bf16 MFMA for Q K^T and P V with fp32 accumulation and an fp32
+ * online-softmax state; P is rounded to bf16 before the P V product.
+ */
+int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* query_start_loc, const int32_t* context_lens,
+                     int32_t num_reqs, int32_t total_q_tokens, int32_t max_q_len,
+                     int32_t num_q_heads, float scale, const pa_cache_desc* desc, void* stream);
+
+/* Static description of a status code. */
+const char* pa_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

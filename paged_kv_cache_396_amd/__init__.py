@@ -1,0 +1,20 @@
+"""MI355X (gfx950) paged KV-cache attention: cache writes, paged decode with
+split-K, and chunked prefill, as hand-written HIP kernels behind a C ABI
+(``include/pa.h``).  This package holds the kernels' sources (``csrc/``), the
+build step and a ctypes binding; torch supplies device memory and streams."""
+
+from .binding import (  # noqa: F401
+    BLOCK_SIZE,
+    PA_BF16,
+    PA_F32,
+    CacheDesc,
+    PAError,
+    cache_desc,
+    lib,
+    pa_cache_bytes,
+    pa_decode,
+    pa_decode_partition_size,
+    pa_decode_workspace_bytes,
+    pa_prefill_chunk,
+    pa_reshape_and_cache,
+)

@@ -1,0 +1,189 @@
+"""Thin ctypes binding over libpa.so.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Torch tensors supply device memory and the current HIP stream; the
+functions keep the C names (``pa_reshape_and_cache``, ``pa_decode``,
+``pa_prefill_chunk``) and raise ``PAError`` on a non-zero status.
+
+The library must have been built (``python -m paged_kv_cache_396_amd.build``);
+loading fails loudly otherwise.  There is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpa.so")
+
+PA_F32 = 0
+PA_BF16 = 1
+BLOCK_SIZE = 16
+
+_STATUS = {
+    0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
+    -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_OVERFLOW", -7: "PA_ERR_HIP",
+}
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libpa.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_396_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32, f32, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        D = ctypes.POINTER(CacheDesc)
+        L.pa_abi_version.restype = ctypes.c_int
+        L.pa_cache_bytes.argtypes = [D]
+        L.pa_cache_bytes.restype = sz
+        L.pa_reshape_and_cache.argtypes = [P, P, P, i32, P, P, D, P]
+        L.pa_reshape_and_cache.restype = ctypes.c_int
+        L.pa_decode_partition_size.argtypes = [i32, i32, i32, i32]
+        L.pa_decode_partition_size.restype = i32
+        L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.pa_decode_workspace_bytes.restype = sz
+        L.pa_decode.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, f32, i32, P, sz, D, P]
+        L.pa_decode.restype = ctypes.c_int
+        L.pa_prefill_chunk.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, i32, f32, D, P]
+        L.pa_prefill_chunk.restype = ctypes.c_int
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PAError(status, lib().pa_last_error().decode())
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def dtype_code(torch_dtype) -> int:
+    torch = _torch()
+    if torch_dtype == torch.bfloat16:
+        return PA_BF16
+    if torch_dtype == torch.float32:
+        return PA_F32
+    raise ValueError(f"unsupported dtype {torch_dtype}")
+
+
+def cache_desc(num_blocks: int, num_kv_heads: int, head_dim: int, dtype) -> CacheDesc:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return CacheDesc(num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, code)
+
+
+def pa_cache_bytes(desc: CacheDesc) -> int:
+    return int(lib().pa_cache_bytes(ctypes.byref(desc)))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pa_reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, desc: CacheDesc, stream=None):
+    """Scatter ``k``/``v`` [T, Hkv, D] into the pools at ``slot_mapping`` (int64 [T])."""
+    torch = _torch()
+    for t, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _dev(t, n)
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    T = slot_mapping.shape[0]
+    _check(lib().pa_reshape_and_cache(_ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache),
+                                      _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
+
+
+def pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, partition_size=0) -> int:
+    r = int(lib().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, partition_size))
+    if r < 0:
+        _check(r)
+    return r
+
+
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                              partition_size=0) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               max_context_len, partition_size))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+              scale: float, desc: CacheDesc, partition_size: int = 0, workspace=None, stream=None):
+    """Paged decode attention; ``out``/``q`` are [S, Hq, D]; tables int32 [S, MB]."""
+    torch = _torch()
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _dev(t, n)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    S, Hq, _ = q.shape
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                           block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq,
+                           float(scale), int(partition_size), _ptr(workspace), ws_bytes,
+                           ctypes.byref(desc), _stream(stream)))
+
+
+def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                     max_q_len: int, scale: float, desc: CacheDesc, stream=None):
+    """Causal chunk attention; ``q``/``out`` are [total_q, Hq, D] (bf16)."""
+    torch = _torch()
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_tables, "block_tables"), (query_start_loc, "query_start_loc"),
+                 (context_lens, "context_lens")):
+        _dev(t, n)
+    for t, n in ((block_tables, "block_tables"), (query_start_loc, "query_start_loc"),
+                 (context_lens, "context_lens")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{n} must be int32")
+    Tq, Hq, _ = q.shape
+    R = context_lens.shape[0]
+    _check(lib().pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(block_tables), block_tables.shape[1], _ptr(query_start_loc),
+                                  _ptr(context_lens), R, Tq, int(max_q_len), Hq, float(scale),
+                                  ctypes.byref(desc), _stream(stream)))

@@ -1,0 +1,550 @@
+// Paged decode attention for gfx950 (one query token per sequence).
+//
+// What is computed: for every sequence s and query head h,
+//   out[s,h] = softmax(scale * K_s q_{s,h}) V_s
+// over the sequence's ctx_s cached tokens, where K_s/V_s are read block by
+// block through the block table (zihan-zhang.net vLLM study, 3.2: per block,
+// look up the physical block, score its 16 keys, then weight its 16 values;
+// 1.1.1 for the attention formula) and the softmax is evaluated online
+// (same page, 4.3.1: keep a running max m and sum l, rescale the running
+// output by exp(m_old - m_new) when m grows, divide by l at the end).
+//
+// Mapping onto CDNA4:
+//  * one workgroup (4 waves) per (sequence, kv head, partition); a partition
+//    is a run of consecutive 16-token blocks.  The G = Hq/Hkv query heads of
+//    the kv head share every K/V byte read (GQA).
+//  * wave w takes blocks w, w+4, ... of the partition.  A (block, kv head)
+//    tile of K is one contiguous 16*D run; each load instruction reads whole
+//    128-byte lines.  The next block's K and V are loaded into registers
+//    before the current block is computed.
+//  * Q.K: a K row is spread over LPR lanes; every lane forms partial dots for
+//    its rows and all G heads (bf16 dot2, fp32 accumulate), then a
+//    reduce-scatter over the LPR lanes (DPP mirrors and quad permutes) leaves
+//    each lane with complete scores for one head and one or two tokens.
+//  * softmax: scores are kept in the log2 domain.  The running max is only
+//    raised when some score exceeds it by more than 2^8, which after the first
+//    block is rare; the rescale is exact whenever it happens, so the result
+//    is the same softmax (the reference max only has to be common to all
+//    terms that are summed together).
+//  * P.V: probabilities go through LDS as bf16 pairs of consecutive tokens;
+//    V stores token pairs side by side, so each lane does bf16 dot2 over the
+//    pair for its 4 dims and all G heads, accumulating fp32.
+//  * the 4 waves merge their (m, l, O) in LDS with the same rescale.  With
+//    one partition the workgroup writes the output; otherwise it writes its
+//    partial state and decode_reduce merges the partitions.
+#include <float.h>
+
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+constexpr int kDecodeWaves = 4;
+constexpr float kRescaleGap = 8.0f;   // log2 units: p may reach 2^8 before a rescale
+constexpr float kNegBig = -FLT_MAX;   // "no score yet"; keeps exp2 of differences finite
+
+template <int EB, int D, int G>
+struct DecodeCfg {
+  static constexpr int RB = D * EB;                  // bytes of one K row
+  static constexpr int LPR = RB >= 256 ? 16 : 8;     // lanes per K row
+  static constexpr int U = RB / 16 / LPR;            // 16-byte chunks per lane per row
+  static constexpr int NR = LPR / 4;                 // K rows per lane per tile
+  static constexpr int EPC = 16 / EB;                // elements per 16-byte chunk
+  static constexpr int N0 = NR * G;                  // partial dots per lane
+  static constexpr int LOGL = ilog2(LPR);
+  static constexpr int HALV = cmin(LOGL, ilog2(N0)); // halving steps of the reduce-scatter
+  static constexpr int AR = LOGL - HALV;             // trailing all-reduce steps
+  static constexpr int NF = N0 >> HALV;              // complete scores per lane
+  static constexpr int HEAD_SPAN = NR / NF;          // lanes (after AR) sharing one head
+  static constexpr int HEAD_BITS = (HEAD_SPAN - 1) << AR;
+  static constexpr int DUP_BITS = (1 << AR) - 1;     // lanes holding identical scores
+  static constexpr int ROW_BITS = (kWave - 1) & ~(LPR - 1);
+  // V: 8 pair-rows of 2*RB bytes per tile
+  static constexpr int VCH = 2 * RB / 16;            // chunks per pair-row
+  static constexpr int VL = VCH < kWave ? VCH : kWave;  // lanes per pair-row
+  static constexpr int NPV = 8 * VL / kWave;         // pair-rows per lane
+  static constexpr int XPC = 16 / (2 * EB);          // dims per chunk
+  static constexpr int VGRP_BITS = (kWave - 1) & ~(VL - 1);
+  static constexpr int PWORDS = EB == 2 ? 1 : 2;     // 32-bit words per (pair, head) of P
+  static_assert(NF <= 2 && NF <= NR, "unsupported GQA group for this head size");
+  static_assert(VCH % VL == 0 && VCH / VL == 1, "V chunk mapping");
+};
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const char* k_cache;
+  const char* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int max_blocks_per_seq;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int num_blocks;
+  int num_partitions;
+  int partition_blocks;
+  float scale_log2;
+};
+
+// Context length actually processed: bounded by the table row and the grid.
+__device__ inline int clamp_ctx(int ctx, const DecodeParams& p) {
+  long cap = (long)p.max_blocks_per_seq * kBlock;
+  const long grid_cap = (long)p.num_partitions * p.partition_blocks * kBlock;
+  if (grid_cap < cap) cap = grid_cap;
+  if (ctx < 0) ctx = 0;
+  return ctx > cap ? (int)cap : ctx;
+}
+
+// Reduce-scatter of L partial dots over the LPR lanes of a K row.  Step k
+// pairs lanes through a mask whose highest set bit is (LPR >> (k+1)); the
+// lane with that bit set keeps the upper half of the values.  After log2 L
+// halvings (capped at log2 LPR) the lane with row index c holds the complete
+// sums for values c*NF .. c*NF+NF-1; any remaining steps sum over the low
+// lane bits (those lanes then hold identical values).
+template <int LPR, int L>
+__device__ inline void reduce_scatter_lpr(float (&v)[L], int c) {
+  constexpr int LOGL = ilog2(LPR);
+  constexpr int HALV = cmin(LOGL, ilog2(L));
+  // masks per step for a 16-lane row: 15 (row_mirror), 7 (half mirror), 2, 1;
+  // for an 8-lane row: 7, 2, 1.
+  auto step = [&](auto kconst) {
+    constexpr int k = decltype(kconst)::value;
+    constexpr int bit = LPR >> (k + 1);
+    constexpr int mask = (LPR == 16) ? (k == 0 ? 15 : k == 1 ? 7 : k == 2 ? 2 : 1)
+                                     : (k == 0 ? 7 : k == 1 ? 2 : 1);
+    if constexpr (k < HALV) {
+      constexpr int n = L >> k;
+      const bool upper = (c & bit) != 0;
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) {
+        const float a = v[i];
+        const float b = v[i + n / 2];
+        const float keep = upper ? b : a;
+        const float send = upper ? a : b;
+        v[i] = keep + xor_lane<mask>(send);
+      }
+    } else {
+      v[0] = v[0] + xor_lane<mask>(v[0]);
+    }
+  };
+  step(std::integral_constant<int, 0>{});
+  step(std::integral_constant<int, 1>{});
+  step(std::integral_constant<int, 2>{});
+  if constexpr (LOGL == 4) step(std::integral_constant<int, 3>{});
+}
+
+
+template <int EB, int D, int G>
+__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(DecodeParams p) {
+  using C = DecodeCfg<EB, D, G>;
+  constexpr int NW = kDecodeWaves;
+
+  __shared__ __attribute__((aligned(16))) uint32_t pbuf[NW][8 * G * C::PWORDS];
+  __shared__ float sm[NW][G];
+  __shared__ float sl[NW][G];
+  __shared__ __attribute__((aligned(16))) float so[NW][G][D];
+
+  const int bid = blockIdx.x;
+  const int g = bid % p.num_kv_heads;
+  const int s = (bid / p.num_kv_heads) % p.num_seqs;
+  const int part = bid / (p.num_kv_heads * p.num_seqs);
+
+  const int ctx = clamp_ctx(p.context_lens[s], p);
+  const int nblk = (ctx + kBlock - 1) / kBlock;
+  const int nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  if (part >= nparts) return;  // uniform over the workgroup
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int c = lane & (C::LPR - 1);  // lane within its K row
+  const int r = lane / C::LPR;        // row group
+  const int vgrp = lane / C::VL;      // V pair-row group
+  const int xc = lane & (C::VL - 1);  // V chunk within a pair-row
+
+  const int b0 = part * p.partition_blocks;
+  const int b1 = min(nblk, b0 + p.partition_blocks);
+
+  // ---- q chunks for the G heads of this kv head: [G][U] x 16 bytes
+  uint4 qv[G][C::U];
+  {
+    const char* qbase = (const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::RB;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int u = 0; u < C::U; ++u)
+        qv[h][u] = *(const uint4*)(qbase + (int64_t)h * C::RB + (u * C::LPR + c) * 16);
+  }
+
+  float o[G][C::XPC];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int x = 0; x < C::XPC; ++x) o[h][x] = 0.f;
+  float m_mine = kNegBig;  // reference max (log2 units) of this lane's head
+  float l_mine = 0.f;      // sum of this lane's probabilities
+
+  // this lane's scores: head hh, tokens t0 (+1 if NF == 2)
+  const int j0 = (c >> C::AR) * C::NF;
+  const int hh = j0 / C::NR;
+  const int tk0 = r * C::NR + (j0 % C::NR);
+
+  const int64_t tile_bytes = (int64_t)kBlock * C::RB;
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+
+  // block ids of this wave's blocks, one per lane, refreshed every 64 blocks
+  int my_ids = 0;
+  auto fetch_ids = [&](int n0) {
+    const int jb = b0 + w + NW * (n0 + lane);
+    my_ids = jb < b1 ? bt[jb] : 0;
+  };
+
+  uint4 kc[C::NR][C::U], vc[C::NPV], kn[C::NR][C::U], vn[C::NPV];
+  auto load_tile = [&](int id, uint4 (&kk)[C::NR][C::U], uint4 (&vv)[C::NPV]) {
+    const int64_t base = ((int64_t)id * p.num_kv_heads + g) * tile_bytes;
+    const char* kt = p.k_cache + base;
+    const char* vt = p.v_cache + base;
+#pragma unroll
+    for (int i = 0; i < C::NR; ++i)
+#pragma unroll
+      for (int u = 0; u < C::U; ++u)
+        kk[i][u] = *(const uint4*)(kt + (r * C::NR + i) * C::RB + (u * C::LPR + c) * 16);
+#pragma unroll
+    for (int i = 0; i < C::NPV; ++i)
+      vv[i] = *(const uint4*)(vt + (int64_t)(vgrp + (kWave / C::VL) * i) * 2 * C::RB + xc * 16);
+  };
+
+  const int nmine = b1 > b0 + w ? (b1 - b0 - w + NW - 1) / NW : 0;
+  int id_cur = 0;
+  bool bad_cur = false;
+  if (nmine > 0) {
+    fetch_ids(0);
+    id_cur = __builtin_amdgcn_readfirstlane(my_ids);
+    bad_cur = id_cur < 0 || id_cur >= p.num_blocks;
+    load_tile(bad_cur ? 0 : id_cur, kc, vc);
+  }
+
+  for (int n = 0; n < nmine; ++n) {
+    const int jblk = b0 + w + NW * n;
+    // ---- prefetch the next block
+    int id_next = 0;
+    bool bad_next = false;
+    if (n + 1 < nmine) {
+      if (((n + 1) & 63) == 0) fetch_ids(n + 1);
+      id_next = __builtin_amdgcn_readlane(my_ids, (n + 1) & 63);
+      bad_next = id_next < 0 || id_next >= p.num_blocks;
+      load_tile(bad_next ? 0 : id_next, kn, vn);
+    }
+
+    // ---- partial dots
+    float acc[C::N0];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < C::NR; ++i) {
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < C::U; ++u) {
+          const uint4 kk = kc[i][u];
+          const uint4 qq = qv[h][u];
+          if constexpr (EB == 2) {
+            a = dot2_bf16(qq.x, kk.x, a);
+            a = dot2_bf16(qq.y, kk.y, a);
+            a = dot2_bf16(qq.z, kk.z, a);
+            a = dot2_bf16(qq.w, kk.w, a);
+          } else {
+            a = fmaf(__uint_as_float(qq.x), __uint_as_float(kk.x), a);
+            a = fmaf(__uint_as_float(qq.y), __uint_as_float(kk.y), a);
+            a = fmaf(__uint_as_float(qq.z), __uint_as_float(kk.z), a);
+            a = fmaf(__uint_as_float(qq.w), __uint_as_float(kk.w), a);
+          }
+        }
+        acc[h * C::NR + i] = a;
+      }
+    reduce_scatter_lpr<C::LPR, C::N0>(acc, c);
+
+    // ---- scores (log2 units), masking tokens past the context
+    const int nvalid = bad_cur ? 0 : min(kBlock, ctx - jblk * kBlock);
+    float z[C::NF];
+#pragma unroll
+    for (int k = 0; k < C::NF; ++k) {
+      z[k] = acc[k] * p.scale_log2;
+      if (nvalid < kBlock) z[k] = (tk0 + k < nvalid) ? z[k] : -INFINITY;
+    }
+    if (nvalid < kBlock) {
+      // zero V of hidden tokens: a zero probability must not meet a NaN
+#pragma unroll
+      for (int i = 0; i < C::NPV; ++i) {
+        const int t0 = 2 * (vgrp + (kWave / C::VL) * i);
+        uint32_t* wv = (uint32_t*)&vc[i];
+        if constexpr (EB == 2) {
+          const uint32_t keep = t0 >= nvalid ? 0u : (t0 + 1 >= nvalid ? 0x0000ffffu : 0xffffffffu);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wv[e] &= keep;
+        } else {
+          const uint32_t k0 = t0 >= nvalid ? 0u : 0xffffffffu;
+          const uint32_t k1 = t0 + 1 >= nvalid ? 0u : 0xffffffffu;
+          wv[0] &= k0; wv[1] &= k1; wv[2] &= k0; wv[3] &= k1;
+        }
+      }
+    }
+
+    // ---- online softmax: raise the reference max only when needed
+    bool over = false;
+#pragma unroll
+    for (int k = 0; k < C::NF; ++k) over |= z[k] > m_mine + kRescaleGap;
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      float bm = z[0];
+#pragma unroll
+      for (int k = 1; k < C::NF; ++k) bm = fmaxf(bm, z[k]);
+      bm = group_max<C::HEAD_BITS | C::ROW_BITS>(bm);
+      const float m_new = fmaxf(m_mine, bm);
+      const float alpha = exp2f(m_mine - m_new);
+      l_mine *= alpha;
+      m_mine = m_new;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ah = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(alpha), (h * C::HEAD_SPAN) << C::AR));
+#pragma unroll
+        for (int x = 0; x < C::XPC; ++x) o[h][x] *= ah;
+      }
+    }
+    float pr[C::NF];
+#pragma unroll
+    for (int k = 0; k < C::NF; ++k) {
+      pr[k] = exp2f(z[k] - m_mine);
+      l_mine += pr[k];
+    }
+
+    // ---- probabilities -> LDS as [pair][head] (bf16 pairs or fp32 pairs)
+    uint32_t* pb = pbuf[w];
+    if constexpr (EB == 2) {
+      if constexpr (C::NF == 2) {
+        pb[(tk0 >> 1) * G + hh] = pack_bf16(pr[0], pr[1]);
+      } else {
+        if ((c & C::DUP_BITS) == 0)
+          ((uint16_t*)pb)[((tk0 >> 1) * G + hh) * 2 + (tk0 & 1)] = to_bf16(pr[0]);
+      }
+    } else {
+      if ((c & C::DUP_BITS) == 0) {
+#pragma unroll
+        for (int k = 0; k < C::NF; ++k) {
+          const int t = tk0 + k;
+          ((float*)pb)[((t >> 1) * G + hh) * 2 + (t & 1)] = pr[k];
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- P.V
+#pragma unroll
+    for (int i = 0; i < C::NPV; ++i) {
+      const int tp = vgrp + (kWave / C::VL) * i;
+      const uint4 vv = vc[i];
+      const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+      if constexpr (EB == 2) {
+        uint32_t pw[G];
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+          for (int h4 = 0; h4 < G / 4; ++h4) {
+            const uint4 t4 = *(const uint4*)&pb[tp * G + h4 * 4];
+            pw[h4 * 4 + 0] = t4.x; pw[h4 * 4 + 1] = t4.y;
+            pw[h4 * 4 + 2] = t4.z; pw[h4 * 4 + 3] = t4.w;
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h) pw[h] = pb[tp * G + h];
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int x = 0; x < C::XPC; ++x) o[h][x] = dot2_bf16(pw[h], wv[x], o[h][x]);
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float2 pp = *(const float2*)&pb[(tp * G + h) * 2];
+#pragma unroll
+          for (int x = 0; x < C::XPC; ++x) {
+            o[h][x] = fmaf(pp.x, __uint_as_float(wv[2 * x]), o[h][x]);
+            o[h][x] = fmaf(pp.y, __uint_as_float(wv[2 * x + 1]), o[h][x]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    if (n + 1 < nmine) {
+#pragma unroll
+      for (int i = 0; i < C::NR; ++i)
+#pragma unroll
+        for (int u = 0; u < C::U; ++u) kc[i][u] = kn[i][u];
+#pragma unroll
+      for (int i = 0; i < C::NPV; ++i) vc[i] = vn[i];
+      id_cur = id_next;
+      bad_cur = bad_next;
+    }
+  }
+
+  // ---- wave totals
+  float l_head = (c & C::DUP_BITS) == 0 ? l_mine : 0.f;
+  l_head = group_sum<C::HEAD_BITS | C::DUP_BITS | C::ROW_BITS>(l_head);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int x = 0; x < C::XPC; ++x) o[h][x] = group_sum<C::VGRP_BITS>(o[h][x]);
+
+  if ((lane & (C::ROW_BITS | C::HEAD_BITS | C::DUP_BITS)) == 0) {
+    sm[w][hh] = m_mine;
+    sl[w][hh] = l_head;
+  }
+  if (vgrp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int x = 0; x < C::XPC; ++x) so[w][h][xc * C::XPC + x] = o[h][x];
+  }
+  __syncthreads();
+
+  // ---- merge the waves
+  const bool single = nparts == 1;
+  for (int e = threadIdx.x; e < G * D; e += NW * kWave) {
+    const int h = e / D;
+    const int x = e - h * D;
+    float M = sm[0][h];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm[ww][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = exp2f(sm[ww][h] - M);
+      L = fmaf(sl[ww][h], f, L);
+      O = fmaf(so[ww][h][x], f, O);
+    }
+    const int hq = g * G + h;
+    const int64_t row = (int64_t)s * p.num_q_heads + hq;
+    if (single) {
+      const float val = L > 0.f ? O / L : 0.f;
+      if constexpr (EB == 2)
+        ((uint16_t*)p.out)[row * D + x] = to_bf16(val);
+      else
+        ((float*)p.out)[row * D + x] = val;
+    } else {
+      const int64_t slot = row * p.num_partitions + part;
+      p.ws_o[slot * D + x] = O;
+      if (x == 0) {
+        p.ws_m[slot] = M;
+        p.ws_l[slot] = L;
+      }
+    }
+  }
+}
+
+
+// Split-K merge: every partition p of a sequence left (m_p, l_p, O_p) with
+// m in log2 units and O unnormalised.  The partitions are merged with the
+// same rescale the online softmax uses within one:
+//   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  out = sum_p O_p 2^(m_p - M) / L.
+// One wave per (sequence, query head); sequences with a single partition were
+// finished by the partition kernel.
+template <int EB, int D>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
+  const int s = blockIdx.x / p.num_q_heads;
+  const int hq = blockIdx.x - s * p.num_q_heads;
+  const int ctx = clamp_ctx(p.context_lens[s], p);
+  const int nblk = (ctx + kBlock - 1) / kBlock;
+  const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  if (nparts <= 1) return;
+  const int64_t row = (int64_t)s * p.num_q_heads + hq;
+  const float* wm = p.ws_m + row * p.num_partitions;
+  const float* wl = p.ws_l + row * p.num_partitions;
+  const float* wo = p.ws_o + row * p.num_partitions * D;
+  const int lane = threadIdx.x;
+
+  // lane-parallel max / sum over the partitions
+  float M = kNegBig;
+  for (int q = lane; q < nparts; q += kWave) M = fmaxf(M, wm[q]);
+  M = group_max<63>(M);
+  float L = 0.f;
+  for (int q = lane; q < nparts; q += kWave) L = fmaf(wl[q], exp2f(wm[q] - M), L);
+  L = group_sum<63>(L);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+
+  constexpr int XL = D / kWave;  // dims per lane
+  float acc[XL];
+#pragma unroll
+  for (int e = 0; e < XL; ++e) acc[e] = 0.f;
+  for (int q = 0; q < nparts; ++q) {
+    const float f = exp2f(wm[q] - M);
+#pragma unroll
+    for (int e = 0; e < XL; ++e) acc[e] = fmaf(wo[(int64_t)q * D + lane + e * kWave], f, acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < XL; ++e) {
+    const float val = acc[e] * inv;
+    const int x = lane + e * kWave;
+    if constexpr (EB == 2)
+      ((uint16_t*)p.out)[row * D + x] = to_bf16(val);
+    else
+      ((float*)p.out)[row * D + x] = val;
+  }
+}
+
+template <int EB, int D, int G>
+static hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream) {
+  const int64_t grid = (int64_t)prm.num_partitions * prm.num_seqs * prm.num_kv_heads;
+  hipLaunchKernelGGL((decode_partition_kernel<EB, D, G>), dim3((unsigned)grid),
+                     dim3(kDecodeWaves * kWave), 0, stream, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || prm.num_partitions <= 1) return e;
+  hipLaunchKernelGGL((decode_reduce_kernel<EB, D>), dim3((unsigned)(prm.num_seqs * prm.num_q_heads)),
+                     dim3(kWave), 0, stream, prm);
+  return hipGetLastError();
+}
+
+bool decode_supported(int elem_bytes, int head_dim, int group) {
+  return (elem_bytes == 2 || elem_bytes == 4) && (head_dim == 64 || head_dim == 128) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const CacheGeom& g, hipStream_t stream) {
+  DecodeParams p;
+  p.out = a.out;
+  p.q = a.q;
+  p.k_cache = (const char*)a.k_cache;
+  p.v_cache = (const char*)a.v_cache;
+  p.block_tables = a.block_tables;
+  p.context_lens = a.context_lens;
+  const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads * a.num_partitions;
+  p.ws_m = a.ws;
+  p.ws_l = a.ws ? a.ws + rows : nullptr;
+  p.ws_o = a.ws ? a.ws + 2 * rows : nullptr;
+  p.max_blocks_per_seq = a.max_blocks_per_seq;
+  p.num_seqs = a.num_seqs;
+  p.num_q_heads = a.num_q_heads;
+  p.num_kv_heads = g.num_kv_heads;
+  p.num_blocks = g.num_blocks;
+  p.num_partitions = a.num_partitions;
+  p.partition_blocks = a.partition_blocks;
+  p.scale_log2 = a.scale * kLog2e;
+  const int G = a.num_q_heads / g.num_kv_heads;
+
+#define PA_DECODE_CASE(EB_, D_, G_) \
+  if (g.elem_bytes == EB_ && g.head_dim == D_ && G == G_) return launch_decode_t<EB_, D_, G_>(p, stream);
+#define PA_DECODE_GROUPS(EB_, D_) \
+  PA_DECODE_CASE(EB_, D_, 1) PA_DECODE_CASE(EB_, D_, 2) PA_DECODE_CASE(EB_, D_, 4) PA_DECODE_CASE(EB_, D_, 8)
+  PA_DECODE_GROUPS(2, 128)
+  PA_DECODE_GROUPS(2, 64)
+  PA_DECODE_GROUPS(4, 128)
+  PA_DECODE_GROUPS(4, 64)
+#undef PA_DECODE_GROUPS
+#undef PA_DECODE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

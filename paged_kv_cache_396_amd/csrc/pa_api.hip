@@ -1,0 +1,272 @@
+// C ABI of libpa.so: argument validation, variant dispatch, split-K sizing.
+// The semantics of every entry point are documented in include/pa.h.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "pa_launch.h"
+
+#define PA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes_of(int32_t dtype) {
+  if (dtype == PA_F32) return 4;
+  if (dtype == PA_BF16) return 2;
+  return 0;
+}
+
+// Validates a cache descriptor; fills geometry on success.
+int check_desc(const pa_cache_desc* d, pa::CacheGeom* g) {
+  if (!d) return fail(PA_ERR_NULL, "cache descriptor is NULL");
+  const int eb = elem_bytes_of(d->dtype);
+  if (!eb) return fail(PA_ERR_DTYPE, "unknown dtype %d", (int)d->dtype);
+  if (d->block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d (only %d is built)", (int)d->block_size,
+                PA_BLOCK_SIZE);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d (64 or 128 are built)", (int)d->head_dim);
+  if (d->num_blocks < 1 || d->num_kv_heads < 1)
+    return fail(PA_ERR_SHAPE, "num_blocks %d / num_kv_heads %d must be >= 1", (int)d->num_blocks,
+                (int)d->num_kv_heads);
+  // slots are int64 on the wire but kernels index tokens with 32-bit block
+  // offsets times 16; keep num_blocks * 16 below 2^31
+  if ((int64_t)d->num_blocks * PA_BLOCK_SIZE >= (int64_t)1 << 31)
+    return fail(PA_ERR_OVERFLOW, "num_blocks %d * 16 slots exceeds 2^31", (int)d->num_blocks);
+  if (g) {
+    g->num_blocks = d->num_blocks;
+    g->num_kv_heads = d->num_kv_heads;
+    g->head_dim = d->head_dim;
+    g->elem_bytes = eb;
+  }
+  return PA_OK;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int32_t round_up16(int64_t x) { return (int32_t)((x + 15) / 16 * 16); }
+
+// Resolves the partition size (tokens) for a decode call.
+int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx, int32_t req) {
+  const int32_t whole = max_ctx < 16 ? 16 : round_up16(max_ctx);
+  if (req < 0) return whole;
+  if (req > 0) return req;
+  // automatic: 512-token partitions (32 blocks, 8 per wave) unless the
+  // sequences alone already give every CU several workgroups and the
+  // contexts are short enough that one pass is cheap.
+  const int cus = device_cu_count();
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  int32_t part = 512;
+  if (units >= 8LL * cus && max_ctx <= 1024) part = whole;
+  // very long contexts with few sequences: keep partitions at 512 tokens
+  // (more partitions only add merge work)
+  return part >= whole ? whole : part;
+}
+
+}  // namespace
+
+PA_API int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+PA_API size_t pa_cache_bytes(const pa_cache_desc* desc) {
+  pa::CacheGeom g;
+  if (check_desc(desc, &g) != PA_OK) return 0;
+  return (size_t)g.num_blocks * g.num_kv_heads * PA_BLOCK_SIZE * g.head_dim * g.elem_bytes;
+}
+
+PA_API int pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
+                                int32_t num_tokens, void* k_cache, void* v_cache,
+                                const pa_cache_desc* desc, void* stream) {
+  pa::CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d < 0", (int)num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PA_ERR_NULL, "k, v, slot_mapping, k_cache and v_cache must be non-NULL");
+  if ((int64_t)num_tokens * g.num_kv_heads * g.head_dim * g.elem_bytes / 16 >= ((int64_t)1 << 40))
+    return fail(PA_ERR_OVERFLOW, "too many tokens for one call");
+  hipError_t e = pa::launch_cache_write(k, v, slot_mapping, num_tokens, k_cache, v_cache, g,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cache write launch");
+  return ok();
+}
+
+PA_API int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                        int32_t max_context_len, int32_t partition_size_request) {
+  if (num_seqs < 0 || num_kv_heads < 1 || max_context_len < 0)
+    return fail(PA_ERR_SHAPE, "num_seqs %d, num_kv_heads %d, max_context_len %d", (int)num_seqs,
+                (int)num_kv_heads, (int)max_context_len);
+  if (partition_size_request > 0 && partition_size_request % PA_BLOCK_SIZE != 0)
+    return fail(PA_ERR_SHAPE, "partition_size %d is not a multiple of 16",
+                (int)partition_size_request);
+  return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size_request);
+}
+
+PA_API size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_context_len,
+                                        int32_t partition_size_request) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0)
+    return 0;
+  if (partition_size_request > 0 && partition_size_request % PA_BLOCK_SIZE != 0) return 0;
+  const int32_t part = resolve_partition(num_seqs, num_kv_heads, max_context_len,
+                                         partition_size_request);
+  const int64_t nparts = ((int64_t)max_context_len + part - 1) / part;
+  if (nparts <= 1) return 0;
+  return (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
+}
+
+PA_API int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                     int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
+                     size_t workspace_bytes, const pa_cache_desc* desc, void* stream) {
+  pa::CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 1 || num_q_heads < 1)
+    return fail(PA_ERR_SHAPE, "num_seqs %d, max_context_len %d, max_blocks_per_seq %d, num_q_heads %d",
+                (int)num_seqs, (int)max_context_len, (int)max_blocks_per_seq, (int)num_q_heads);
+  if (num_q_heads % g.num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                (int)num_q_heads, g.num_kv_heads);
+  const int group = num_q_heads / g.num_kv_heads;
+  if (!pa::decode_supported(g.elem_bytes, g.head_dim, group))
+    return fail(PA_ERR_UNSUPPORTED, "decode variant dtype=%d head_dim=%d group=%d is not built",
+                (int)desc->dtype, g.head_dim, group);
+  if (partition_size > 0 && partition_size % PA_BLOCK_SIZE != 0)
+    return fail(PA_ERR_SHAPE, "partition_size %d is not a multiple of 16", (int)partition_size);
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL, "out, q, k_cache, v_cache, block_tables and context_lens must be non-NULL");
+  const int32_t part = resolve_partition(num_seqs, g.num_kv_heads, max_context_len, partition_size);
+  int64_t nparts = ((int64_t)max_context_len + part - 1) / part;
+  if (nparts < 1) nparts = 1;
+  if (nparts * num_seqs * g.num_kv_heads >= ((int64_t)1 << 31) ||
+      (int64_t)num_seqs * num_q_heads >= ((int64_t)1 << 31))
+    return fail(PA_ERR_OVERFLOW, "decode grid too large");
+  float* ws = nullptr;
+  if (nparts > 1) {
+    const size_t need = (size_t)num_seqs * num_q_heads * nparts * (g.head_dim + 2) * sizeof(float);
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given (ptr %p)", need,
+                  workspace_bytes, workspace);
+    ws = (float*)workspace;
+  }
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws = ws;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_partitions = (int)nparts;
+  a.partition_blocks = part / PA_BLOCK_SIZE;
+  a.scale = scale;
+  hipError_t e = pa::launch_decode(a, g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+PA_API int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* query_start_loc, const int32_t* context_lens,
+                            int32_t num_reqs, int32_t total_q_tokens, int32_t max_q_len,
+                            int32_t num_q_heads, float scale, const pa_cache_desc* desc,
+                            void* stream) {
+  pa::CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != PA_OK) return st;
+  if (num_reqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_blocks_per_seq < 1 ||
+      num_q_heads < 1)
+    return fail(PA_ERR_SHAPE,
+                "num_reqs %d, total_q_tokens %d, max_q_len %d, max_blocks_per_seq %d, num_q_heads %d",
+                (int)num_reqs, (int)total_q_tokens, (int)max_q_len, (int)max_blocks_per_seq,
+                (int)num_q_heads);
+  if (num_q_heads % g.num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                (int)num_q_heads, g.num_kv_heads);
+  const int group = num_q_heads / g.num_kv_heads;
+  if (!pa::prefill_supported(g.elem_bytes, g.head_dim, group))
+    return fail(PA_ERR_UNSUPPORTED, "prefill variant dtype=%d head_dim=%d group=%d is not built",
+                (int)desc->dtype, g.head_dim, group);
+  if (num_reqs == 0 || total_q_tokens == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
+    return fail(PA_ERR_NULL, "prefill pointers must be non-NULL");
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.query_start_loc = query_start_loc;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_reqs = num_reqs;
+  a.total_q_tokens = total_q_tokens;
+  a.max_q_len = max_q_len;
+  a.num_q_heads = num_q_heads;
+  a.scale = scale;
+  hipError_t e = pa::launch_prefill(a, g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+PA_API const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer";
+    case PA_ERR_SHAPE: return "invalid shape";
+    case PA_ERR_DTYPE: return "invalid dtype";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_OVERFLOW: return "size overflow";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+PA_API const char* pa_last_error(void) { return g_last_error.c_str(); }

@@ -1,0 +1,135 @@
+"""Helpers for GPU tests: move seeded workloads to the device, run the library
+through its C ABI, and compare with the oracle at the stated tolerances."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import paged_kv_cache_396_amd as pa
+from workloads import poison_bits
+
+# spec tolerances
+F32_MAX_ABS = 1e-5
+BF16_ATOL = 2e-2
+BF16_RTOL = 2e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch():
+    import torch as _t
+
+    return _t
+
+
+def tdtype(dtype):
+    t = torch()
+    return t.bfloat16 if dtype == "bf16" else t.float32
+
+
+def to_dev(raw: np.ndarray, dtype: str):
+    t = torch()
+    if dtype == "bf16":
+        return t.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(t.bfloat16).cuda()
+    return t.from_numpy(np.ascontiguousarray(raw).view(np.float32)).cuda()
+
+
+def to_f64(t) -> np.ndarray:
+    """Exact float64 of a device tensor (bf16 and fp32 widen exactly)."""
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def raw_bits(t) -> np.ndarray:
+    tt = torch()
+    if t.dtype == tt.bfloat16:
+        return t.view(tt.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == tt.float32:
+        return t.view(tt.int32).cpu().numpy().view(np.uint32)
+    return t.cpu().numpy()
+
+
+class GpuPool:
+    """K and V pools in device memory, filled with the NaN poison pattern."""
+
+    def __init__(self, num_blocks, num_kv_heads, head_dim, dtype):
+        t = torch()
+        self.dtype = dtype
+        self.desc = pa.cache_desc(num_blocks, num_kv_heads, head_dim, tdtype(dtype))
+        nbytes = pa.pa_cache_bytes(self.desc)
+        assert nbytes > 0
+        self.k = t.empty(nbytes, dtype=t.uint8, device="cuda")
+        self.v = t.empty(nbytes, dtype=t.uint8, device="cuda")
+        if dtype == "bf16":
+            self.k.view(t.int16).fill_(poison_bits("bf16"))
+            self.v.view(t.int16).fill_(poison_bits("bf16"))
+        else:
+            self.k.view(t.int32).fill_(np.int32(np.uint32(poison_bits("f32")).view(np.int32)).item())
+            self.v.view(t.int32).fill_(np.int32(np.uint32(poison_bits("f32")).view(np.int32)).item())
+
+    def write(self, k_raw, v_raw, slots):
+        t = torch()
+        if len(slots) == 0:
+            return
+        k = to_dev(k_raw, self.dtype)
+        v = to_dev(v_raw, self.dtype)
+        s = t.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).cuda()
+        pa.pa_reshape_and_cache(k, v, s, self.k, self.v, self.desc)
+
+    def k_bits(self):
+        return self.k.cpu().numpy().view(np.uint16 if self.dtype == "bf16" else np.uint32)
+
+    def v_bits(self):
+        return self.v.cpu().numpy().view(np.uint16 if self.dtype == "bf16" else np.uint32)
+
+
+def gpu_pool_for(wl, with_new=True):
+    pool = GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
+    pool.write(wl.hist_k, wl.hist_v, wl.hist_slots)
+    if with_new:
+        pool.write(wl.new_k, wl.new_v, wl.new_slots)
+    return pool
+
+
+def oracle_pools(wl, oracle):
+    pk = oracle.new_pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype, poison_bits(wl.dtype))
+    pv = oracle.new_pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype, poison_bits(wl.dtype))
+    oracle.reshape_and_cache_fast(pk, pv, wl.hist_k, wl.hist_v, wl.hist_slots)
+    oracle.reshape_and_cache_fast(pk, pv, wl.new_k, wl.new_v, wl.new_slots)
+    return pk, pv
+
+
+def gpu_decode(wl, pool, partition_size=0, context_lens=None, max_ctx=None):
+    t = torch()
+    q = to_dev(wl.q, wl.dtype)
+    out = t.empty_like(q)
+    cl_np = wl.context_lens if context_lens is None else context_lens
+    bt = t.from_numpy(np.ascontiguousarray(wl.block_tables)).cuda()
+    cl = t.from_numpy(np.ascontiguousarray(cl_np, dtype=np.int32)).cuda()
+    maxctx = int(cl_np.max()) if max_ctx is None else int(max_ctx)
+    S, Hq, D = wl.q.shape
+    ws_bytes = pa.pa_decode_workspace_bytes(S, Hq, wl.num_kv_heads, D, maxctx, partition_size)
+    ws = t.empty((ws_bytes + 3) // 4, dtype=t.float32, device="cuda") if ws_bytes else None
+    pa.pa_decode(out, q, pool.k, pool.v, bt, cl, maxctx, float(wl.scale), pool.desc,
+                 partition_size=partition_size, workspace=ws)
+    t.cuda.synchronize()
+    return out
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        m = float(err.max()) if err.size else 0.0
+        assert m <= F32_MAX_ABS, f"{what}: max abs err {m:.3g} > {F32_MAX_ABS}"
+    else:
+        bound = BF16_ATOL + BF16_RTOL * np.abs(ref)
+        bad = err > bound
+        assert not bad.any(), (
+            f"{what}: {int(bad.sum())} elements outside atol/rtol 2e-2; max abs err {err.max():.3g}")
+    return float(err.max()) if err.size else 0.0

@@ -1,0 +1,170 @@
+"""Paged decode on the GPU against the fp64 oracle.
+
+Tolerances: fp32 inputs max-abs 1e-5; bf16 inputs |gpu - ref| <= 2e-2 + 2e-2|ref|.
+Pools are NaN-poisoned before any write, so a read of a slot that no table
+references, or of a token past the context, shows up as a non-finite output.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_decode, make_tiny_decode, make_tiny_shared
+
+from gpu_util import assert_close, gpu_decode, gpu_pool_for, log, oracle_pools, raw_bits, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_decode(wl, seqs=None):
+    pk, pv = oracle_pools(wl, oracle)
+    return oracle.decode(wl.q, pk, pv, wl.block_tables, wl.context_lens, wl.scale, wl.dtype,
+                         seqs=seqs)
+
+
+@pytest.mark.parametrize("partition", [0, -1, 16, 32])
+def test_config1_tiny_fp32(partition):
+    log(f"decode config 1 partition={partition}")
+    wl = make_decode(1)
+    out = gpu_decode(wl, gpu_pool_for(wl), partition_size=partition)
+    assert_close(to_f64(out), _oracle_decode(wl), "f32", "config 1")
+
+
+SHAPES = [
+    # dtype, D, Hq, Hkv, ctx
+    ("bf16", 128, 32, 8, (1, 7, 16, 17, 100, 513, 1000)),
+    ("bf16", 128, 64, 8, (3, 48, 255, 700)),
+    ("bf16", 128, 4, 2, (5, 31, 300)),
+    ("bf16", 128, 3, 3, (2, 66, 129)),
+    ("bf16", 64, 16, 2, (9, 160, 401)),
+    ("bf16", 64, 8, 4, (1, 33, 77)),
+    ("bf16", 64, 4, 1, (17, 64)),
+    ("f32", 64, 4, 2, (5, 17, 33, 64, 130)),
+    ("f32", 64, 8, 1, (40, 200)),
+    ("f32", 128, 4, 4, (3, 90)),
+    ("f32", 128, 16, 4, (12, 150)),
+    ("f32", 128, 8, 1, (70,)),
+]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,ctx", SHAPES)
+@pytest.mark.parametrize("partition", [0, -1, 64])
+def test_tiny_shapes(dtype, D, Hq, Hkv, ctx, partition):
+    log(f"decode tiny {dtype} D={D} Hq={Hq} Hkv={Hkv} ctx={ctx} partition={partition}")
+    wl = make_tiny_decode(seed=41 + D + Hq, ctx=ctx, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype)
+    out = gpu_decode(wl, gpu_pool_for(wl), partition_size=partition)
+    assert_close(to_f64(out), _oracle_decode(wl), dtype, f"tiny {dtype} {D} {Hq}/{Hkv}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_token_context_is_bit_exact(dtype):
+    """ctx = 1: the softmax weight is exactly 1, so the output is the V row."""
+    log(f"decode single token {dtype}")
+    wl = make_tiny_decode(seed=5, ctx=(1, 1, 1, 1), Hq=8, Hkv=2, D=128, dtype=dtype)
+    out = gpu_decode(wl, gpu_pool_for(wl))
+    got = to_f64(out)
+    for s in range(4):
+        for h in range(8):
+            v = oracle.widen(wl.new_v[s, h // 4], dtype)
+            assert np.array_equal(got[s, h], v)
+
+
+def test_zero_length_context_gives_zeros():
+    log("decode ctx 0")
+    wl = make_tiny_decode(seed=6, ctx=(5, 40), Hq=8, Hkv=2, D=128, dtype="bf16")
+    pool = gpu_pool_for(wl)
+    cl = wl.context_lens.copy()
+    cl[0] = 0
+    out = to_f64(gpu_decode(wl, pool, context_lens=cl, partition_size=16))
+    assert (out[0] == 0).all()
+    ref = _oracle_decode(wl)
+    assert_close(out[1], ref[1], "bf16", "ctx 0 neighbour")
+
+
+def test_permutation_of_physical_blocks_is_bitwise_invariant():
+    log("decode permutation invariance")
+    a = make_tiny_decode(seed=7, ctx=(33, 500, 1024, 77), Hq=32, Hkv=8, D=128, dtype="bf16",
+                         layout_variant=0)
+    b = make_tiny_decode(seed=7, ctx=(33, 500, 1024, 77), Hq=32, Hkv=8, D=128, dtype="bf16",
+                         layout_variant=1)
+    assert not np.array_equal(a.block_tables, b.block_tables)
+    for part in (0, -1):
+        oa = gpu_decode(a, gpu_pool_for(a), partition_size=part)
+        ob = gpu_decode(b, gpu_pool_for(b), partition_size=part)
+        assert np.array_equal(raw_bits(oa), raw_bits(ob))
+
+
+def test_shared_prefix_equals_private_copies_bitwise_tiny():
+    log("decode shared vs private tiny")
+    a = make_tiny_shared(dtype="bf16", D=128, Hq=8, Hkv=2)
+    b = make_tiny_shared(dtype="bf16", D=128, Hq=8, Hkv=2, private_copies=True)
+    oa = gpu_decode(a, gpu_pool_for(a))
+    ob = gpu_decode(b, gpu_pool_for(b))
+    assert np.array_equal(raw_bits(oa), raw_bits(ob))
+    assert_close(to_f64(oa), _oracle_decode(a), "bf16", "tiny shared")
+
+
+def test_split_k_partitions_agree():
+    """Different partition sizes give results within the bf16 tolerance of the
+    oracle and of each other."""
+    log("decode split-K sweep")
+    wl = make_tiny_decode(seed=8, ctx=(4000, 2049, 513, 16), Hq=32, Hkv=8, D=128, dtype="bf16")
+    pool = gpu_pool_for(wl)
+    ref = _oracle_decode(wl)
+    for part in (0, -1, 16, 48, 512, 1024):
+        out = to_f64(gpu_decode(wl, pool, partition_size=part))
+        assert_close(out, ref, "bf16", f"partition {part}")
+
+
+def test_config2_llama3_8b_full():
+    log("decode config 2 (full)")
+    wl = make_decode(2)
+    pool = gpu_pool_for(wl)
+    ref = _oracle_decode(wl)
+    for part in (0, -1, 256):
+        out = to_f64(gpu_decode(wl, pool, partition_size=part))
+        err = assert_close(out, ref, "bf16", f"config 2 partition {part}")
+        log(f"  partition {part}: max abs err {err:.3g}")
+
+
+def test_config2_permuted_layout_bitwise_equal():
+    log("decode config 2 permutation")
+    a = make_decode(2, layout_variant=0)
+    b = make_decode(2, layout_variant=1)
+    oa = gpu_decode(a, gpu_pool_for(a))
+    ob = gpu_decode(b, gpu_pool_for(b))
+    assert np.array_equal(raw_bits(oa), raw_bits(ob))
+
+
+def test_config3_llama2_70b_sampled():
+    """Full-size launch; the oracle checks 16 sampled sequences (all heads)."""
+    log("decode config 3 (full launch, sampled check)")
+    wl = make_decode(3)
+    pool = gpu_pool_for(wl)
+    out = to_f64(gpu_decode(wl, pool))
+    seqs = list(range(0, 256, 16))
+    ref = _oracle_decode(wl, seqs=seqs)
+    assert np.isfinite(out).all()
+    assert_close(out[seqs], ref[seqs], "bf16", "config 3 sampled")
+
+
+def test_config4_shared_prefix():
+    log("decode config 4 shared prefix")
+    a = make_decode(4)
+    out = to_f64(gpu_decode(a, gpu_pool_for(a)))
+    seqs = list(range(0, 128, 5))
+    ref = _oracle_decode(a, seqs=seqs)
+    assert_close(out[seqs], ref[seqs], "bf16", "config 4 sampled")
+    b = make_decode(4, private_copies=True)
+    ob = to_f64(gpu_decode(b, gpu_pool_for(b)))
+    assert np.array_equal(out, ob), "shared and private tables differ"
+
+
+def test_config5_long_context_decode():
+    log("decode config 5 (8 x 32768)")
+    wl = make_decode(5)
+    pool = gpu_pool_for(wl)
+    ref = _oracle_decode(wl)
+    for part in (0, 512, -1):
+        out = to_f64(gpu_decode(wl, pool, partition_size=part))
+        assert_close(out, ref, "bf16", f"config 5 partition {part}")
