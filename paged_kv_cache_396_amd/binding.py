@@ -15,7 +15,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpa.so")
+# PA_LIB may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("PA_LIB") or os.path.join(PKG, "libpa.so")
 
 PA_F32 = 0
 PA_BF16 = 1

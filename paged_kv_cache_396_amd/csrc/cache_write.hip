@@ -24,6 +24,9 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int chunk = (int)(idx - row * chunks_per_row);
   const int64_t tok = row / num_kv_heads;
   const int g = (int)(row - tok * num_kv_heads);
+  // the row loads do not depend on the slot: issue all three together
+  const uint4 kv = k[idx];
+  const uint4 vv = v[idx];
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= pool_slots) return;
   const int64_t b = slot / kBlock;
@@ -31,12 +34,10 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int64_t base = tile_base(b, g, num_kv_heads, head_dim);  // elements
 
   // K: element (b, g, o, x) at base + o * D + x
-  const uint4 kv = k[idx];
   const int64_t kdst = (base + (int64_t)o * head_dim) * EB / 16 + chunk;
   k_cache[kdst] = kv;
 
   // V: element (b, g, o, x) at base + ((o / 2) * D + x) * 2 + o % 2
-  const uint4 vv = v[idx];
   constexpr int E = 16 / EB;  // elements in this chunk
   const int x0 = chunk * E;
   const int64_t vrow = base + (int64_t)(o >> 1) * head_dim * 2 + (o & 1);

@@ -41,9 +41,29 @@
 
 namespace pa {
 
-constexpr int kDecodeWaves = 4;
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1
+#endif
+constexpr int kDecodeWaves = PA_DECODE_WAVES;      // waves per workgroup
+
 constexpr float kRescaleGap = 8.0f;   // log2 units: p may reach 2^8 before a rescale
 constexpr float kNegBig = -FLT_MAX;   // "no score yet"; keeps exp2 of differences finite
+
+// Raw buffer descriptor over [ptr, ptr + bytes): loads beyond `bytes` return 0.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const char* ptr, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0, bytes, 0x00020000);
+}
+
+// 16-byte KV load at byte offset `off`.  KV is streamed once per call, so the
+// load is marked non-temporal (cache policy bit nt).
+__device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PA_DECODE_NT ? 2 : 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int EB, int D, int G>
 struct DecodeCfg {
@@ -140,8 +160,16 @@ __device__ inline void reduce_scatter_lpr(float (&v)[L], int c) {
 }
 
 
+// Occupancy target (waves per SIMD) the register allocator must meet.
 template <int EB, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(DecodeParams p) {
+constexpr int decode_waves_per_eu() {
+  return (EB == 2 && G <= 4) || (EB == 4 && D == 64 && G <= 2) ? 3 : (EB == 4 && D == 128 && G >= 4) ? 1 : 2;
+}
+
+template <int EB, int D, int G>
+__global__ __launch_bounds__(kDecodeWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<EB, D, G>())))
+void decode_partition_kernel(DecodeParams p) {
   using C = DecodeCfg<EB, D, G>;
   constexpr int NW = kDecodeWaves;
 
@@ -155,23 +183,25 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
   const int s = (bid / p.num_kv_heads) % p.num_seqs;
   const int part = bid / (p.num_kv_heads * p.num_seqs);
 
-  const int ctx = clamp_ctx(p.context_lens[s], p);
-  const int nblk = (ctx + kBlock - 1) / kBlock;
-  const int nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
-  if (part >= nparts) return;  // uniform over the workgroup
-
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
+  // wave index, provably uniform so that loop control stays scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int c = lane & (C::LPR - 1);  // lane within its K row
   const int r = lane / C::LPR;        // row group
   const int vgrp = lane / C::VL;      // V pair-row group
   const int xc = lane & (C::VL - 1);  // V chunk within a pair-row
-
   const int b0 = part * p.partition_blocks;
-  const int b1 = min(nblk, b0 + p.partition_blocks);
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
 
-  // ---- q chunks for the G heads of this kv head: [G][U] x 16 bytes
-  uint4 qv[G][C::U];
+  // The first block ids of this wave and q do not depend on the context
+  // length: issue them together with its load, so the first KV tile waits on
+  // one memory round trip instead of two.
+  int my_ids;  // id of block b0 + w + NW*(c0 + lane) for the current chunk c0
+  {
+    const int jb = b0 + w + NW * lane;
+    my_ids = jb < min(p.max_blocks_per_seq, b0 + p.partition_blocks) ? bt[jb] : 0;
+  }
+  uint4 qv[G][C::U];  // q chunks for the G heads of this kv head
   {
     const char* qbase = (const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::RB;
 #pragma unroll
@@ -180,6 +210,12 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
       for (int u = 0; u < C::U; ++u)
         qv[h][u] = *(const uint4*)(qbase + (int64_t)h * C::RB + (u * C::LPR + c) * 16);
   }
+
+  const int ctx = clamp_ctx(p.context_lens[s], p);
+  const int nblk = (ctx + kBlock - 1) / kBlock;
+  const int nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  if (part >= nparts) return;  // uniform over the workgroup
+  const int b1 = min(nblk, b0 + p.partition_blocks);
 
   float o[G][C::XPC];
 #pragma unroll
@@ -195,51 +231,38 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
   const int tk0 = r * C::NR + (j0 % C::NR);
 
   const int64_t tile_bytes = (int64_t)kBlock * C::RB;
-  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
 
   // block ids of this wave's blocks, one per lane, refreshed every 64 blocks
-  int my_ids = 0;
   auto fetch_ids = [&](int n0) {
     const int jb = b0 + w + NW * (n0 + lane);
     my_ids = jb < b1 ? bt[jb] : 0;
   };
 
-  uint4 kc[C::NR][C::U], vc[C::NPV], kn[C::NR][C::U], vn[C::NPV];
-  auto load_tile = [&](int id, uint4 (&kk)[C::NR][C::U], uint4 (&vv)[C::NPV]) {
+  uint4 kb[2][C::NR][C::U], vb[2][C::NPV];  // two tile slots
+  // Tile loads go through a per-tile buffer descriptor.  A tile that must not
+  // be read (past the end of the chunk, or a block id outside the pool) gets
+  // a descriptor with no records: its loads return zeros without touching
+  // memory but still retire in order, which keeps every wait count static.
+  auto load_tile = [&](int id, bool real, uint4 (&kk)[C::NR][C::U], uint4 (&vv)[C::NPV]) {
     const int64_t base = ((int64_t)id * p.num_kv_heads + g) * tile_bytes;
-    const char* kt = p.k_cache + base;
-    const char* vt = p.v_cache + base;
+    const int nrec = real ? (int)tile_bytes : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k_cache + base, nrec);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v_cache + base, nrec);
 #pragma unroll
     for (int i = 0; i < C::NR; ++i)
 #pragma unroll
       for (int u = 0; u < C::U; ++u)
-        kk[i][u] = *(const uint4*)(kt + (r * C::NR + i) * C::RB + (u * C::LPR + c) * 16);
+        kk[i][u] = load16(kr, (r * C::NR + i) * C::RB + (u * C::LPR + c) * 16);
 #pragma unroll
     for (int i = 0; i < C::NPV; ++i)
-      vv[i] = *(const uint4*)(vt + (int64_t)(vgrp + (kWave / C::VL) * i) * 2 * C::RB + xc * 16);
+      vv[i] = load16(vr, (vgrp + (kWave / C::VL) * i) * 2 * C::RB + xc * 16);
   };
-
+  auto id_ok = [&](int id) { return id >= 0 && id < p.num_blocks; };
   const int nmine = b1 > b0 + w ? (b1 - b0 - w + NW - 1) / NW : 0;
-  int id_cur = 0;
-  bool bad_cur = false;
-  if (nmine > 0) {
-    fetch_ids(0);
-    id_cur = __builtin_amdgcn_readfirstlane(my_ids);
-    bad_cur = id_cur < 0 || id_cur >= p.num_blocks;
-    load_tile(bad_cur ? 0 : id_cur, kc, vc);
-  }
 
-  for (int n = 0; n < nmine; ++n) {
+  auto process = [&](uint4 (&kc)[C::NR][C::U], uint4 (&vc)[C::NPV], int id_cur, int n) {
     const int jblk = b0 + w + NW * n;
-    // ---- prefetch the next block
-    int id_next = 0;
-    bool bad_next = false;
-    if (n + 1 < nmine) {
-      if (((n + 1) & 63) == 0) fetch_ids(n + 1);
-      id_next = __builtin_amdgcn_readlane(my_ids, (n + 1) & 63);
-      bad_next = id_next < 0 || id_next >= p.num_blocks;
-      load_tile(bad_next ? 0 : id_next, kn, vn);
-    }
+    const bool bad_cur = id_cur < 0 || id_cur >= p.num_blocks;
 
     // ---- partial dots
     float acc[C::N0];
@@ -378,16 +401,22 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
       }
     }
     __builtin_amdgcn_wave_barrier();
+  };
 
-    if (n + 1 < nmine) {
-#pragma unroll
-      for (int i = 0; i < C::NR; ++i)
-#pragma unroll
-        for (int u = 0; u < C::U; ++u) kc[i][u] = kn[i][u];
-#pragma unroll
-      for (int i = 0; i < C::NPV; ++i) vc[i] = vn[i];
-      id_cur = id_next;
-      bad_cur = bad_next;
+  // Blocks are taken in chunks of 64 (one block id per lane).  Two register
+  // slots alternate: while one tile is computed the next is in flight.  The
+  // loads are unconditional (a tile past the chunk's end is an empty
+  // descriptor), so the wait before each tile is a static count.
+  for (int c0 = 0; c0 < nmine; c0 += 64) {
+    const int cnt = min(64, nmine - c0);
+    if (c0 > 0) fetch_ids(c0);
+    auto id_at = [&](int i) { return __builtin_amdgcn_readlane(my_ids, min(i, cnt - 1)); };
+    load_tile(id_at(0), id_ok(id_at(0)), kb[0], vb[0]);
+    for (int n = 0; n < cnt; n += 2) {
+      load_tile(id_at(n + 1), n + 1 < cnt && id_ok(id_at(n + 1)), kb[1], vb[1]);
+      process(kb[0], vb[0], id_at(n), c0 + n);
+      load_tile(id_at(n + 2), n + 2 < cnt && id_ok(id_at(n + 2)), kb[0], vb[0]);
+      if (n + 1 < cnt) process(kb[1], vb[1], id_at(n + 1), c0 + n + 1);
     }
   }
 
@@ -466,24 +495,25 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
   const float* wo = p.ws_o + row * p.num_partitions * D;
   const int lane = threadIdx.x;
 
-  // lane-parallel max / sum over the partitions
+  // pass 1: lane-parallel max over the partitions' reference maxima
   float M = kNegBig;
   for (int q = lane; q < nparts; q += kWave) M = fmaxf(M, wm[q]);
   M = group_max<63>(M);
-  float L = 0.f;
-  for (int q = lane; q < nparts; q += kWave) L = fmaf(wl[q], exp2f(wm[q] - M), L);
-  L = group_sum<63>(L);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-
+  // pass 2: weights from uniform (scalar) loads; the O loads do not depend on
+  // M and are issued ahead of the arithmetic
   constexpr int XL = D / kWave;  // dims per lane
   float acc[XL];
 #pragma unroll
   for (int e = 0; e < XL; ++e) acc[e] = 0.f;
+  float L = 0.f;
+#pragma unroll 4
   for (int q = 0; q < nparts; ++q) {
     const float f = exp2f(wm[q] - M);
+    L = fmaf(wl[q], f, L);
 #pragma unroll
     for (int e = 0; e < XL; ++e) acc[e] = fmaf(wo[(int64_t)q * D + lane + e * kWave], f, acc[e]);
   }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
   for (int e = 0; e < XL; ++e) {
     const float val = acc[e] * inv;

@@ -90,15 +90,16 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ct
   const int32_t whole = max_ctx < 16 ? 16 : round_up16(max_ctx);
   if (req < 0) return whole;
   if (req > 0) return req;
-  // automatic: 512-token partitions (32 blocks, 8 per wave) unless the
-  // sequences alone already give every CU several workgroups and the
-  // contexts are short enough that one pass is cheap.
-  const int cus = device_cu_count();
+  // automatic: every workgroup pays a fixed start-up cost (a few dependent
+  // memory round trips) and every extra partition adds merge traffic, so
+  // split only as far as needed to give the device about 8 workgroups per
+  // compute unit, and never below 256 tokens per partition.
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  int32_t part = 512;
-  if (units >= 8LL * cus && max_ctx <= 1024) part = whole;
-  // very long contexts with few sequences: keep partitions at 512 tokens
-  // (more partitions only add merge work)
+  const int64_t target = 8LL * device_cu_count();
+  if (units >= target) return whole;
+  int64_t splits = target / (units > 0 ? units : 1);
+  int32_t part = round_up16((max_ctx + splits - 1) / splits);
+  if (part < 256) part = 256;
   return part >= whole ? whole : part;
 }
 
