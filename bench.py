@@ -41,7 +41,7 @@ WORKLOADS = {
     "long_mixed_decode": 5,
     "tiny_f32": 1,
 }
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_{name}_pmc.json")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_{name}_pmc.txt")
 
 
 def _source_hash():
@@ -58,11 +58,16 @@ def _traffic(name, decode_launch_bytes):
     path = PMC_SUMMARY.format(name=name)
     if not os.path.exists(path):
         return None
+    d = {}
     with open(path) as f:
-        d = json.load(f)
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            d[k.strip()] = v.strip()
     if d.get("source_hash") != _source_hash():
         return None
-    return d.get("hbm_bytes_per_call")
+    return int(float(d["hbm_bytes_per_call"]))
 
 
 def cpu_baseline(wl, budget_s=10.0):
