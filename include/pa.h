@@ -35,11 +35,14 @@
  *   K pool element (block b, kv head g, token offset o, dim x) at element index
  *       ((b * Hkv + g) * 16 + o) * D + x
  *   V pool element (b, g, o, x) at element index
- *       (((b * Hkv + g) * 8 + o / 2) * D + x) * 2 + o % 2
+ *       ((b * Hkv + g) * D + x) * 16 + o
  *   i.e. every (block, kv head) tile is one contiguous run (4 KiB for bf16
- *   with D = 128); K rows are token-major, V stores two consecutive tokens of
- *   one dim side by side.  The pages print three different block-internal
- *   orders; this one is chosen for full 128-byte reads on gfx950.
+ *   with D = 128); K rows are token-major (one token's D values together), V
+ *   rows are dim-major (one dim's 16 tokens together).  The pages print three
+ *   different block-internal orders; this one is chosen so that every tile
+ *   read is whole 128-byte lines on gfx950 and every 16-byte piece of a tile
+ *   is directly a matrix-core operand fragment (K: 8 dims of one token,
+ *   V: 8 tokens of one dim).
  */
 #ifndef PA_H
 #define PA_H

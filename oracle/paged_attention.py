@@ -37,10 +37,8 @@ here from its written definition, independently of the library:
 
 * K pool: element (block b, kv head g, token offset o, dim x) at
   ``((b * Hkv + g) * 16 + o) * D + x``.
-* V pool: element (b, g, o, x) at
-  ``(((b * Hkv + g) * 8 + o // 2) * D + x) * 2 + o % 2``  (token pairs
-  interleaved, so two consecutive tokens of one dim share a 32-bit word for
-  bf16).
+* V pool: element (b, g, o, x) at ``((b * Hkv + g) * D + x) * 16 + o``
+  (dim-major inside a tile: the 16 tokens of one dim are consecutive).
 """
 
 from __future__ import annotations
@@ -115,11 +113,8 @@ def k_pool_bytes(pool_k: np.ndarray) -> np.ndarray:
 
 
 def v_pool_bytes(pool_v: np.ndarray) -> np.ndarray:
-    """The V pool in the library's physical order
-    [block][kv head][token pair][dim][token within pair]."""
-    nb, bs, hkv, d = pool_v.shape
-    t = pool_v.reshape(nb, bs // 2, 2, hkv, d)  # [b][pair][o%2][g][x]
-    return np.ascontiguousarray(t.transpose(0, 3, 1, 4, 2)).reshape(-1)
+    """The V pool in the library's physical order [block][kv head][dim][token]."""
+    return np.ascontiguousarray(pool_v.transpose(0, 2, 3, 1)).reshape(-1)
 
 
 def k_pool_from_bytes(flat: np.ndarray, num_blocks, num_kv_heads, head_dim) -> np.ndarray:
@@ -128,9 +123,8 @@ def k_pool_from_bytes(flat: np.ndarray, num_blocks, num_kv_heads, head_dim) -> n
 
 
 def v_pool_from_bytes(flat: np.ndarray, num_blocks, num_kv_heads, head_dim) -> np.ndarray:
-    t = np.asarray(flat).reshape(num_blocks, num_kv_heads, BLOCK_SIZE // 2, head_dim, 2)
-    t = t.transpose(0, 2, 4, 1, 3)  # [b][pair][o%2][g][x]
-    return np.ascontiguousarray(t).reshape(num_blocks, BLOCK_SIZE, num_kv_heads, head_dim)
+    t = np.asarray(flat).reshape(num_blocks, num_kv_heads, head_dim, BLOCK_SIZE)
+    return np.ascontiguousarray(t.transpose(0, 3, 1, 2))
 
 
 # ----------------------------------------------------------------------------

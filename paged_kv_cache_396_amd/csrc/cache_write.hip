@@ -6,8 +6,9 @@
 // raw bits (no conversion), so the result is bit-exact by construction.
 //
 // One thread moves one 16-byte chunk of a (token, kv head) row.  K rows land
-// as contiguous 16-byte stores; V elements are interleaved by token pair in
-// the pool, so each element goes out as its own 2- or 4-byte store.
+// as contiguous 16-byte stores; the V tile is dim-major (16 tokens of one dim
+// together), so each V element of the row goes out as its own 2- or 4-byte
+// store, 16 elements apart.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -37,23 +38,23 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int64_t kdst = (base + (int64_t)o * head_dim) * EB / 16 + chunk;
   k_cache[kdst] = kv;
 
-  // V: element (b, g, o, x) at base + ((o / 2) * D + x) * 2 + o % 2
+  // V: element (b, g, o, x) at base + x * 16 + o
   constexpr int E = 16 / EB;  // elements in this chunk
   const int x0 = chunk * E;
-  const int64_t vrow = base + (int64_t)(o >> 1) * head_dim * 2 + (o & 1);
+  const int64_t vrow = base + (int64_t)x0 * kBlock + o;
   if constexpr (EB == 2) {
     uint16_t* dst = reinterpret_cast<uint16_t*>(v_cache) + vrow;
     const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint32_t word = w[e >> 1];
-      dst[(int64_t)(x0 + e) * 2] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
+      dst[e * kBlock] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
     }
   } else {
     uint32_t* dst = reinterpret_cast<uint32_t*>(v_cache) + vrow;
     const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[(int64_t)(x0 + e) * 2] = w[e];
+    for (int e = 0; e < E; ++e) dst[e * kBlock] = w[e];
   }
 }
 

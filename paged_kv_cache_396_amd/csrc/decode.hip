@@ -26,9 +26,11 @@
 //    block is rare; the rescale is exact whenever it happens, so the result
 //    is the same softmax (the reference max only has to be common to all
 //    terms that are summed together).
-//  * P.V: probabilities go through LDS as bf16 pairs of consecutive tokens;
-//    V stores token pairs side by side, so each lane does bf16 dot2 over the
-//    pair for its 4 dims and all G heads, accumulating fp32.
+//  * P.V: V tiles are dim-major, so a lane's 16-byte V chunk holds 8 (bf16)
+//    or 4 (fp32) consecutive tokens of one dim.  Probabilities go through LDS
+//    as bf16 pairs of consecutive tokens; each lane does bf16 dot2 over token
+//    pairs for its dims and all G heads, accumulating fp32, and the lanes
+//    that hold the other tokens of the same dims are summed at the end.
 //  * the 4 waves merge their (m, l, O) in LDS with the same rescale.  With
 //    one partition the workgroup writes the output; otherwise it writes its
 //    partial state and decode_reduce merges the partitions.
@@ -81,15 +83,15 @@ struct DecodeCfg {
   static constexpr int HEAD_BITS = (HEAD_SPAN - 1) << AR;
   static constexpr int DUP_BITS = (1 << AR) - 1;     // lanes holding identical scores
   static constexpr int ROW_BITS = (kWave - 1) & ~(LPR - 1);
-  // V: 8 pair-rows of 2*RB bytes per tile
-  static constexpr int VCH = 2 * RB / 16;            // chunks per pair-row
-  static constexpr int VL = VCH < kWave ? VCH : kWave;  // lanes per pair-row
-  static constexpr int NPV = 8 * VL / kWave;         // pair-rows per lane
-  static constexpr int XPC = 16 / (2 * EB);          // dims per chunk
-  static constexpr int VGRP_BITS = (kWave - 1) & ~(VL - 1);
+  // V: D dim-rows of 16 tokens per tile; chunk i of lane l is chunk
+  // l + 64 i of the tile: dim (l + 64 i) / VCPR, tokens VTPC * (l % VCPR) ..
+  static constexpr int VTPC = 16 / EB;               // tokens per V chunk
+  static constexpr int VCPR = kBlock / VTPC;         // chunks per dim-row (= EB)
+  static constexpr int NV = D * VCPR / kWave;        // V chunks (dims) per lane
+  static constexpr int VPART_BITS = VCPR - 1;        // lanes holding other tokens of our dims
   static constexpr int PWORDS = EB == 2 ? 1 : 2;     // 32-bit words per (pair, head) of P
   static_assert(NF <= 2 && NF <= NR, "unsupported GQA group for this head size");
-  static_assert(VCH % VL == 0 && VCH / VL == 1, "V chunk mapping");
+  static_assert(NV >= 1 && D * VCPR % kWave == 0, "V chunk mapping");
 };
 
 struct DecodeParams {
@@ -188,8 +190,8 @@ void decode_partition_kernel(DecodeParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int c = lane & (C::LPR - 1);  // lane within its K row
   const int r = lane / C::LPR;        // row group
-  const int vgrp = lane / C::VL;      // V pair-row group
-  const int xc = lane & (C::VL - 1);  // V chunk within a pair-row
+  const int vpart = lane & C::VPART_BITS;  // which tokens of a dim-row this lane holds
+  const int vdim0 = lane / C::VCPR;        // first of this lane's dims (stride 64 / VCPR)
   const int b0 = part * p.partition_blocks;
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
 
@@ -217,11 +219,11 @@ void decode_partition_kernel(DecodeParams p) {
   if (part >= nparts) return;  // uniform over the workgroup
   const int b1 = min(nblk, b0 + p.partition_blocks);
 
-  float o[G][C::XPC];
+  float o[G][C::NV];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int x = 0; x < C::XPC; ++x) o[h][x] = 0.f;
+    for (int x = 0; x < C::NV; ++x) o[h][x] = 0.f;
   float m_mine = kNegBig;  // reference max (log2 units) of this lane's head
   float l_mine = 0.f;      // sum of this lane's probabilities
 
@@ -238,12 +240,12 @@ void decode_partition_kernel(DecodeParams p) {
     my_ids = jb < b1 ? bt[jb] : 0;
   };
 
-  uint4 kb[2][C::NR][C::U], vb[2][C::NPV];  // two tile slots
+  uint4 kb[2][C::NR][C::U], vb[2][C::NV];  // two tile slots
   // Tile loads go through a per-tile buffer descriptor.  A tile that must not
   // be read (past the end of the chunk, or a block id outside the pool) gets
   // a descriptor with no records: its loads return zeros without touching
   // memory but still retire in order, which keeps every wait count static.
-  auto load_tile = [&](int id, bool real, uint4 (&kk)[C::NR][C::U], uint4 (&vv)[C::NPV]) {
+  auto load_tile = [&](int id, bool real, uint4 (&kk)[C::NR][C::U], uint4 (&vv)[C::NV]) {
     const int64_t base = ((int64_t)id * p.num_kv_heads + g) * tile_bytes;
     const int nrec = real ? (int)tile_bytes : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k_cache + base, nrec);
@@ -254,13 +256,12 @@ void decode_partition_kernel(DecodeParams p) {
       for (int u = 0; u < C::U; ++u)
         kk[i][u] = load16(kr, (r * C::NR + i) * C::RB + (u * C::LPR + c) * 16);
 #pragma unroll
-    for (int i = 0; i < C::NPV; ++i)
-      vv[i] = load16(vr, (vgrp + (kWave / C::VL) * i) * 2 * C::RB + xc * 16);
+    for (int i = 0; i < C::NV; ++i) vv[i] = load16(vr, (lane + kWave * i) * 16);
   };
   auto id_ok = [&](int id) { return id >= 0 && id < p.num_blocks; };
   const int nmine = b1 > b0 + w ? (b1 - b0 - w + NW - 1) / NW : 0;
 
-  auto process = [&](uint4 (&kc)[C::NR][C::U], uint4 (&vc)[C::NPV], int id_cur, int n) {
+  auto process = [&](uint4 (&kc)[C::NR][C::U], uint4 (&vc)[C::NV], int id_cur, int n) {
     const int jblk = b0 + w + NW * n;
     const bool bad_cur = id_cur < 0 || id_cur >= p.num_blocks;
 
@@ -301,19 +302,21 @@ void decode_partition_kernel(DecodeParams p) {
     }
     if (nvalid < kBlock) {
       // zero V of hidden tokens: a zero probability must not meet a NaN
+      uint32_t keep[4];
 #pragma unroll
-      for (int i = 0; i < C::NPV; ++i) {
-        const int t0 = 2 * (vgrp + (kWave / C::VL) * i);
-        uint32_t* wv = (uint32_t*)&vc[i];
+      for (int e = 0; e < 4; ++e) {
         if constexpr (EB == 2) {
-          const uint32_t keep = t0 >= nvalid ? 0u : (t0 + 1 >= nvalid ? 0x0000ffffu : 0xffffffffu);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) wv[e] &= keep;
+          const int t0 = vpart * C::VTPC + 2 * e;
+          keep[e] = t0 >= nvalid ? 0u : (t0 + 1 >= nvalid ? 0x0000ffffu : 0xffffffffu);
         } else {
-          const uint32_t k0 = t0 >= nvalid ? 0u : 0xffffffffu;
-          const uint32_t k1 = t0 + 1 >= nvalid ? 0u : 0xffffffffu;
-          wv[0] &= k0; wv[1] &= k1; wv[2] &= k0; wv[3] &= k1;
+          keep[e] = vpart * C::VTPC + e >= nvalid ? 0u : 0xffffffffu;
         }
+      }
+#pragma unroll
+      for (int i = 0; i < C::NV; ++i) {
+        uint32_t* wv = (uint32_t*)&vc[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] &= keep[e];
       }
     }
 
@@ -335,7 +338,7 @@ void decode_partition_kernel(DecodeParams p) {
         const float ah = __int_as_float(
             __builtin_amdgcn_readlane(__float_as_int(alpha), (h * C::HEAD_SPAN) << C::AR));
 #pragma unroll
-        for (int x = 0; x < C::XPC; ++x) o[h][x] *= ah;
+        for (int x = 0; x < C::NV; ++x) o[h][x] *= ah;
       }
     }
     float pr[C::NF];
@@ -365,13 +368,12 @@ void decode_partition_kernel(DecodeParams p) {
     }
     __builtin_amdgcn_wave_barrier();
 
-    // ---- P.V
+    // ---- P.V: word e of a V chunk holds tokens 2e, 2e+1 of the chunk (bf16)
+    // or token e (fp32)
 #pragma unroll
-    for (int i = 0; i < C::NPV; ++i) {
-      const int tp = vgrp + (kWave / C::VL) * i;
-      const uint4 vv = vc[i];
-      const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+    for (int e = 0; e < 4; ++e) {
       if constexpr (EB == 2) {
+        const int tp = vpart * (C::VTPC / 2) + e;  // token pair within the block
         uint32_t pw[G];
         if constexpr (G % 4 == 0) {
 #pragma unroll
@@ -385,18 +387,21 @@ void decode_partition_kernel(DecodeParams p) {
           for (int h = 0; h < G; ++h) pw[h] = pb[tp * G + h];
         }
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int i = 0; i < C::NV; ++i) {
+          const uint32_t wv = ((const uint32_t*)&vc[i])[e];
 #pragma unroll
-          for (int x = 0; x < C::XPC; ++x) o[h][x] = dot2_bf16(pw[h], wv[x], o[h][x]);
+          for (int h = 0; h < G; ++h) o[h][i] = dot2_bf16(pw[h], wv, o[h][i]);
+        }
       } else {
+        const int t = vpart * C::VTPC + e;  // token within the block
+        float pp[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float2 pp = *(const float2*)&pb[(tp * G + h) * 2];
+        for (int h = 0; h < G; ++h) pp[h] = ((const float*)pb)[((t >> 1) * G + h) * 2 + (t & 1)];
 #pragma unroll
-          for (int x = 0; x < C::XPC; ++x) {
-            o[h][x] = fmaf(pp.x, __uint_as_float(wv[2 * x]), o[h][x]);
-            o[h][x] = fmaf(pp.y, __uint_as_float(wv[2 * x + 1]), o[h][x]);
-          }
+        for (int i = 0; i < C::NV; ++i) {
+          const float vf = __uint_as_float(((const uint32_t*)&vc[i])[e]);
+#pragma unroll
+          for (int h = 0; h < G; ++h) o[h][i] = fmaf(pp[h], vf, o[h][i]);
         }
       }
     }
@@ -426,17 +431,17 @@ void decode_partition_kernel(DecodeParams p) {
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int x = 0; x < C::XPC; ++x) o[h][x] = group_sum<C::VGRP_BITS>(o[h][x]);
+    for (int x = 0; x < C::NV; ++x) o[h][x] = group_sum<C::VPART_BITS>(o[h][x]);
 
   if ((lane & (C::ROW_BITS | C::HEAD_BITS | C::DUP_BITS)) == 0) {
     sm[w][hh] = m_mine;
     sl[w][hh] = l_head;
   }
-  if (vgrp == 0) {
+  if (vpart == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int x = 0; x < C::XPC; ++x) so[w][h][xc * C::XPC + x] = o[h][x];
+      for (int x = 0; x < C::NV; ++x) so[w][h][vdim0 + (kWave / C::VCPR) * x] = o[h][x];
   }
   __syncthreads();
 

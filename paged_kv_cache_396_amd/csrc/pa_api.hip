@@ -237,6 +237,10 @@ PA_API int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const
   if (num_reqs == 0 || total_q_tokens == 0 || max_q_len == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
     return fail(PA_ERR_NULL, "prefill pointers must be non-NULL");
+  const int64_t qt = pa::prefill_queries_per_tile(group);
+  if ((max_q_len + qt - 1) / qt * (int64_t)num_reqs * g.num_kv_heads >= ((int64_t)1 << 31) ||
+      (int64_t)total_q_tokens * num_q_heads * g.head_dim >= ((int64_t)1 << 40))
+    return fail(PA_ERR_OVERFLOW, "prefill grid too large");
   pa::PrefillArgs a;
   a.out = out;
   a.q = q;

@@ -16,7 +16,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // Pool layout.  One (block, kv head) tile is contiguous:
 //   K: [16 tokens][D]          (token-major rows)
-//   V: [8 token pairs][D][2]   (two consecutive tokens of a dim side by side)
+//   V: [D][16 tokens]          (dim-major rows)
 // Both tiles hold 16 * D elements, so the tile base is the same for K and V.
 __host__ __device__ constexpr int64_t tile_elems(int D) { return (int64_t)kBlock * D; }
 

@@ -58,6 +58,9 @@ struct PrefillArgs {
 
 bool prefill_supported(int elem_bytes, int head_dim, int group);
 
+// Query rows one prefill workgroup covers for GQA group size `group`.
+int prefill_queries_per_tile(int group);
+
 hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t stream);
 
 }  // namespace pa

@@ -1,14 +1,444 @@
-// Chunked-prefill attention over paged KV (bf16 MFMA).  Not built yet: the
-// entry point reports PA_ERR_UNSUPPORTED until the kernel lands.
+// Chunked-prefill attention over paged KV for gfx950 (bf16 matrix cores).
+//
+// What is computed: a long prompt is processed one chunk at a time, and the
+// tokens of one step from several requests are flattened into one batch
+// (zihan-zhang.net vLLM study, 3.5 and the model-runner part of 5.x).  For
+// request r with chunk rows query_start_loc[r] .. query_start_loc[r+1]-1
+// (n_r of them) and context ctx_r (prior tokens plus the chunk, all already in
+// the pools), query i sits at position pos = ctx_r - n_r + i and attends
+// causally (same page, 1.1.1) to keys 0 .. pos:
+//   out[i, h] = softmax(scale * K[0..pos, h/G] q[i, h]) V[0..pos, h/G]
+// with K and V read block by block through the request's block table
+// (same page, 3.2) and the softmax evaluated online (same page, 4.3.1).
+//
+// Mapping onto CDNA4:
+//  * one workgroup of 4 waves per (request, kv head, tile of query rows).
+//    A "column" is one (query, q head) pair; the G q heads of the kv head and
+//    QT consecutive queries give 128 * NCB columns, 32 * NCB per wave.
+//    Workgroup ids are mapped so that all tiles of one (request, kv head)
+//    run on the same XCD and share its L2 copy of the K/V tiles.
+//  * the workgroup walks the keys 64 at a time (four 16-token blocks).  The
+//    K and V tiles of the four blocks are copied from the pools into LDS
+//    (double buffered, the next tile's global loads in flight while the
+//    current one is computed).  Blocks past the context are never read.
+//  * scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16 (32 keys x 32 columns per instruction), so
+//    each lane holds one column's scores for 16 keys and the row max of the
+//    softmax needs a single exchange between the two lane halves.  The MFMA
+//    row -> key assignment is permuted so that the 8 fp32 scores a lane holds
+//    for one 16-key step are 8 consecutive keys: after conversion to bf16
+//    they are directly the B operand of the P V product.
+//  * O^T = V^T P accumulates in fp32 (32 dims x 32 columns per instruction);
+//    the V tile in LDS is dim-major, so each A fragment is one 16-byte read.
+//  * softmax state (running max in log2 units, running sum) is per lane;
+//    the max is raised only when a score exceeds it by more than 2^8 (the
+//    rescale is exact when it happens; any common reference max gives the
+//    same softmax).  P is rounded to bf16 for the matrix product.
+#include <float.h>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
-bool prefill_supported(int, int, int) { return false; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-hipError_t launch_prefill(const PrefillArgs&, const CacheGeom&, hipStream_t) {
-  return hipErrorNotSupported;
+constexpr int kPfWaves = 4;        // waves per workgroup
+constexpr int kPfKT = 64;          // keys per iteration (four 16-token blocks)
+constexpr int kPfBlocks = kPfKT / kBlock;
+constexpr float kPfGap = 8.0f;     // log2 units a score may exceed the reference max
+constexpr float kPfNegBig = -FLT_MAX;
+
+template <int D>
+struct PrefillCfg {
+  static constexpr int RB = D * 2;             // bytes of one K row (bf16)
+  static constexpr int KCH = RB / 16;          // 16-byte chunks per K row
+  static constexpr int KROWS_PER_256 = 256 / RB;
+  static constexpr int DS = D / 16;            // k-steps of S^T = K Q^T
+  static constexpr int DB = D / 32;            // 32-dim blocks of O^T
+  static constexpr int VRB = kPfKT * 2;        // bytes of one V row (one dim) in LDS
+  static constexpr int K_LDS = kPfKT * RB;     // one K stage
+  static constexpr int V_LDS = D * VRB;        // one V stage
+  static constexpr int STAGE = K_LDS + V_LDS;
+  static constexpr int NKL = kPfKT * KCH / (kPfWaves * kWave);  // K chunks per thread
+  static constexpr int NVL = 2 * D * kPfBlocks / (kPfWaves * kWave);  // V chunks per thread
+  static_assert(NKL >= 1 && NVL >= 1, "tile too small for the workgroup");
+};
+
+struct PrefillParams {
+  void* out;
+  const char* q;
+  const char* k_cache;
+  const char* v_cache;
+  const int32_t* block_tables;
+  const int32_t* query_start_loc;
+  const int32_t* context_lens;
+  int max_blocks_per_seq;
+  int num_reqs;
+  int total_q_tokens;
+  int num_q_heads;
+  int num_kv_heads;
+  int num_blocks;
+  int num_qtiles;
+  float scale_log2;
+};
+
+// LDS byte offset of 16-byte chunk c of K row `row` (XOR swizzle: the 32 rows
+// one MFMA fragment reads at a fixed chunk fall on distinct banks).
+template <int D>
+__device__ inline int k_lds_off(int row, int c) {
+  using C = PrefillCfg<D>;
+  return row * C::RB + ((c ^ ((row / C::KROWS_PER_256) % C::KCH)) << 4);
+}
+// LDS byte offset of 16-byte chunk c (keys 8c .. 8c+7) of V row `dim`.
+template <int D>
+__device__ inline int v_lds_off(int dim, int c) {
+  using C = PrefillCfg<D>;
+  return C::K_LDS + dim * C::VRB + ((c ^ ((dim >> 1) & 7)) << 4);
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t pf_rsrc(const char* ptr, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0, bytes, 0x00020000);
+}
+__device__ inline uint4 pf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Key (within a 32-key block) that MFMA row m of S^T stands for.  Rows are
+// permuted inside each group of 16 (quads 1 and 2 swapped) so that the
+// accumulator registers 8t..8t+7 of lane l hold keys 16t + 8(l/32) + 0..7.
+__device__ inline int pf_row_key(int m) {
+  const int quad = (m >> 2) & 3;
+  const int sq = quad == 1 ? 2 : quad == 2 ? 1 : quad;
+  return (m & 16) + sq * 4 + (m & 3);
+}
+
+template <int D, int G, int NCB>
+__global__ __launch_bounds__(kPfWaves * kWave) void prefill_chunk_kernel(PrefillParams p) {
+  using C = PrefillCfg<D>;
+  constexpr int COLS = kPfWaves * 32 * NCB;  // columns per workgroup
+  constexpr int QT = COLS / G;               // queries per workgroup
+  static_assert(COLS % G == 0, "group must divide the column tile");
+
+  __shared__ __attribute__((aligned(16))) char lds[2][C::STAGE];
+
+  // ---- which (request, kv head, query tile): tiles of one (request, kv
+  // head) are consecutive in the "logical" order, and logical runs are
+  // assigned to one XCD (workgroups go round-robin over the 8 XCDs)
+  const int N = p.num_qtiles * p.num_reqs * p.num_kv_heads;
+  const int L = blockIdx.x;
+  const int xcd = L & 7, slot = L >> 3;
+  const int per = N >> 3, rem = N & 7;
+  const int logical = xcd * per + min(xcd, rem) + slot;
+  const int tile = logical % p.num_qtiles;
+  const int pair = logical / p.num_qtiles;
+  const int g = pair % p.num_kv_heads;
+  const int r = pair / p.num_kv_heads;
+
+  int qs = p.query_start_loc[r];
+  int qe = p.query_start_loc[r + 1];
+  qs = max(0, min(qs, p.total_q_tokens));
+  qe = max(qs, min(qe, p.total_q_tokens));
+  const int n_r = qe - qs;
+  const int q0 = tile * QT;
+  if (q0 >= n_r) return;  // uniform
+  const int ctx_cap = p.max_blocks_per_seq * kBlock;
+  const int ctx = max(0, min(p.context_lens[r], ctx_cap));
+  const int prior = ctx - n_r;  // < 0 only for out-of-contract input
+  const int q_end = min(n_r, q0 + QT);
+  const int nk = max(0, min(ctx, prior + q_end));  // keys this workgroup needs
+  const int iters = (nk + kPfKT - 1) / kPfKT;
+  const int nblk = (ctx + kBlock - 1) / kBlock;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int half = lane >> 5;
+  const int cw = lane & 31;
+  const int32_t* bt = p.block_tables + (int64_t)r * p.max_blocks_per_seq;
+
+  // ---- this lane's columns and their query positions
+  int pos[NCB];
+  uint4 qf[NCB][C::DS];
+  int wave_max_pos = -1, wave_min_pos = 0x7fffffff;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int c = 32 * (w * NCB + cb) + cw;
+    const int qi = q0 + c / G;
+    const int hh = c % G;
+    const bool valid = qi < n_r;
+    pos[cb] = valid ? prior + qi : -1;
+    const char* qrow = p.q + ((int64_t)(qs + (valid ? qi : 0)) * p.num_q_heads + g * G + hh) * C::RB;
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s)
+      qf[cb][s] = valid ? *(const uint4*)(qrow + (2 * s + half) * 16) : make_uint4(0, 0, 0, 0);
+    // first and last query of this column block (columns are query-major)
+    const int qa = q0 + (32 * (w * NCB + cb)) / G;
+    const int qb = min(n_r - 1, q0 + (32 * (w * NCB + cb) + 31) / G);
+    if (qa < n_r) {
+      wave_max_pos = max(wave_max_pos, prior + qb);
+      wave_min_pos = min(wave_min_pos, prior + qa);
+    }
+  }
+  if (q0 + (32 * (w * NCB + NCB - 1) + 31) / G >= n_r) wave_min_pos = -1;  // has padding columns
+
+  f32x16_t acco[NCB][C::DB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acco[cb][db][i] = 0.f;
+  float m_run[NCB], l_run[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    m_run[cb] = kPfNegBig;
+    l_run[cb] = 0.f;
+  }
+
+  // ---- global -> register -> LDS staging of one 64-key tile
+  uint4 kreg[C::NKL], vreg[C::NVL];
+  auto block_id = [&](int jb) -> int {
+    if (jb >= nblk) return -1;
+    const int id = bt[jb];
+    return (id >= 0 && id < p.num_blocks) ? id : -1;
+  };
+  int ids[kPfBlocks];
+  auto fetch_ids = [&](int it) {
+#pragma unroll
+    for (int b = 0; b < kPfBlocks; ++b) ids[b] = block_id(it * kPfBlocks + b);
+  };
+  auto id_of = [&](int b) {
+    int v = ids[0];
+#pragma unroll
+    for (int bb = 1; bb < kPfBlocks; ++bb) v = b == bb ? ids[bb] : v;
+    return v;
+  };
+  const int64_t tile_bytes = (int64_t)kBlock * C::RB;
+  auto global_load = [&]() {
+#pragma unroll
+    for (int u = 0; u < C::NKL; ++u) {
+      const int ci = tid + kPfWaves * kWave * u;
+      const int key = ci / C::KCH;
+      const int b = __builtin_amdgcn_readfirstlane(key / kBlock);  // uniform per wave
+      const int id = id_of(b);
+      const __amdgpu_buffer_rsrc_t rs =
+          pf_rsrc(p.k_cache + ((int64_t)max(id, 0) * p.num_kv_heads + g) * tile_bytes,
+                  id >= 0 ? (int)tile_bytes : 0);
+      kreg[u] = pf_load16(rs, (key % kBlock) * C::RB + (ci % C::KCH) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < C::NVL; ++u) {
+      const int ci = tid + kPfWaves * kWave * u;
+      const int b = __builtin_amdgcn_readfirstlane(ci / (2 * D));
+      const int id = id_of(b);
+      const __amdgpu_buffer_rsrc_t rs =
+          pf_rsrc(p.v_cache + ((int64_t)max(id, 0) * p.num_kv_heads + g) * tile_bytes,
+                  id >= 0 ? (int)tile_bytes : 0);
+      vreg[u] = pf_load16(rs, (ci % (2 * D)) * 16);
+    }
+  };
+  auto lds_store = [&](int it, char* st) {
+#pragma unroll
+    for (int u = 0; u < C::NKL; ++u) {
+      const int ci = tid + kPfWaves * kWave * u;
+      *(uint4*)(st + k_lds_off<D>(ci / C::KCH, ci % C::KCH)) = kreg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < C::NVL; ++u) {
+      const int ci = tid + kPfWaves * kWave * u;
+      const int b = ci / (2 * D);
+      const int wi = ci % (2 * D);
+      const int dim = wi >> 1, hv = wi & 1;
+      // keys past the context hold whatever the pool has (possibly NaN): a
+      // zero probability must meet a finite value, so clear them here
+      const int key0 = it * kPfKT + b * kBlock + hv * 8;
+      uint4 v = vreg[u];
+      if (key0 + 8 > ctx) {
+        uint32_t* wv = (uint32_t*)&v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = key0 + 2 * e;
+          wv[e] &= t >= ctx ? 0u : (t + 1 >= ctx ? 0x0000ffffu : 0xffffffffu);
+        }
+      }
+      *(uint4*)(st + v_lds_off<D>(dim, 2 * b + hv)) = v;
+    }
+  };
+
+  if (iters > 0) {
+    fetch_ids(0);
+    global_load();
+    if (iters > 1) fetch_ids(1);
+    lds_store(0, lds[0]);
+  }
+
+  const int krow = pf_row_key(cw);  // key (within a 32-key block) of this lane's MFMA row
+
+  for (int it = 0; it < iters; ++it) {
+    __syncthreads();
+    if (it + 1 < iters) {
+      global_load();
+      if (it + 2 < iters) fetch_ids(it + 2);
+    }
+    const char* st = lds[it & 1];
+    const int k0 = it * kPfKT;
+    if (k0 <= wave_max_pos) {
+      // ---- S^T = K Q^T for 64 keys x 32*NCB columns
+      f32x16_t sacc[NCB][2];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[cb][kb][i] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          const uint4 a = *(const uint4*)(st + k_lds_off<D>(32 * kb + krow, 2 * s + half));
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            sacc[cb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qf[cb][s]),
+                sacc[cb][kb], 0, 0, 0);
+        }
+
+      // ---- online softmax per column; register i of key block kb is key
+      // k0 + 32 kb + 16 (i / 8) + 8 half + i % 8
+      const bool need_mask = k0 + kPfKT - 1 > wave_min_pos;
+      bf16x8_t pf[NCB][2][2];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        float z[2][16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float v = sacc[cb][kb][i] * p.scale_log2;
+            if (need_mask) {
+              const int key = k0 + 32 * kb + 16 * (i >> 3) + 8 * half + (i & 7);
+              v = key <= pos[cb] ? v : -INFINITY;
+            }
+            z[kb][i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, xor_lane<32>(mx));
+        const bool over = mx > m_run[cb] + kPfGap;
+        if (__builtin_amdgcn_ballot_w64(over)) {
+          const float m_new = fmaxf(m_run[cb], mx);
+          const float alpha = exp2f(m_run[cb] - m_new);
+          m_run[cb] = m_new;
+          l_run[cb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acco[cb][db][i] *= alpha;
+        }
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            uint32_t wds[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = exp2f(z[kb][8 * t + 2 * e] - m_run[cb]);
+              const float p1 = exp2f(z[kb][8 * t + 2 * e + 1] - m_run[cb]);
+              lsum += p0 + p1;
+              wds[e] = pack_bf16(p0, p1);
+            }
+            pf[cb][kb][t] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
+          }
+        l_run[cb] += lsum;
+      }
+
+      // ---- O^T += V^T P
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const uint4 a = *(const uint4*)(st + v_lds_off<D>(32 * db + cw, 4 * kb + 2 * t + half));
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              acco[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8_t, a), pf[cb][kb][t], acco[cb][db], 0, 0, 0);
+          }
+    }
+    if (it + 1 < iters) lds_store(it + 1, lds[(it + 1) & 1]);
+  }
+
+  // ---- normalise and store: register i of dim block db is dim
+  // 32 db + 8 (i / 4) + 4 half + i % 4 of this lane's column
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const float lt = l_run[cb] + xor_lane<32>(l_run[cb]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int c = 32 * (w * NCB + cb) + cw;
+    const int qi = q0 + c / G;
+    if (qi >= n_r) continue;
+    char* orow = (char*)p.out + ((int64_t)(qs + qi) * p.num_q_heads + g * G + c % G) * C::RB;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x16_t& a = acco[cb][db];
+        uint2 v;
+        v.x = pack_bf16(a[4 * i4 + 0] * inv, a[4 * i4 + 1] * inv);
+        v.y = pack_bf16(a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv);
+        *(uint2*)(orow + (32 * db + 8 * i4 + 4 * half) * 2) = v;
+      }
+  }
+}
+
+template <int D, int G>
+static hipError_t launch_prefill_t(const PrefillParams& prm, hipStream_t stream) {
+  constexpr int NCB = 1;
+  const int64_t grid = (int64_t)prm.num_qtiles * prm.num_reqs * prm.num_kv_heads;
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB>), dim3((unsigned)grid),
+                     dim3(kPfWaves * kWave), 0, stream, prm);
+  return hipGetLastError();
+}
+
+int prefill_queries_per_tile(int group) { return kPfWaves * 32 / group; }
+
+bool prefill_supported(int elem_bytes, int head_dim, int group) {
+  return elem_bytes == 2 && (head_dim == 64 || head_dim == 128) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t stream) {
+  PrefillParams p;
+  p.out = a.out;
+  p.q = (const char*)a.q;
+  p.k_cache = (const char*)a.k_cache;
+  p.v_cache = (const char*)a.v_cache;
+  p.block_tables = a.block_tables;
+  p.query_start_loc = a.query_start_loc;
+  p.context_lens = a.context_lens;
+  p.max_blocks_per_seq = a.max_blocks_per_seq;
+  p.num_reqs = a.num_reqs;
+  p.total_q_tokens = a.total_q_tokens;
+  p.num_q_heads = a.num_q_heads;
+  p.num_kv_heads = g.num_kv_heads;
+  p.num_blocks = g.num_blocks;
+  p.scale_log2 = a.scale * kLog2e;
+  const int G = a.num_q_heads / g.num_kv_heads;
+  const int qt = prefill_queries_per_tile(G);
+  p.num_qtiles = (a.max_q_len + qt - 1) / qt;
+
+#define PA_PREFILL_CASE(D_, G_) \
+  if (g.head_dim == D_ && G == G_) return launch_prefill_t<D_, G_>(p, stream);
+  PA_PREFILL_CASE(128, 1) PA_PREFILL_CASE(128, 2) PA_PREFILL_CASE(128, 4) PA_PREFILL_CASE(128, 8)
+  PA_PREFILL_CASE(64, 1) PA_PREFILL_CASE(64, 2) PA_PREFILL_CASE(64, 4) PA_PREFILL_CASE(64, 8)
+#undef PA_PREFILL_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

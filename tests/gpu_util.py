@@ -133,3 +133,20 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
         assert not bad.any(), (
             f"{what}: {int(bad.sum())} elements outside atol/rtol 2e-2; max abs err {err.max():.3g}")
     return float(err.max()) if err.size else 0.0
+
+
+def gpu_prefill(wl, pool, max_q_len=None, query_start_loc=None, context_lens=None):
+    """Run pa_prefill_chunk on a PrefillWorkload whose pool already holds the
+    prior and chunk K/V; returns the device output [total_q, Hq, D]."""
+    t = torch()
+    q = to_dev(wl.q, wl.dtype)
+    out = t.empty_like(q)
+    qsl_np = wl.query_start_loc if query_start_loc is None else query_start_loc
+    cl_np = wl.context_lens if context_lens is None else context_lens
+    bt = t.from_numpy(np.ascontiguousarray(wl.block_tables)).cuda()
+    qsl = t.from_numpy(np.ascontiguousarray(qsl_np, dtype=np.int32)).cuda()
+    cl = t.from_numpy(np.ascontiguousarray(cl_np, dtype=np.int32)).cuda()
+    mq = int(np.diff(qsl_np).max()) if max_q_len is None else int(max_q_len)
+    pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, mq, float(wl.scale), pool.desc)
+    t.cuda.synchronize()
+    return out

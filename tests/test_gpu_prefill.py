@@ -1,0 +1,123 @@
+"""Chunked prefill (bf16 matrix cores) on the GPU against the fp64 oracle.
+
+Tolerance: |gpu - ref| <= 2e-2 + 2e-2|ref| (bf16 inputs, fp32 accumulation,
+probabilities rounded to bf16 before the P.V product).  Pools are
+NaN-poisoned before any write: a stray read of an unreferenced block or of a
+slot past the context shows up as a non-finite output.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_decode, make_prefill, make_tiny_decode, make_tiny_prefill
+
+from gpu_util import (assert_close, gpu_decode, gpu_pool_for, gpu_prefill, log, oracle_pools,
+                      raw_bits, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_prefill(wl, rows=None):
+    pk, pv = oracle_pools(wl, oracle)
+    return oracle.prefill_chunk(wl.q, pk, pv, wl.block_tables, wl.query_start_loc,
+                                wl.context_lens, wl.scale, wl.dtype, rows=rows)
+
+
+SHAPES = [
+    # D, Hq, Hkv, prior, chunk
+    (128, 32, 8, (0, 5, 40), (7, 16, 33)),
+    (128, 32, 8, (0,), (1,)),
+    (128, 32, 8, (16, 100, 0, 63), (1, 15, 130, 64)),
+    (128, 64, 8, (3, 200), (17, 70)),
+    (128, 8, 4, (31, 0), (40, 129)),
+    (128, 4, 4, (10,), (200,)),
+    (128, 16, 2, (0, 77), (300, 5)),
+    (64, 16, 2, (9, 0), (20, 65)),
+    (64, 8, 8, (130,), (33,)),
+    (64, 32, 4, (0, 1), (64, 129)),
+]
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,prior,chunk", SHAPES)
+def test_tiny_prefill_shapes(D, Hq, Hkv, prior, chunk):
+    log(f"prefill tiny D={D} Hq={Hq} Hkv={Hkv} prior={prior} chunk={chunk}")
+    wl = make_tiny_prefill(seed=61 + D + Hq + sum(chunk), prior=prior, chunk=chunk, Hq=Hq,
+                           Hkv=Hkv, D=D)
+    out = to_f64(gpu_prefill(wl, gpu_pool_for(wl)))
+    assert_close(out, _oracle_prefill(wl), "bf16", f"prefill D={D} {Hq}/{Hkv}")
+
+
+def test_prefill_prior_zero_is_plain_causal_attention():
+    log("prefill prior 0")
+    wl = make_tiny_prefill(seed=3, prior=(0, 0), chunk=(100, 33), Hq=32, Hkv=8, D=128)
+    out = to_f64(gpu_prefill(wl, gpu_pool_for(wl)))
+    assert_close(out, _oracle_prefill(wl), "bf16", "prior 0")
+
+
+def test_prefill_permutation_of_physical_blocks_is_bitwise_invariant():
+    log("prefill permutation invariance")
+    a = make_tiny_prefill(seed=4, prior=(40, 300), chunk=(70, 129), Hq=32, Hkv=8, D=128,
+                          layout_variant=0)
+    b = make_tiny_prefill(seed=4, prior=(40, 300), chunk=(70, 129), Hq=32, Hkv=8, D=128,
+                          layout_variant=1)
+    assert not np.array_equal(a.block_tables, b.block_tables)
+    oa = gpu_prefill(a, gpu_pool_for(a))
+    ob = gpu_prefill(b, gpu_pool_for(b))
+    assert np.array_equal(raw_bits(oa), raw_bits(ob))
+
+
+def test_prefill_last_row_matches_decode():
+    """A chunk's last query sees the whole context, exactly as decode does."""
+    log("prefill last row vs decode")
+    wl = make_tiny_prefill(seed=5, prior=(90, 500, 0), chunk=(10, 64, 33), Hq=32, Hkv=8, D=128)
+    pool = gpu_pool_for(wl)
+    pre = to_f64(gpu_prefill(wl, pool))
+    last = wl.query_start_loc[1:] - 1
+
+    class _Dec:  # decode view of the same pool: one query per request (its last row)
+        pass
+
+    d = _Dec()
+    d.q = wl.q[last]
+    d.dtype, d.num_kv_heads, d.scale = wl.dtype, wl.num_kv_heads, wl.scale
+    d.block_tables, d.context_lens = wl.block_tables, wl.context_lens
+    dec = to_f64(gpu_decode(d, pool))
+    assert_close(pre[last], dec, "bf16", "last row vs decode")
+
+
+def test_prefill_two_half_chunks_equal_one_chunk():
+    """Splitting a chunk into two requests over the same table (the first half
+    with a shorter context) gives the same rows within tolerance."""
+    log("prefill split chunk")
+    wl = make_tiny_prefill(seed=6, prior=(200,), chunk=(96,), Hq=32, Hkv=8, D=128)
+    pool = gpu_pool_for(wl)
+    whole = to_f64(gpu_prefill(wl, pool))
+    ref = _oracle_prefill(wl)
+    assert_close(whole, ref, "bf16", "whole chunk")
+    # same block table twice: first 48 rows at ctx 248, next 48 at ctx 296
+    wl2 = make_tiny_prefill(seed=6, prior=(200,), chunk=(96,), Hq=32, Hkv=8, D=128)
+    wl2.block_tables = np.repeat(wl.block_tables, 2, axis=0)
+    split = to_f64(gpu_prefill(wl2, pool, query_start_loc=np.array([0, 48, 96], np.int32),
+                               context_lens=np.array([248, 296], np.int32)))
+    assert_close(split, ref, "bf16", "two half chunks")
+
+
+def test_prefill_unreferenced_rows_stay_finite_with_poison():
+    log("prefill poison")
+    wl = make_tiny_prefill(seed=7, prior=(1, 17, 33), chunk=(15, 1, 31), Hq=8, Hkv=2, D=128)
+    out = to_f64(gpu_prefill(wl, gpu_pool_for(wl)))
+    assert np.isfinite(out).all()
+    assert_close(out, _oracle_prefill(wl), "bf16", "poison")
+
+
+def test_config5_prefill_sampled():
+    """The long-context mixed batch's prefill half at full size: 4 requests,
+    512-token chunks against 4096 prior tokens; sampled rows checked."""
+    log("prefill config 5 (full launch, sampled check)")
+    wl = make_prefill(5)
+    out = to_f64(gpu_prefill(wl, gpu_pool_for(wl)))
+    assert np.isfinite(out).all()
+    rows = sorted(set(list(range(0, 2048, 37)) + [0, 511, 512, 1023, 1535, 2047]))
+    ref = _oracle_prefill(wl, rows=rows)
+    assert_close(out[rows], ref[rows], "bf16", "config 5 prefill sampled")

@@ -221,7 +221,7 @@ def test_physical_layout_matches_written_formula():
             for g in range(hkv):
                 for x in range(d):
                     assert kb[((b * hkv + g) * 16 + o) * d + x] == pool[b, o, g, x]
-                    assert vb[(((b * hkv + g) * 8 + o // 2) * d + x) * 2 + o % 2] == pool[b, o, g, x]
+                    assert vb[((b * hkv + g) * d + x) * 16 + o] == pool[b, o, g, x]
     assert np.array_equal(oracle.k_pool_from_bytes(kb, nb, hkv, d), pool)
     assert np.array_equal(oracle.v_pool_from_bytes(vb, nb, hkv, d), pool)
 
