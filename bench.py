@@ -10,6 +10,12 @@ sequences, context lengths U[128, 4096], 32 q / 8 kv heads, head_dim 128,
 bf16, 16-token blocks shuffled over a pool 1.25x the need.  All inputs are
 seeded synthetic data resident in HBM before timing starts.
 
+The same run also times pa_prefill_chunk on the prefill half of the
+long-context mixed batch (4 requests, 512-token causal chunks against 4096
+prior paged tokens, 32 q / 8 kv heads, head_dim 128, bf16) and reports it
+under ``prefill_chunk`` against the bf16 matrix-core peak (skip with
+--no-prefill).
+
 Prints one JSON line.  ``value`` is KV GB/s over the timed steps (the K/V
 bytes attention must read, one read per kv head, divided by step time);
 tokens/s and the HBM fraction are reported beside it.  ``roofline`` refers
@@ -34,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: KV GB/s and % of MI355X HBM peak; decode tokens/s"
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix-core peak
 WORKLOADS = {
     "llama3_8b_b64": 2,
     "llama2_70b_b256": 3,
@@ -106,6 +113,68 @@ def cpu_baseline(wl, budget_s=10.0):
     }
 
 
+def prefill_flops(wl):
+    """Causal-useful FLOPs of one pa_prefill_chunk call: every query row does
+    a 2-FLOP multiply-add per dim for Q.K and for P.V over the keys it sees."""
+    tot = 0
+    for r in range(wl.num_reqs):
+        n_r = int(wl.query_start_loc[r + 1] - wl.query_start_loc[r])
+        prior = int(wl.context_lens[r]) - n_r
+        tot += n_r * prior + n_r * (n_r + 1) // 2  # sum over i of (prior + i + 1)
+    return tot * wl.num_q_heads * 4 * wl.head_dim
+
+
+def bench_prefill(steps, warmup):
+    """Time pa_prefill_chunk on the long-context mixed batch's prefill half."""
+    import torch
+
+    import paged_kv_cache_396_amd as pa
+    from workloads import make_prefill
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import GpuPool, to_dev  # noqa: E402
+
+    wl = make_prefill(5)
+    pool = GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
+    pool.write(wl.hist_k, wl.hist_v, wl.hist_slots)
+    pool.write(wl.new_k, wl.new_v, wl.new_slots)
+    q = to_dev(wl.q, wl.dtype)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(wl.block_tables).cuda()
+    qsl = torch.from_numpy(wl.query_start_loc).cuda()
+    cl = torch.from_numpy(wl.context_lens).cuda()
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, wl.max_q_len, float(wl.scale),
+                            pool.desc)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    fl = prefill_flops(wl)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {
+        "workload": "long_mixed_prefill",
+        "num_reqs": wl.num_reqs, "chunk_tokens": int(wl.max_q_len),
+        "prior_tokens": int(wl.context_lens[0]) - int(wl.max_q_len),
+        "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+        "calls": steps, "call_ms": round(ms, 5), "causal_flops": fl,
+        "q_tokens_per_s": round(wl.total_q_tokens / (ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "kernel": "prefill_chunk_kernel", "achieved": round(tf, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +183,9 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_b64", choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=0, help="0 auto, <0 no split, >0 tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk timing")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only pa_prefill_chunk (for profiling it alone)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of the bench, run N plain 1 GiB device copies (counter calibration)")
@@ -144,6 +216,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": n, "copies": args.calib_copy}))
+        return
+
+    if args.prefill_only:
+        print(json.dumps({"prefill_chunk": bench_prefill(args.steps, args.warmup)}), flush=True)
         return
 
     cfg = WORKLOADS[args.workload]
@@ -239,6 +315,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_prefill:
+        line["prefill_chunk"] = bench_prefill(min(args.steps, 20), min(args.warmup, 3))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)

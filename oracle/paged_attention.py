@@ -24,7 +24,7 @@ What each function follows (the pages are cited by title and section):
   a negative slot marks a padding token and writes nothing.
 * Chunked prefill: a long prompt is processed chunk by chunk; a chunk's
   queries are the last tokens of the context and attend causally to every
-  earlier token (zihan-zhang.net vLLM study, 3.5; batch metadata as in 5.x).
+  earlier token (zihan-zhang.net vLLM study, 3.5; flattened batch metadata, 5.6).
 * GQA: query head ``h`` reads kv head ``h // (Hq / Hkv)`` (contiguous groups).
 
 Because paging only changes where bytes live, the oracle reaches the exact

@@ -2,7 +2,7 @@
 //
 // What is computed: a long prompt is processed one chunk at a time, and the
 // tokens of one step from several requests are flattened into one batch
-// (zihan-zhang.net vLLM study, 3.5 and the model-runner part of 5.x).  For
+// (zihan-zhang.net vLLM study, 3.5 and 5.6).  For
 // request r with chunk rows query_start_loc[r] .. query_start_loc[r+1]-1
 // (n_r of them) and context ctx_r (prior tokens plus the chunk, all already in
 // the pools), query i sits at position pos = ctx_r - n_r + i and attends

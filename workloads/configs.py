@@ -308,7 +308,7 @@ def make_decode(cfg, layout_variant=0, private_copies=False):
         wl.extra["prompt_len"] = 2048
         return wl
     if cfg_no == 5:
-        dec, _ = make_mixed(layout_variant)
+        dec, _ = make_mixed(layout_variant, parts=("decode",))
         return dec
     raise ValueError(f"unknown config {cfg}")
 
@@ -371,15 +371,17 @@ def make_prefill(cfg=5, layout_variant=0):
     against 4096 prior paged tokens, 32q/8kv, d=128, bf16."""
     if int(cfg) != 5:
         raise ValueError("only config 5 has a prefill part")
-    _, pre = make_mixed(layout_variant)
+    _, pre = make_mixed(layout_variant, parts=("prefill",))
     return pre
 
 
-def make_mixed(layout_variant=0):
+def make_mixed(layout_variant=0, parts=("decode", "prefill")):
     """Config 5: long-context decode and chunked prefill sharing one pool.
 
     The pool holds 1.25x the blocks both halves need; the decode half takes
     the first blocks of the shuffled pool, the prefill half the next ones.
+    ``parts`` may name only one half (the other comes back as None); each
+    half is drawn from its own streams, so it is the same either way.
     """
     cfg_no = 5
     vseed = 396_000 + cfg_no
@@ -398,10 +400,13 @@ def make_mixed(layout_variant=0):
         def permutation(self, n):  # noqa: ARG002 - size is fixed by the pool
             return self.ids
 
-    dec = _build_decode(CONFIG_NAMES[5], "bf16", [32768] * 8, 32, 8, 128, 2048, vseed,
-                        _Fixed(perm[:dec_need]), num_blocks=num_blocks)
-    pre = _build_prefill(CONFIG_NAMES[5] + "_prefill", "bf16", [4096] * 4, [512] * 4, 32, 8,
-                         128, 288, vseed + 50, _Fixed(perm[dec_need:]), num_blocks=num_blocks)
+    dec = pre = None
+    if "decode" in parts:
+        dec = _build_decode(CONFIG_NAMES[5], "bf16", [32768] * 8, 32, 8, 128, 2048, vseed,
+                            _Fixed(perm[:dec_need]), num_blocks=num_blocks)
+    if "prefill" in parts:
+        pre = _build_prefill(CONFIG_NAMES[5] + "_prefill", "bf16", [4096] * 4, [512] * 4, 32, 8,
+                             128, 288, vseed + 50, _Fixed(perm[dec_need:]), num_blocks=num_blocks)
     return dec, pre
 
 
