@@ -36,6 +36,8 @@
 //    same softmax).  P is rounded to bf16 for the matrix product.
 #include <float.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -43,6 +45,13 @@ namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+#ifndef PA_PF_NCB
+#define PA_PF_NCB 1
+#endif
+#ifndef PA_PF_WAVES_PER_EU
+#define PA_PF_WAVES_PER_EU 2
+#endif
 
 constexpr int kPfWaves = 4;        // waves per workgroup
 constexpr int kPfKT = 64;          // keys per iteration (four 16-token blocks)
@@ -54,12 +63,17 @@ template <int D>
 struct PrefillCfg {
   static constexpr int RB = D * 2;             // bytes of one K row (bf16)
   static constexpr int KCH = RB / 16;          // 16-byte chunks per K row
-  static constexpr int KROWS_PER_256 = 256 / RB;
   static constexpr int DS = D / 16;            // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;            // 32-dim blocks of O^T
-  static constexpr int VRB = kPfKT * 2;        // bytes of one V row (one dim) in LDS
-  static constexpr int K_LDS = kPfKT * RB;     // one K stage
-  static constexpr int V_LDS = D * VRB;        // one V stage
+  static constexpr int VRB = kPfKT * 2;        // bytes of one V row (one dim) of a tile
+  // LDS rows are padded by 16 bytes: the 32 rows one MFMA fragment reads at
+  // a fixed 16-byte chunk then fall on distinct banks (row strides of 17 or
+  // 9 chunks are odd), whether the bank array is 128 or 256 bytes wide, and
+  // every fragment address is a per-lane base plus an immediate offset.
+  static constexpr int KRS = RB + 16;          // LDS stride of one K row
+  static constexpr int VRS = VRB + 16;         // LDS stride of one V row
+  static constexpr int K_LDS = kPfKT * KRS;    // one K stage
+  static constexpr int V_LDS = D * VRS;        // one V stage
   static constexpr int STAGE = K_LDS + V_LDS;
   static constexpr int NKL = kPfKT * KCH / (kPfWaves * kWave);  // K chunks per thread
   static constexpr int NVL = 2 * D * kPfBlocks / (kPfWaves * kWave);  // V chunks per thread
@@ -84,20 +98,6 @@ struct PrefillParams {
   float scale_log2;
 };
 
-// LDS byte offset of 16-byte chunk c of K row `row` (XOR swizzle: the 32 rows
-// one MFMA fragment reads at a fixed chunk fall on distinct banks).
-template <int D>
-__device__ inline int k_lds_off(int row, int c) {
-  using C = PrefillCfg<D>;
-  return row * C::RB + ((c ^ ((row / C::KROWS_PER_256) % C::KCH)) << 4);
-}
-// LDS byte offset of 16-byte chunk c (keys 8c .. 8c+7) of V row `dim`.
-template <int D>
-__device__ inline int v_lds_off(int dim, int c) {
-  using C = PrefillCfg<D>;
-  return C::K_LDS + dim * C::VRB + ((c ^ ((dim >> 1) & 7)) << 4);
-}
-
 __device__ inline __amdgpu_buffer_rsrc_t pf_rsrc(const char* ptr, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0, bytes, 0x00020000);
 }
@@ -110,6 +110,8 @@ __device__ inline uint4 pf_load16(__amdgpu_buffer_rsrc_t r, int off) {
 // Key (within a 32-key block) that MFMA row m of S^T stands for.  Rows are
 // permuted inside each group of 16 (quads 1 and 2 swapped) so that the
 // accumulator registers 8t..8t+7 of lane l hold keys 16t + 8(l/32) + 0..7.
+// The permutation is its own inverse; the K tile is stored in LDS in this
+// row order, so fragment lane m simply reads LDS row m.
 __device__ inline int pf_row_key(int m) {
   const int quad = (m >> 2) & 3;
   const int sq = quad == 1 ? 2 : quad == 2 ? 1 : quad;
@@ -117,7 +119,8 @@ __device__ inline int pf_row_key(int m) {
 }
 
 template <int D, int G, int NCB>
-__global__ __launch_bounds__(kPfWaves * kWave) void prefill_chunk_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPfWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kernel(PrefillParams p) {
   using C = PrefillCfg<D>;
   constexpr int COLS = kPfWaves * 32 * NCB;  // columns per workgroup
   constexpr int QT = COLS / G;               // queries per workgroup
@@ -154,11 +157,17 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_chunk_kernel(Prefill
   const int nblk = (ctx + kBlock - 1) / kBlock;
 
   const int tid = threadIdx.x;
+  __builtin_assume(tid < kPfWaves * kWave);
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int half = lane >> 5;
   const int cw = lane & 31;
   const int32_t* bt = p.block_tables + (int64_t)r * p.max_blocks_per_seq;
+
+  // Scores are scaled by |scale|; a negative scale is applied by flipping the
+  // sign of q, which is exact in bf16.
+  const float sl = fabsf(p.scale_log2);
+  const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // ---- this lane's columns and their query positions
   int pos[NCB];
@@ -174,7 +183,11 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_chunk_kernel(Prefill
     const char* qrow = p.q + ((int64_t)(qs + (valid ? qi : 0)) * p.num_q_heads + g * G + hh) * C::RB;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s)
-      qf[cb][s] = valid ? *(const uint4*)(qrow + (2 * s + half) * 16) : make_uint4(0, 0, 0, 0);
+    {
+      uint4 v = valid ? *(const uint4*)(qrow + (2 * s + half) * 16) : make_uint4(0, 0, 0, 0);
+      v.x ^= qsign; v.y ^= qsign; v.z ^= qsign; v.w ^= qsign;
+      qf[cb][s] = v;
+    }
     // first and last query of this column block (columns are query-major)
     const int qa = q0 + (32 * (w * NCB + cb)) / G;
     const int qb = min(n_r - 1, q0 + (32 * (w * NCB + cb) + 31) / G);
@@ -200,64 +213,58 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_chunk_kernel(Prefill
   }
 
   // ---- global -> register -> LDS staging of one 64-key tile
+  // Each (block, kv head) tile is one contiguous run of 16 * RB bytes for K
+  // and for V, i.e. TPB 16-byte chunks (256 for D = 128).  Thread t loads
+  // chunk t % TPB of block NBP * u + t / TPB for u = 0 .. NKL-1, so every
+  // load instruction reads consecutive 16-byte pieces of one tile, and the
+  // block a wave loads is known per wave (t / TPB is uniform in a wave).
+  constexpr int TPB = kBlock * C::RB / 16;           // chunks per tile
+  constexpr int NBP = kPfWaves * kWave / TPB;        // blocks per load pass
+  static_assert(TPB % kWave == 0 && C::NKL * NBP == kPfBlocks && C::NVL == C::NKL, "staging map");
+  const int jt = tid % TPB;                          // chunk within the tile
+  const int bsub = (w * kWave) / TPB;                // uniform: which block of the pass
   uint4 kreg[C::NKL], vreg[C::NVL];
   auto block_id = [&](int jb) -> int {
     if (jb >= nblk) return -1;
     const int id = bt[jb];
     return (id >= 0 && id < p.num_blocks) ? id : -1;
   };
-  int ids[kPfBlocks];
+  int id0 = -1, id1 = -1, id2 = -1, id3 = -1;  // block ids of the next tile (uniform)
+  static_assert(kPfBlocks == 4, "four block ids per tile");
   auto fetch_ids = [&](int it) {
-#pragma unroll
-    for (int b = 0; b < kPfBlocks; ++b) ids[b] = block_id(it * kPfBlocks + b);
+    id0 = __builtin_amdgcn_readfirstlane(block_id(it * kPfBlocks + 0));
+    id1 = __builtin_amdgcn_readfirstlane(block_id(it * kPfBlocks + 1));
+    id2 = __builtin_amdgcn_readfirstlane(block_id(it * kPfBlocks + 2));
+    id3 = __builtin_amdgcn_readfirstlane(block_id(it * kPfBlocks + 3));
   };
-  auto id_of = [&](int b) {
-    int v = ids[0];
-#pragma unroll
-    for (int bb = 1; bb < kPfBlocks; ++bb) v = b == bb ? ids[bb] : v;
-    return v;
-  };
+  auto id_of = [&](int b) { return b == 0 ? id0 : b == 1 ? id1 : b == 2 ? id2 : id3; };
   const int64_t tile_bytes = (int64_t)kBlock * C::RB;
   auto global_load = [&]() {
 #pragma unroll
     for (int u = 0; u < C::NKL; ++u) {
-      const int ci = tid + kPfWaves * kWave * u;
-      const int key = ci / C::KCH;
-      const int b = __builtin_amdgcn_readfirstlane(key / kBlock);  // uniform per wave
-      const int id = id_of(b);
-      const __amdgpu_buffer_rsrc_t rs =
-          pf_rsrc(p.k_cache + ((int64_t)max(id, 0) * p.num_kv_heads + g) * tile_bytes,
-                  id >= 0 ? (int)tile_bytes : 0);
-      kreg[u] = pf_load16(rs, (key % kBlock) * C::RB + (ci % C::KCH) * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < C::NVL; ++u) {
-      const int ci = tid + kPfWaves * kWave * u;
-      const int b = __builtin_amdgcn_readfirstlane(ci / (2 * D));
-      const int id = id_of(b);
-      const __amdgpu_buffer_rsrc_t rs =
-          pf_rsrc(p.v_cache + ((int64_t)max(id, 0) * p.num_kv_heads + g) * tile_bytes,
-                  id >= 0 ? (int)tile_bytes : 0);
-      vreg[u] = pf_load16(rs, (ci % (2 * D)) * 16);
+      const int id = id_of(NBP * u + bsub);
+      const int64_t base = ((int64_t)max(id, 0) * p.num_kv_heads + g) * tile_bytes;
+      const int nrec = id >= 0 ? (int)tile_bytes : 0;
+      kreg[u] = pf_load16(pf_rsrc(p.k_cache + base, nrec), jt * 16);
+      vreg[u] = pf_load16(pf_rsrc(p.v_cache + base, nrec), jt * 16);
     }
   };
+  // LDS destinations of this thread's chunks (block b adds a constant):
+  // K chunk jt of block b is key 16 b + jt / KCH, stored in row
+  // 16 b + pf_row_key(jt / KCH); V chunk jt is dim jt / 2, keys 8 (jt % 2)..
+  const int kst = pf_row_key(jt / C::KCH) * C::KRS + (jt % C::KCH) * 16;
+  const int vst = C::K_LDS + (jt >> 1) * C::VRS + (jt & 1) * 16;
   auto lds_store = [&](int it, char* st) {
+    // keys past the context hold whatever the pool has (possibly NaN): a
+    // zero probability must meet a finite value, so clear them here
+    const bool tail = it * kPfKT + kPfKT > ctx;  // uniform
 #pragma unroll
     for (int u = 0; u < C::NKL; ++u) {
-      const int ci = tid + kPfWaves * kWave * u;
-      *(uint4*)(st + k_lds_off<D>(ci / C::KCH, ci % C::KCH)) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < C::NVL; ++u) {
-      const int ci = tid + kPfWaves * kWave * u;
-      const int b = ci / (2 * D);
-      const int wi = ci % (2 * D);
-      const int dim = wi >> 1, hv = wi & 1;
-      // keys past the context hold whatever the pool has (possibly NaN): a
-      // zero probability must meet a finite value, so clear them here
-      const int key0 = it * kPfKT + b * kBlock + hv * 8;
+      const int b = NBP * u + bsub;
+      *(uint4*)(st + kst + b * kBlock * C::KRS) = kreg[u];
       uint4 v = vreg[u];
-      if (key0 + 8 > ctx) {
+      if (tail) {
+        const int key0 = it * kPfKT + b * kBlock + (jt & 1) * 8;
         uint32_t* wv = (uint32_t*)&v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_chunk_kernel(Prefill
           wv[e] &= t >= ctx ? 0u : (t + 1 >= ctx ? 0x0000ffffu : 0xffffffffu);
         }
       }
-      *(uint4*)(st + v_lds_off<D>(dim, 2 * b + hv)) = v;
+      *(uint4*)(st + vst + b * 32) = v;
     }
   };
 
@@ -276,103 +283,122 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_chunk_kernel(Prefill
     lds_store(0, lds[0]);
   }
 
-  const int krow = pf_row_key(cw);  // key (within a 32-key block) of this lane's MFMA row
+  // fragment read bases: K row cw (key pf_row_key(cw)) dims 8 half ..;
+  // V row (dim) cw keys 8 half ..
+  const int kfr = cw * C::KRS + half * 16;
+  const int vfr = C::K_LDS + cw * C::VRS + half * 16;
 
-  for (int it = 0; it < iters; ++it) {
+  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P.  MASK
+  // selects the variant for tiles that reach past some column's position
+  // (the causal diagonal, the context end or padding columns).
+  auto tile_step = [&](const char* st, int k0, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    f32x16_t sacc[NCB][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        const uint4 a = *(const uint4*)(st + kfr + kb * 32 * C::KRS + s * 32);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const f32x16_t zero = {};
+          sacc[cb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qf[cb][s]),
+              s == 0 ? zero : sacc[cb][kb], 0, 0, 0);
+        }
+      }
+
+    // register i of key block kb is key k0 + 32 kb + 16 (i / 8) + 8 half + i % 8.
+    // The max is taken on raw scores (the scale is >= 0 here); scale and max
+    // are then applied in one fma per score.  In masked tiles a hidden key's
+    // probability is selected to zero, which also discards any NaN from a
+    // poisoned slot past the context.
+    bf16x8_t pf[NCB][2][2];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      auto visible = [&](int kb, int i) {
+        return k0 + 32 * kb + 16 * (i >> 3) + 8 * half + (i & 7) <= pos[cb];
+      };
+      float mraw = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float v = sacc[cb][kb][i];
+          mraw = fmaxf(mraw, (MASK && !visible(kb, i)) ? -INFINITY : v);
+        }
+      mraw = fmaxf(mraw, xor_lane<32>(mraw));
+      const float mx = mraw == -INFINITY ? -INFINITY : mraw * sl;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[cb] + kPfGap)) {
+        const float m_new = fmaxf(m_run[cb], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);
+        m_run[cb] = m_new;
+        l_run[cb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acco[cb][db][i] *= alpha;
+      }
+      const float nm = -m_run[cb];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          uint32_t wds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i0 = 8 * t + 2 * e;
+            float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i0], sl, nm));
+            float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i0 + 1], sl, nm));
+            if (MASK) {
+              p0 = visible(kb, i0) ? p0 : 0.f;
+              p1 = visible(kb, i0 + 1) ? p1 : 0.f;
+            }
+            lsum += p0 + p1;
+            wds[e] = pack_bf16(p0, p1);
+          }
+          pf[cb][kb][t] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
+        }
+      l_run[cb] += lsum;
+    }
+
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint4 a = *(const uint4*)(st + vfr + 32 * db * C::VRS + (4 * kb + 2 * t) * 16);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            acco[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, a), pf[cb][kb][t], acco[cb][db], 0, 0, 0);
+        }
+  };
+
+  // One pipelined iteration: wait for tile it in LDS, start the global
+  // loads of tile it+1, compute tile it, then park tile it+1 in the other
+  // LDS buffer.  Every wave of the workgroup runs every iteration.
+  auto iteration = [&](int it, auto mask_c) {
     __syncthreads();
     if (it + 1 < iters) {
       global_load();
       if (it + 2 < iters) fetch_ids(it + 2);
     }
-    const char* st = lds[it & 1];
     const int k0 = it * kPfKT;
-    if (k0 <= wave_max_pos) {
-      // ---- S^T = K Q^T for 64 keys x 32*NCB columns
-      f32x16_t sacc[NCB][2];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[cb][kb][i] = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s = 0; s < C::DS; ++s) {
-          const uint4 a = *(const uint4*)(st + k_lds_off<D>(32 * kb + krow, 2 * s + half));
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-            sacc[cb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qf[cb][s]),
-                sacc[cb][kb], 0, 0, 0);
-        }
-
-      // ---- online softmax per column; register i of key block kb is key
-      // k0 + 32 kb + 16 (i / 8) + 8 half + i % 8
-      const bool need_mask = k0 + kPfKT - 1 > wave_min_pos;
-      bf16x8_t pf[NCB][2][2];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        float z[2][16];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float v = sacc[cb][kb][i] * p.scale_log2;
-            if (need_mask) {
-              const int key = k0 + 32 * kb + 16 * (i >> 3) + 8 * half + (i & 7);
-              v = key <= pos[cb] ? v : -INFINITY;
-            }
-            z[kb][i] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, xor_lane<32>(mx));
-        const bool over = mx > m_run[cb] + kPfGap;
-        if (__builtin_amdgcn_ballot_w64(over)) {
-          const float m_new = fmaxf(m_run[cb], mx);
-          const float alpha = exp2f(m_run[cb] - m_new);
-          m_run[cb] = m_new;
-          l_run[cb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acco[cb][db][i] *= alpha;
-        }
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            uint32_t wds[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p0 = exp2f(z[kb][8 * t + 2 * e] - m_run[cb]);
-              const float p1 = exp2f(z[kb][8 * t + 2 * e + 1] - m_run[cb]);
-              lsum += p0 + p1;
-              wds[e] = pack_bf16(p0, p1);
-            }
-            pf[cb][kb][t] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
-          }
-        l_run[cb] += lsum;
-      }
-
-      // ---- O^T += V^T P
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const uint4 a = *(const uint4*)(st + v_lds_off<D>(32 * db + cw, 4 * kb + 2 * t + half));
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-              acco[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8_t, a), pf[cb][kb][t], acco[cb][db], 0, 0, 0);
-          }
-    }
+    if (k0 <= wave_max_pos)  // uniform: some column of this wave sees a key here
+      tile_step(lds[it & 1], k0, mask_c);
     if (it + 1 < iters) lds_store(it + 1, lds[(it + 1) & 1]);
-  }
+  };
+  // Tiles that end before the workgroup's first query position need no
+  // mask for any column; the rest (the causal diagonal, the context end and
+  // padding columns) take the masked variant.  Two plain loops keep the
+  // accumulators in fixed registers across iterations.
+  const int wg_min_pos = prior + q0;
+  const int n_plain = wg_min_pos >= 0 ? min(iters, (wg_min_pos + 1) / kPfKT) : 0;
+  for (int it = 0; it < n_plain; ++it) iteration(it, std::false_type{});
+  for (int it = n_plain; it < iters; ++it) iteration(it, std::true_type{});
 
   // ---- normalise and store: register i of dim block db is dim
   // 32 db + 8 (i / 4) + 4 half + i % 4 of this lane's column
@@ -399,14 +425,14 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_chunk_kernel(Prefill
 
 template <int D, int G>
 static hipError_t launch_prefill_t(const PrefillParams& prm, hipStream_t stream) {
-  constexpr int NCB = 1;
+  constexpr int NCB = PA_PF_NCB;
   const int64_t grid = (int64_t)prm.num_qtiles * prm.num_reqs * prm.num_kv_heads;
   hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB>), dim3((unsigned)grid),
                      dim3(kPfWaves * kWave), 0, stream, prm);
   return hipGetLastError();
 }
 
-int prefill_queries_per_tile(int group) { return kPfWaves * 32 / group; }
+int prefill_queries_per_tile(int group) { return kPfWaves * 32 * PA_PF_NCB / group; }
 
 bool prefill_supported(int elem_bytes, int head_dim, int group) {
   return elem_bytes == 2 && (head_dim == 64 || head_dim == 128) &&
