@@ -53,7 +53,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 #define PA_PF_WAVES_PER_EU 2
 #endif
 
-constexpr int kPfWaves = 4;        // waves per workgroup
+#ifndef PA_PF_WAVES
+#define PA_PF_WAVES 4
+#endif
+#ifndef PA_PF_SCHED
+#define PA_PF_SCHED 0
+#endif
+
+constexpr int kPfWaves = PA_PF_WAVES;  // waves per workgroup
 constexpr int kPfKT = 64;          // keys per iteration (four 16-token blocks)
 constexpr int kPfBlocks = kPfKT / kBlock;
 constexpr float kPfGap = 8.0f;     // log2 units a score may exceed the reference max
@@ -97,15 +104,6 @@ struct PrefillParams {
   int num_qtiles;
   float scale_log2;
 };
-
-__device__ inline __amdgpu_buffer_rsrc_t pf_rsrc(const char* ptr, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0, bytes, 0x00020000);
-}
-__device__ inline uint4 pf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // Key (within a 32-key block) that MFMA row m of S^T stands for.  Rows are
 // permuted inside each group of 16 (quads 1 and 2 swapped) so that the
@@ -222,31 +220,52 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   constexpr int NBP = kPfWaves * kWave / TPB;        // blocks per load pass
   static_assert(TPB % kWave == 0 && C::NKL * NBP == kPfBlocks && C::NVL == C::NKL, "staging map");
   const int jt = tid % TPB;                          // chunk within the tile
-  const int bsub = (w * kWave) / TPB;                // uniform: which block of the pass
+  const int bsub = NBP > 1 ? (w * kWave) / TPB : 0;  // uniform: which block of the pass
   uint4 kreg[C::NKL], vreg[C::NVL];
-  auto block_id = [&](int jb) -> int {
-    if (jb >= nblk) return -1;
-    const int id = bt[jb];
-    return (id >= 0 && id < p.num_blocks) ? id : -1;
+  // Byte offsets of the next tile's four (block, kv head) tiles in the pools
+  // (uniform).  A block past the context or an id outside the pool is read
+  // from block 0 instead (always in bounds) and flagged in `bad`; its K and
+  // V are replaced by zeros before they reach LDS, i.e. it is an empty block.
+  //
+  // The ids of a tile are loaded one iteration before they are needed, by
+  // one vector load (lane l reads block 4 it + l % 4); they are turned into
+  // scalar offsets just before the tile's loads are issued, when the load
+  // that fetched them has long completed, so no wait on the memory counter
+  // ever covers tile loads still in flight.
+  constexpr int64_t tile_bytes = (int64_t)kBlock * C::RB;
+  const char* kbase0 = p.k_cache + (int64_t)g * tile_bytes;
+  const char* vbase0 = p.v_cache + (int64_t)g * tile_bytes;
+  const int64_t bstride = (int64_t)p.num_kv_heads * tile_bytes;  // bytes per block
+  const unsigned jt16 = (unsigned)jt * 16u;
+  int idv = -1;  // lane l: raw id of block 4 * (tile) + l % 4 of the tile being fetched
+  auto issue_ids = [&](int it) {
+    const int jb = it * kPfBlocks + (lane & (kPfBlocks - 1));
+    idv = jb < nblk ? bt[jb] : -1;
   };
-  int id0 = -1, id1 = -1, id2 = -1, id3 = -1;  // block ids of the next tile (uniform)
+  int64_t off0 = 0, off1 = 0, off2 = 0, off3 = 0;
+  int bad_inflight = 0;
   static_assert(kPfBlocks == 4, "four block ids per tile");
-  auto fetch_ids = [&](int it) {
-    id0 = __builtin_amdgcn_readfirstlane(block_id(it * kPfBlocks + 0));
-    id1 = __builtin_amdgcn_readfirstlane(block_id(it * kPfBlocks + 1));
-    id2 = __builtin_amdgcn_readfirstlane(block_id(it * kPfBlocks + 2));
-    id3 = __builtin_amdgcn_readfirstlane(block_id(it * kPfBlocks + 3));
+  auto resolve_ids = [&]() {
+    int bad = 0;
+    auto one = [&](int b) -> int64_t {
+      const int id = __builtin_amdgcn_readlane(idv, b);
+      const bool ok = id >= 0 && id < p.num_blocks;
+      bad |= ok ? 0 : 1 << b;
+      return (int64_t)(ok ? id : 0) * bstride;
+    };
+    off0 = one(0);
+    off1 = one(1);
+    off2 = one(2);
+    off3 = one(3);
+    bad_inflight = bad;
   };
-  auto id_of = [&](int b) { return b == 0 ? id0 : b == 1 ? id1 : b == 2 ? id2 : id3; };
-  const int64_t tile_bytes = (int64_t)kBlock * C::RB;
+  auto off_of = [&](int b) { return b == 0 ? off0 : b == 1 ? off1 : b == 2 ? off2 : off3; };
   auto global_load = [&]() {
 #pragma unroll
     for (int u = 0; u < C::NKL; ++u) {
-      const int id = id_of(NBP * u + bsub);
-      const int64_t base = ((int64_t)max(id, 0) * p.num_kv_heads + g) * tile_bytes;
-      const int nrec = id >= 0 ? (int)tile_bytes : 0;
-      kreg[u] = pf_load16(pf_rsrc(p.k_cache + base, nrec), jt * 16);
-      vreg[u] = pf_load16(pf_rsrc(p.v_cache + base, nrec), jt * 16);
+      const int64_t o = off_of(NBP * u + bsub);
+      kreg[u] = *(const uint4*)(kbase0 + o + jt16);
+      vreg[u] = *(const uint4*)(vbase0 + o + jt16);
     }
   };
   // LDS destinations of this thread's chunks (block b adds a constant):
@@ -261,6 +280,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
 #pragma unroll
     for (int u = 0; u < C::NKL; ++u) {
       const int b = NBP * u + bsub;
+      if (bad_inflight & (1 << b)) {  // uniform, rare
+        kreg[u] = make_uint4(0, 0, 0, 0);
+        vreg[u] = make_uint4(0, 0, 0, 0);
+      }
       *(uint4*)(st + kst + b * kBlock * C::KRS) = kreg[u];
       uint4 v = vreg[u];
       if (tail) {
@@ -277,9 +300,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   };
 
   if (iters > 0) {
-    fetch_ids(0);
+    issue_ids(0);
+    resolve_ids();
+    if (iters > 1) issue_ids(1);
     global_load();
-    if (iters > 1) fetch_ids(1);
     lds_store(0, lds[0]);
   }
 
@@ -293,20 +317,29 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // (the causal diagonal, the context end or padding columns).
   auto tile_step = [&](const char* st, int k0, auto mask_c) {
     constexpr bool MASK = decltype(mask_c)::value;
+    // The two key blocks' accumulator chains alternate, and the K fragments
+    // of step s+1 are read while the products of step s run.
     f32x16_t sacc[NCB][2];
+    uint4 ka[2][2];
+    auto kfrag = [&](int s, int kb) { return *(const uint4*)(st + kfr + kb * 32 * C::KRS + s * 32); };
+    ka[0][0] = kfrag(0, 0);
+    ka[0][1] = kfrag(0, 1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int s = 0; s < C::DS; ++s) {
+      if (s + 1 < C::DS) {
+        ka[(s + 1) & 1][0] = kfrag(s + 1, 0);
+        ka[(s + 1) & 1][1] = kfrag(s + 1, 1);
+      }
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) {
-        const uint4 a = *(const uint4*)(st + kfr + kb * 32 * C::KRS + s * 32);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const f32x16_t zero = {};
           sacc[cb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qf[cb][s]),
+              __builtin_bit_cast(bf16x8_t, ka[s & 1][kb]), __builtin_bit_cast(bf16x8_t, qf[cb][s]),
               s == 0 ? zero : sacc[cb][kb], 0, 0, 0);
         }
-      }
+    }
 
     // register i of key block kb is key k0 + 32 kb + 16 (i / 8) + 8 half + i % 8.
     // The max is taken on raw scores (the scale is >= 0 here); scale and max
@@ -314,6 +347,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     // probability is selected to zero, which also discards any NaN from a
     // poisoned slot past the context.
     bf16x8_t pf[NCB][2][2];
+    float nm[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       auto visible = [&](int kb, int i) {
@@ -339,42 +373,72 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
 #pragma unroll
           for (int i = 0; i < 16; ++i) acco[cb][db][i] *= alpha;
       }
-      const float nm = -m_run[cb];
-      float lsum = 0.f;
+      nm[cb] = -m_run[cb];
+    }
+
+    // probabilities of key block kb -> bf16 B operands; then O^T += V^T P for
+    // that block.  Block 0's products are issued before block 1's
+    // exponentials so that the matrix cores and the VALU overlap.
+    auto probs = [&](int kb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int cb = 0; cb < NCB; ++cb) {
+        float lsum = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           uint32_t wds[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i0 = 8 * t + 2 * e;
-            float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i0], sl, nm));
-            float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i0 + 1], sl, nm));
+            float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i0], sl, nm[cb]));
+            float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i0 + 1], sl, nm[cb]));
             if (MASK) {
-              p0 = visible(kb, i0) ? p0 : 0.f;
-              p1 = visible(kb, i0 + 1) ? p1 : 0.f;
+              const int lim = pos[cb] - (k0 + 32 * kb + 16 * t + 8 * half);
+              p0 = 2 * e <= lim ? p0 : 0.f;
+              p1 = 2 * e + 1 <= lim ? p1 : 0.f;
             }
-            lsum += p0 + p1;
             wds[e] = pack_bf16(p0, p1);
+            // the sum runs over the bf16 weights the P V product applies
+            lsum = dot2_bf16(wds[e], 0x3f803f80u, lsum);
           }
           pf[cb][kb][t] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
         }
-      l_run[cb] += lsum;
-    }
-
+        l_run[cb] += lsum;
+      }
+    };
+    // the DB output chains alternate; V fragments are read one step ahead
+    auto vfrag = [&](int kb, int t, int db) {
+      return *(const uint4*)(st + vfr + 32 * db * C::VRS + (4 * kb + 2 * t) * 16);
+    };
+    auto pv = [&](int kb) {
+      uint4 va[2][C::DB];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+      for (int db = 0; db < C::DB; ++db) va[0][db] = vfrag(kb, 0, db);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int t = 0; t < 2; ++t) {
+        if (t == 0) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint4 a = *(const uint4*)(st + vfr + 32 * db * C::VRS + (4 * kb + 2 * t) * 16);
+          for (int db = 0; db < C::DB; ++db) va[1][db] = vfrag(kb, 1, db);
+        }
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
             acco[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, a), pf[cb][kb][t], acco[cb][db], 0, 0, 0);
-        }
+                __builtin_bit_cast(bf16x8_t, va[t][db]), pf[cb][kb][t], acco[cb][db], 0, 0, 0);
+      }
+    };
+    probs(0);
+    pv(0);
+    probs(1);
+    pv(1);
+#if PA_PF_SCHED == 1
+    // exponentials of block 1 between the products of block 0
+#pragma unroll
+    for (int i = 0; i < 2 * C::DB * NCB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+    }
+#endif
   };
 
   // One pipelined iteration: wait for tile it in LDS, start the global
@@ -383,8 +447,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   auto iteration = [&](int it, auto mask_c) {
     __syncthreads();
     if (it + 1 < iters) {
+      resolve_ids();                      // tile it+1 (ids loaded last iteration)
+      if (it + 2 < iters) issue_ids(it + 2);
       global_load();
-      if (it + 2 < iters) fetch_ids(it + 2);
     }
     const int k0 = it * kPfKT;
     if (k0 <= wave_max_pos)  // uniform: some column of this wave sees a key here
