@@ -142,7 +142,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                  second kernel with the same rescaling identity.
  *   workspace      device scratch of pa_decode_workspace_bytes(...) bytes
  *                  (may be NULL when that is 0).  Contents need no
- *                  initialisation and are overwritten.
+ *                  initialisation and are overwritten; two calls in flight at
+ *                  the same time must not share a workspace.
  * Query head h reads kv head h / (num_q_heads / Hkv).  Supported:
  * D in {64, 128}, num_q_heads / Hkv in {1, 2, 4, 8}.  Accumulation is fp32.
  */

@@ -33,7 +33,11 @@
 //    that hold the other tokens of the same dims are summed at the end.
 //  * the 4 waves merge their (m, l, O) in LDS with the same rescale.  With
 //    one partition the workgroup writes the output; otherwise it writes its
-//    partial state and decode_reduce merges the partitions.
+//    partial state and decode_reduce merges the partitions (a merge done by
+//    the last partition to finish, found with an arrival counter, measured
+//    slower: publishing partial states across XCDs takes an agent-scope
+//    release, which writes back the whole L2 of the XCD).
+
 #include <float.h>
 
 #include <type_traits>
@@ -162,94 +166,60 @@ __device__ inline void reduce_scatter_lpr(float (&v)[L], int c) {
 }
 
 
-// Occupancy target (waves per SIMD) the register allocator must meet.
+// Per-wave decode state and the arithmetic of one (block, kv head) tile,
+// shared by both decode kernels.  Lane geometry: a K row is spread over LPR
+// lanes (c = lane within the row, r = row group); V chunk i of the lane is
+// chunk lane + 64 i of the tile.
 template <int EB, int D, int G>
-constexpr int decode_waves_per_eu() {
-  return (EB == 2 && G <= 4) || (EB == 4 && D == 64 && G <= 2) ? 3 : (EB == 4 && D == 128 && G >= 4) ? 1 : 2;
-}
-
-template <int EB, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<EB, D, G>())))
-void decode_partition_kernel(DecodeParams p) {
+struct WaveDecoder {
   using C = DecodeCfg<EB, D, G>;
-  constexpr int NW = kDecodeWaves;
+  int lane, c, r, vpart, vdim0;
+  int hh, tk0;  // this lane's scores: head hh, tokens tk0 (+1 if NF == 2)
+  float scale_log2;
+  uint32_t* pb;  // this wave's probability exchange buffer in LDS
+  uint4 qv[G][C::U];
+  float o[G][C::NV];
+  float m_mine;  // reference max (log2 units) of this lane's head
+  float l_mine;  // sum of this lane's probabilities
 
-  __shared__ __attribute__((aligned(16))) uint32_t pbuf[NW][8 * G * C::PWORDS];
-  __shared__ float sm[NW][G];
-  __shared__ float sl[NW][G];
-  __shared__ __attribute__((aligned(16))) float so[NW][G][D];
-
-  const int bid = blockIdx.x;
-  const int g = bid % p.num_kv_heads;
-  const int s = (bid / p.num_kv_heads) % p.num_seqs;
-  const int part = bid / (p.num_kv_heads * p.num_seqs);
-
-  const int lane = threadIdx.x & (kWave - 1);
-  // wave index, provably uniform so that loop control stays scalar
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int c = lane & (C::LPR - 1);  // lane within its K row
-  const int r = lane / C::LPR;        // row group
-  const int vpart = lane & C::VPART_BITS;  // which tokens of a dim-row this lane holds
-  const int vdim0 = lane / C::VCPR;        // first of this lane's dims (stride 64 / VCPR)
-  const int b0 = part * p.partition_blocks;
-  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-
-  // The first block ids of this wave and q do not depend on the context
-  // length: issue them together with its load, so the first KV tile waits on
-  // one memory round trip instead of two.
-  int my_ids;  // id of block b0 + w + NW*(c0 + lane) for the current chunk c0
-  {
-    const int jb = b0 + w + NW * lane;
-    my_ids = jb < min(p.max_blocks_per_seq, b0 + p.partition_blocks) ? bt[jb] : 0;
+  __device__ void init(uint32_t* pbuf_wave, float sl2) {
+    lane = threadIdx.x & (kWave - 1);
+    c = lane & (C::LPR - 1);
+    r = lane / C::LPR;
+    vpart = lane & C::VPART_BITS;
+    vdim0 = lane / C::VCPR;
+    const int j0 = (c >> C::AR) * C::NF;
+    hh = j0 / C::NR;
+    tk0 = r * C::NR + (j0 % C::NR);
+    scale_log2 = sl2;
+    pb = pbuf_wave;
   }
-  uint4 qv[G][C::U];  // q chunks for the G heads of this kv head
-  {
-    const char* qbase = (const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::RB;
+
+  __device__ void reset() {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int x = 0; x < C::NV; ++x) o[h][x] = 0.f;
+    m_mine = kNegBig;
+    l_mine = 0.f;
+  }
+
+  // q chunks of the G heads of one kv head; qbase points at its first head's row
+  __device__ void load_q(const char* qbase, uint4 (&dst)[G][C::U]) const {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int u = 0; u < C::U; ++u)
-        qv[h][u] = *(const uint4*)(qbase + (int64_t)h * C::RB + (u * C::LPR + c) * 16);
+        dst[h][u] = *(const uint4*)(qbase + (int64_t)h * C::RB + (u * C::LPR + c) * 16);
   }
 
-  const int ctx = clamp_ctx(p.context_lens[s], p);
-  const int nblk = (ctx + kBlock - 1) / kBlock;
-  const int nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
-  if (part >= nparts) return;  // uniform over the workgroup
-  const int b1 = min(nblk, b0 + p.partition_blocks);
-
-  float o[G][C::NV];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int x = 0; x < C::NV; ++x) o[h][x] = 0.f;
-  float m_mine = kNegBig;  // reference max (log2 units) of this lane's head
-  float l_mine = 0.f;      // sum of this lane's probabilities
-
-  // this lane's scores: head hh, tokens t0 (+1 if NF == 2)
-  const int j0 = (c >> C::AR) * C::NF;
-  const int hh = j0 / C::NR;
-  const int tk0 = r * C::NR + (j0 % C::NR);
-
-  const int64_t tile_bytes = (int64_t)kBlock * C::RB;
-
-  // block ids of this wave's blocks, one per lane, refreshed every 64 blocks
-  auto fetch_ids = [&](int n0) {
-    const int jb = b0 + w + NW * (n0 + lane);
-    my_ids = jb < b1 ? bt[jb] : 0;
-  };
-
-  uint4 kb[2][C::NR][C::U], vb[2][C::NV];  // two tile slots
-  // Tile loads go through a per-tile buffer descriptor.  A tile that must not
-  // be read (past the end of the chunk, or a block id outside the pool) gets
-  // a descriptor with no records: its loads return zeros without touching
-  // memory but still retire in order, which keeps every wait count static.
-  auto load_tile = [&](int id, bool real, uint4 (&kk)[C::NR][C::U], uint4 (&vv)[C::NV]) {
-    const int64_t base = ((int64_t)id * p.num_kv_heads + g) * tile_bytes;
-    const int nrec = real ? (int)tile_bytes : 0;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k_cache + base, nrec);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v_cache + base, nrec);
+  // One (block, kv head) tile through buffer descriptors of nrec bytes: a
+  // tile that must not be read gets nrec = 0, its loads return zeros without
+  // touching memory but still retire in order (static wait counts).
+  __device__ void load_tile(const char* kp, const char* vp, int nrec, uint4 (&kk)[C::NR][C::U],
+                            uint4 (&vv)[C::NV]) const {
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp, nrec);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp, nrec);
 #pragma unroll
     for (int i = 0; i < C::NR; ++i)
 #pragma unroll
@@ -257,14 +227,11 @@ void decode_partition_kernel(DecodeParams p) {
         kk[i][u] = load16(kr, (r * C::NR + i) * C::RB + (u * C::LPR + c) * 16);
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) vv[i] = load16(vr, (lane + kWave * i) * 16);
-  };
-  auto id_ok = [&](int id) { return id >= 0 && id < p.num_blocks; };
-  const int nmine = b1 > b0 + w ? (b1 - b0 - w + NW - 1) / NW : 0;
+  }
 
-  auto process = [&](uint4 (&kc)[C::NR][C::U], uint4 (&vc)[C::NV], int id_cur, int n) {
-    const int jblk = b0 + w + NW * n;
-    const bool bad_cur = id_cur < 0 || id_cur >= p.num_blocks;
-
+  // Scores, online-softmax update and P.V for one tile whose first `nvalid`
+  // tokens belong to the context (0 for a tile that must be skipped).
+  __device__ void process(uint4 (&kc)[C::NR][C::U], uint4 (&vc)[C::NV], int nvalid) {
     // ---- partial dots
     float acc[C::N0];
 #pragma unroll
@@ -293,11 +260,10 @@ void decode_partition_kernel(DecodeParams p) {
     reduce_scatter_lpr<C::LPR, C::N0>(acc, c);
 
     // ---- scores (log2 units), masking tokens past the context
-    const int nvalid = bad_cur ? 0 : min(kBlock, ctx - jblk * kBlock);
     float z[C::NF];
 #pragma unroll
     for (int k = 0; k < C::NF; ++k) {
-      z[k] = acc[k] * p.scale_log2;
+      z[k] = acc[k] * scale_log2;
       if (nvalid < kBlock) z[k] = (tk0 + k < nvalid) ? z[k] : -INFINITY;
     }
     if (nvalid < kBlock) {
@@ -335,8 +301,7 @@ void decode_partition_kernel(DecodeParams p) {
       m_mine = m_new;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float ah = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(alpha), (h * C::HEAD_SPAN) << C::AR));
+        const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), head_lane(h)));
 #pragma unroll
         for (int x = 0; x < C::NV; ++x) o[h][x] *= ah;
       }
@@ -349,7 +314,6 @@ void decode_partition_kernel(DecodeParams p) {
     }
 
     // ---- probabilities -> LDS as [pair][head] (bf16 pairs or fp32 pairs)
-    uint32_t* pb = pbuf[w];
     if constexpr (EB == 2) {
       if constexpr (C::NF == 2) {
         pb[(tk0 >> 1) * G + hh] = pack_bf16(pr[0], pr[1]);
@@ -406,6 +370,97 @@ void decode_partition_kernel(DecodeParams p) {
       }
     }
     __builtin_amdgcn_wave_barrier();
+  }
+
+  // Wave totals: afterwards lanes with vpart == 0 hold the complete o[h][x]
+  // for dims vdim0 + (64 / VCPR) x, and lane head_lane(h) holds head h's
+  // reference max (m_mine) and returned sum.
+  __device__ float totals() {
+    float l_head = (c & C::DUP_BITS) == 0 ? l_mine : 0.f;
+    l_head = group_sum<C::HEAD_BITS | C::DUP_BITS | C::ROW_BITS>(l_head);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int x = 0; x < C::NV; ++x) o[h][x] = group_sum<C::VPART_BITS>(o[h][x]);
+    return l_head;
+  }
+
+  static __device__ constexpr int head_lane(int h) { return (h * C::HEAD_SPAN) << C::AR; }
+  __device__ int dim_of(int x) const { return vdim0 + (kWave / C::VCPR) * x; }
+};
+
+// Occupancy target (waves per SIMD) the register allocator must meet.
+#ifndef PA_DECODE_OCC_BF16_G4
+#define PA_DECODE_OCC_BF16_G4 3
+#endif
+template <int EB, int D, int G>
+constexpr int decode_waves_per_eu() {
+  return (EB == 2 && G <= 4) ? PA_DECODE_OCC_BF16_G4
+         : (EB == 4 && D == 64 && G <= 2) ? 3 : (EB == 4 && D == 128 && G >= 4) ? 1 : 2;
+}
+
+template <int EB, int D, int G>
+__global__ __launch_bounds__(kDecodeWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<EB, D, G>())))
+void decode_partition_kernel(DecodeParams p) {
+  using C = DecodeCfg<EB, D, G>;
+  constexpr int NW = kDecodeWaves;
+
+  __shared__ __attribute__((aligned(16))) uint32_t pbuf[NW][8 * G * C::PWORDS];
+  __shared__ float sm[NW][G];
+  __shared__ float sl[NW][G];
+  __shared__ __attribute__((aligned(16))) float so[NW][G][D];
+
+  const int bid = blockIdx.x;
+  const int g = bid % p.num_kv_heads;
+  const int s = (bid / p.num_kv_heads) % p.num_seqs;
+  const int part = bid / (p.num_kv_heads * p.num_seqs);
+
+  // wave index, provably uniform so that loop control stays scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  WaveDecoder<EB, D, G> wd;
+  wd.init(pbuf[w], p.scale_log2);
+  const int lane = wd.lane;
+  const int b0 = part * p.partition_blocks;
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+
+  // The first block ids of this wave and q do not depend on the context
+  // length: issue them together with its load, so the first KV tile waits on
+  // one memory round trip instead of two.
+  int my_ids;  // id of block b0 + w + NW*(c0 + lane) for the current chunk c0
+  {
+    const int jb = b0 + w + NW * lane;
+    my_ids = jb < min(p.max_blocks_per_seq, b0 + p.partition_blocks) ? bt[jb] : 0;
+  }
+  wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::RB, wd.qv);
+
+  const int ctx = clamp_ctx(p.context_lens[s], p);
+  const int nblk = (ctx + kBlock - 1) / kBlock;
+  const int nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  if (part >= nparts) return;  // uniform over the workgroup
+  const int b1 = min(nblk, b0 + p.partition_blocks);
+  wd.reset();
+
+  const int64_t tile_bytes = (int64_t)kBlock * C::RB;
+
+  // block ids of this wave's blocks, one per lane, refreshed every 64 blocks
+  auto fetch_ids = [&](int n0) {
+    const int jb = b0 + w + NW * (n0 + lane);
+    my_ids = jb < b1 ? bt[jb] : 0;
+  };
+
+  uint4 kb[2][C::NR][C::U], vb[2][C::NV];  // two tile slots
+  auto load_tile = [&](int id, bool real, uint4 (&kk)[C::NR][C::U], uint4 (&vv)[C::NV]) {
+    const int64_t base = ((int64_t)id * p.num_kv_heads + g) * tile_bytes;
+    wd.load_tile(p.k_cache + base, p.v_cache + base, real ? (int)tile_bytes : 0, kk, vv);
+  };
+  auto id_ok = [&](int id) { return id >= 0 && id < p.num_blocks; };
+  const int nmine = b1 > b0 + w ? (b1 - b0 - w + NW - 1) / NW : 0;
+
+  auto process = [&](uint4 (&kc)[C::NR][C::U], uint4 (&vc)[C::NV], int id_cur, int n) {
+    const int jblk = b0 + w + NW * n;
+    const int nvalid = id_ok(id_cur) ? min(kBlock, ctx - jblk * kBlock) : 0;
+    wd.process(kc, vc, nvalid);
   };
 
   // Blocks are taken in chunks of 64 (one block id per lane).  Two register
@@ -426,22 +481,16 @@ void decode_partition_kernel(DecodeParams p) {
   }
 
   // ---- wave totals
-  float l_head = (c & C::DUP_BITS) == 0 ? l_mine : 0.f;
-  l_head = group_sum<C::HEAD_BITS | C::DUP_BITS | C::ROW_BITS>(l_head);
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int x = 0; x < C::NV; ++x) o[h][x] = group_sum<C::VPART_BITS>(o[h][x]);
-
+  const float l_head = wd.totals();
   if ((lane & (C::ROW_BITS | C::HEAD_BITS | C::DUP_BITS)) == 0) {
-    sm[w][hh] = m_mine;
-    sl[w][hh] = l_head;
+    sm[w][wd.hh] = wd.m_mine;
+    sl[w][wd.hh] = l_head;
   }
-  if (vpart == 0) {
+  if (wd.vpart == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int x = 0; x < C::NV; ++x) so[w][h][vdim0 + (kWave / C::VCPR) * x] = o[h][x];
+      for (int x = 0; x < C::NV; ++x) so[w][h][wd.dim_of(x)] = wd.o[h][x];
   }
   __syncthreads();
 

@@ -90,16 +90,22 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ct
   const int32_t whole = max_ctx < 16 ? 16 : round_up16(max_ctx);
   if (req < 0) return whole;
   if (req > 0) return req;
-  // automatic: every workgroup pays a fixed start-up cost (a few dependent
-  // memory round trips) and every extra partition adds merge traffic, so
-  // split only as far as needed to give the device about 8 workgroups per
-  // compute unit, and never below 256 tokens per partition.
+  // automatic: every workgroup pays a fixed start-up cost (dependent memory
+  // round trips that take microseconds once the memory system is loaded),
+  // every extra partition adds merge traffic, and workgroups of one sequence
+  // that run together share its blocks through the caches (shared prefixes).
+  // With at least 4 (sequence, kv head) units per compute unit there is no
+  // split.  Otherwise split towards 8 workgroups per compute unit (shorter
+  // pieces even out sequences of unequal length), but never below 512
+  // tokens or 1/16 of the longest context per partition.
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  const int64_t target = 8LL * device_cu_count();
-  if (units >= target) return whole;
+  const int64_t cus = device_cu_count();
+  if (units >= 4 * cus) return whole;
+  const int64_t target = 8 * cus;
   int64_t splits = target / (units > 0 ? units : 1);
   int32_t part = round_up16((max_ctx + splits - 1) / splits);
-  if (part < 256) part = 256;
+  const int32_t floor_part = max_ctx / 16 > 512 ? round_up16(max_ctx / 16) : 512;
+  if (part < floor_part) part = floor_part;
   return part >= whole ? whole : part;
 }
 

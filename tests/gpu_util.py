@@ -103,7 +103,14 @@ def oracle_pools(wl, oracle):
     return pk, pv
 
 
-def gpu_decode(wl, pool, partition_size=0, context_lens=None, max_ctx=None):
+def decode_workspace(S, Hq, Hkv, D, max_ctx, partition_size=0):
+    """A decode workspace (zero-filled, although the library needs no initial contents)."""
+    t = torch()
+    ws_bytes = pa.pa_decode_workspace_bytes(S, Hq, Hkv, D, max_ctx, partition_size)
+    return t.zeros((ws_bytes + 3) // 4, dtype=t.float32, device="cuda") if ws_bytes else None
+
+
+def gpu_decode(wl, pool, partition_size=0, context_lens=None, max_ctx=None, workspace=None):
     t = torch()
     q = to_dev(wl.q, wl.dtype)
     out = t.empty_like(q)
@@ -112,8 +119,8 @@ def gpu_decode(wl, pool, partition_size=0, context_lens=None, max_ctx=None):
     cl = t.from_numpy(np.ascontiguousarray(cl_np, dtype=np.int32)).cuda()
     maxctx = int(cl_np.max()) if max_ctx is None else int(max_ctx)
     S, Hq, D = wl.q.shape
-    ws_bytes = pa.pa_decode_workspace_bytes(S, Hq, wl.num_kv_heads, D, maxctx, partition_size)
-    ws = t.empty((ws_bytes + 3) // 4, dtype=t.float32, device="cuda") if ws_bytes else None
+    ws = workspace if workspace is not None else decode_workspace(S, Hq, wl.num_kv_heads, D, maxctx,
+                                                                   partition_size)
     pa.pa_decode(out, q, pool.k, pool.v, bt, cl, maxctx, float(wl.scale), pool.desc,
                  partition_size=partition_size, workspace=ws)
     t.cuda.synchronize()

@@ -79,6 +79,7 @@ def test_decode_argument_errors_return_codes():
 
 def test_workspace_size_formula():
     # 2 partitions of 64 tokens for a 100-token context
+    # partial states (m, l, O) per (seq, q head, partition)
     assert pa.pa_decode_workspace_bytes(2, 8, 2, 64, 100, 64) == 2 * 8 * 2 * (64 + 2) * 4
     assert pa.pa_decode_workspace_bytes(2, 8, 2, 64, 64, 64) == 0    # one partition
     assert pa.pa_decode_workspace_bytes(2, 8, 2, 64, 100, -1) == 0   # no split

@@ -11,7 +11,8 @@ import pytest
 import oracle
 from workloads import make_decode, make_tiny_decode, make_tiny_shared
 
-from gpu_util import assert_close, gpu_decode, gpu_pool_for, log, oracle_pools, raw_bits, to_f64
+from gpu_util import (assert_close, decode_workspace, gpu_decode, gpu_pool_for, log, oracle_pools,
+                      raw_bits, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -168,3 +169,59 @@ def test_config5_long_context_decode():
     for part in (0, 512, -1):
         out = to_f64(gpu_decode(wl, pool, partition_size=part))
         assert_close(out, ref, "bf16", f"config 5 partition {part}")
+
+
+# ---- automatic partitions on irregular batches: many short sequences,
+# empty contexts mixed in, one very long sequence, fewer blocks than waves
+
+IRREGULAR = [
+    # dtype, D, Hq, Hkv, ctx
+    ("bf16", 128, 32, 8, tuple(int(x) for x in np.random.default_rng(5).integers(1, 120, 300))),
+    ("bf16", 128, 32, 8, (0, 17, 0, 1, 4096, 0, 33)),       # empty contexts mixed in
+    ("bf16", 128, 64, 8, (20000,)),                         # one sequence over every wave
+    ("bf16", 64, 8, 2, (5, 3)),                             # fewer blocks than waves
+    ("f32", 64, 4, 2, tuple(int(x) for x in np.random.default_rng(6).integers(1, 300, 70))),
+    ("f32", 128, 8, 1, (1, 2000, 15)),
+]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,ctx", IRREGULAR)
+def test_irregular_batches(dtype, D, Hq, Hkv, ctx):
+    log(f"decode irregular {dtype} D={D} Hq={Hq} Hkv={Hkv} S={len(ctx)} max ctx={max(ctx)}")
+    wl = make_tiny_decode(seed=70 + len(ctx), ctx=tuple(max(c, 1) for c in ctx), Hq=Hq, Hkv=Hkv,
+                          D=D, dtype=dtype)
+    cl = np.asarray(ctx, dtype=np.int32)
+    out = to_f64(gpu_decode(wl, gpu_pool_for(wl), partition_size=0, context_lens=cl))
+    ref = _oracle_decode(wl)
+    for s in np.nonzero(cl == 0)[0]:
+        assert (out[s] == 0).all(), "empty context must give a zero row"
+    nz = np.nonzero(cl > 0)[0]
+    assert_close(out[nz], ref[nz], dtype, f"irregular {dtype} {D} {Hq}/{Hkv}")
+
+
+def test_many_sequences():
+    log("decode 4100 sequences")
+    ctx = tuple(int(x) for x in np.random.default_rng(7).integers(1, 40, 4100))
+    wl = make_tiny_decode(seed=77, ctx=ctx, Hq=4, Hkv=1, D=64, dtype="bf16")
+    out = to_f64(gpu_decode(wl, gpu_pool_for(wl), partition_size=0))
+    seqs = list(range(0, 4100, 41))
+    ref = _oracle_decode(wl, seqs=seqs)
+    assert_close(out[seqs], ref[seqs], "bf16", "4100 sequences")
+
+
+def test_split_k_workspace_reused_across_calls():
+    """One workspace serves consecutive calls whose partition counts differ."""
+    log("decode workspace reuse")
+    wl = make_tiny_decode(seed=9, ctx=(3000, 700, 1500, 64), Hq=32, Hkv=8, D=128, dtype="bf16")
+    pool = gpu_pool_for(wl)
+    ref = _oracle_decode(wl)
+    ws = decode_workspace(4, 32, 8, 128, 3000, 256)
+    shorter = np.minimum(wl.context_lens, 600).astype(np.int32)
+    ref_short = oracle.decode(wl.q, *oracle_pools(wl, oracle), wl.block_tables, shorter, wl.scale,
+                              wl.dtype)
+    for it in range(3):
+        out = to_f64(gpu_decode(wl, pool, partition_size=256, max_ctx=3000, workspace=ws))
+        assert_close(out, ref, "bf16", f"call {it}")
+        out = to_f64(gpu_decode(wl, pool, partition_size=256, context_lens=shorter, max_ctx=3000,
+                                workspace=ws))
+        assert_close(out, ref_short, "bf16", f"shorter call {it}")
