@@ -414,7 +414,10 @@ void decode_partition_kernel(DecodeParams p) {
   const int bid = blockIdx.x;
   const int g = bid % p.num_kv_heads;
   const int s = (bid / p.num_kv_heads) % p.num_seqs;
-  const int part = bid / (p.num_kv_heads * p.num_seqs);
+  // partitions past the first exist only for the longer sequences: they are
+  // dispatched first, so the last workgroups to start are first partitions,
+  // which every (sequence, kv head) has and which even out the tail
+  const int part = p.num_partitions - 1 - bid / (p.num_kv_heads * p.num_seqs);
 
   // wave index, provably uniform so that loop control stays scalar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -539,33 +542,57 @@ template <int EB, int D>
 __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
   const int s = blockIdx.x / p.num_q_heads;
   const int hq = blockIdx.x - s * p.num_q_heads;
-  const int ctx = clamp_ctx(p.context_lens[s], p);
-  const int nblk = (ctx + kBlock - 1) / kBlock;
-  const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
-  if (nparts <= 1) return;
   const int64_t row = (int64_t)s * p.num_q_heads + hq;
   const float* wm = p.ws_m + row * p.num_partitions;
   const float* wl = p.ws_l + row * p.num_partitions;
   const float* wo = p.ws_o + row * p.num_partitions * D;
   const int lane = threadIdx.x;
 
-  // pass 1: lane-parallel max over the partitions' reference maxima
-  float M = kNegBig;
-  for (int q = lane; q < nparts; q += kWave) M = fmaxf(M, wm[q]);
-  M = group_max<63>(M);
-  // pass 2: weights from uniform (scalar) loads; the O loads do not depend on
-  // M and are issued ahead of the arithmetic
   constexpr int XL = D / kWave;  // dims per lane
   float acc[XL];
 #pragma unroll
   for (int e = 0; e < XL; ++e) acc[e] = 0.f;
   float L = 0.f;
-#pragma unroll 4
-  for (int q = 0; q < nparts; ++q) {
-    const float f = exp2f(wm[q] - M);
-    L = fmaf(wl[q], f, L);
+  // Up to 8 partitions at a time: their m, l and O are loaded together and
+  // merged after one memory round trip (the running maximum is carried from
+  // group to group with the same rescale).  The first group's loads are
+  // issued before the context length is known (slots below num_partitions
+  // always exist), so a short merge costs a single round trip.
+  constexpr int PG = 8;
+  float M = kNegBig;
+  int nparts = PG;  // refined below once the context length has arrived
+  for (int q0 = 0; q0 < nparts; q0 += PG) {
+    float mq[PG], lq[PG], oq[PG][XL];
 #pragma unroll
-    for (int e = 0; e < XL; ++e) acc[e] = fmaf(wo[(int64_t)q * D + lane + e * kWave], f, acc[e]);
+    for (int j = 0; j < PG; ++j) {
+      const int q = min(q0 + j, (q0 == 0 ? p.num_partitions : nparts) - 1);
+      mq[j] = wm[q];
+      lq[j] = wl[q];
+#pragma unroll
+      for (int e = 0; e < XL; ++e) oq[j][e] = wo[(int64_t)q * D + lane + e * kWave];
+    }
+    if (q0 == 0) {
+      const int ctx = clamp_ctx(p.context_lens[s], p);
+      const int nblk = (ctx + kBlock - 1) / kBlock;
+      nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+      if (nparts <= 1) return;  // finished by the partition kernel
+    }
+    float Mg = M;
+#pragma unroll
+    for (int j = 0; j < PG; ++j)
+      if (q0 + j < nparts) Mg = fmaxf(Mg, mq[j]);
+    const float r = exp2f(M - Mg);  // rescale of what was merged so far
+    L *= r;
+#pragma unroll
+    for (int e = 0; e < XL; ++e) acc[e] *= r;
+#pragma unroll
+    for (int j = 0; j < PG; ++j) {
+      const float f = q0 + j < nparts ? exp2f(mq[j] - Mg) : 0.f;
+      L = fmaf(lq[j], f, L);
+#pragma unroll
+      for (int e = 0; e < XL; ++e) acc[e] = fmaf(oq[j][e], f, acc[e]);
+    }
+    M = Mg;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
