@@ -175,6 +175,35 @@ def bench_prefill(steps, warmup):
     }
 
 
+def read_ceiling(steps=10):
+    """Read bandwidth of the streaming probe over 1 GiB of shuffled 4 KiB
+    tiles: the practical ceiling for paged K/V reads on this device."""
+    import torch
+
+    import paged_kv_cache_396_amd as pa
+
+    nbytes = 1 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    ntiles = nbytes // 4096
+    order = torch.from_numpy(np.random.default_rng(396).permutation(ntiles).astype(np.int32)).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        pa.pa_bw_probe(buf, order, sink)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        pa.pa_bw_probe(buf, order, sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    gbs = nbytes * steps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del buf
+    return {"pattern": "1 GiB of 4 KiB tiles read once in shuffled order (pa_bw_probe)",
+            "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,6 +353,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    ceiling = read_ceiling()
+    line["hbm_read_ceiling"] = ceiling
+    line["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
     if not args.no_prefill:
         line["prefill_chunk"] = bench_prefill(min(args.steps, 20), min(args.warmup, 3))
     if not args.no_cpu_baseline:

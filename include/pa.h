@@ -176,6 +176,22 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
                      int32_t num_reqs, int32_t total_q_tokens, int32_t max_q_len,
                      int32_t num_q_heads, float scale, const pa_cache_desc* desc, void* stream);
 
+/*
+ * pa_bw_probe — measurement helper, not part of attention: reads num_tiles
+ * 4 KiB tiles of `buf` once each, tile tile_order[i] for i = 0..num_tiles-1,
+ * with the same non-temporal 16-byte loads the decode kernel uses for K/V
+ * tiles.  Timing it gives the read bandwidth the device sustains for
+ * scattered 4 KiB tiles, the practical ceiling beside the published HBM peak
+ * (decode is bound by the bytes it moves: zihan-zhang.net vLLM study, 1.4).
+ *
+ *   buf         device buffer of `bytes` bytes (>= 4096)
+ *   tile_order  device int32 [num_tiles]; values are clamped into the buffer
+ *   sink        device uint32 [1]; written only for one improbable data value
+ * Enqueued on `stream`; nothing is returned but the status.
+ */
+int pa_bw_probe(const void* buf, size_t bytes, const int32_t* tile_order, int32_t num_tiles,
+                uint32_t* sink, void* stream);
+
 /* Static description of a status code. */
 const char* pa_status_string(int status);
 

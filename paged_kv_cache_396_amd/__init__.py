@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     PAError,
     cache_desc,
     lib,
+    pa_bw_probe,
     pa_cache_bytes,
     pa_decode,
     pa_decode_partition_size,

@@ -71,6 +71,8 @@ def lib():
         L.pa_decode.restype = ctypes.c_int
         L.pa_prefill_chunk.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, i32, f32, D, P]
         L.pa_prefill_chunk.restype = ctypes.c_int
+        L.pa_bw_probe.argtypes = [P, sz, P, i32, P, P]
+        L.pa_bw_probe.restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_last_error.restype = ctypes.c_char_p
@@ -188,3 +190,14 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, co
                                   _ptr(block_tables), block_tables.shape[1], _ptr(query_start_loc),
                                   _ptr(context_lens), R, Tq, int(max_q_len), Hq, float(scale),
                                   ctypes.byref(desc), _stream(stream)))
+
+
+def pa_bw_probe(buf, tile_order, sink, stream=None):
+    """Read the 4 KiB tiles of ``buf`` (a device tensor) in ``tile_order`` (int32)."""
+    torch = _torch()
+    for t, n in ((buf, "buf"), (tile_order, "tile_order"), (sink, "sink")):
+        _dev(t, n)
+    if tile_order.dtype != torch.int32:
+        raise ValueError("tile_order must be int32")
+    _check(lib().pa_bw_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(tile_order),
+                             tile_order.numel(), _ptr(sink), _stream(stream)))

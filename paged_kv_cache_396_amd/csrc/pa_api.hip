@@ -266,6 +266,18 @@ PA_API int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const
   return ok();
 }
 
+PA_API int pa_bw_probe(const void* buf, size_t bytes, const int32_t* tile_order, int32_t num_tiles,
+                       uint32_t* sink, void* stream) {
+  if (num_tiles < 0) return fail(PA_ERR_SHAPE, "num_tiles %d < 0", (int)num_tiles);
+  if (num_tiles == 0) return ok();
+  if (!buf || !tile_order || !sink) return fail(PA_ERR_NULL, "buf, tile_order and sink must be non-NULL");
+  if (bytes < 4096) return fail(PA_ERR_SHAPE, "buffer of %zu bytes holds no 4 KiB tile", bytes);
+  if (bytes / 4096 >= ((size_t)1 << 31)) return fail(PA_ERR_OVERFLOW, "buffer too large");
+  hipError_t e = pa::launch_bw_probe(buf, bytes, tile_order, num_tiles, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}
+
 PA_API const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";

@@ -63,4 +63,8 @@ int prefill_queries_per_tile(int group);
 
 hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t stream);
 
+// Streaming-read probe over 4 KiB tiles in the given order.
+hipError_t launch_bw_probe(const void* buf, size_t bytes, const int32_t* order, int ntiles,
+                           uint32_t* sink, hipStream_t stream);
+
 }  // namespace pa

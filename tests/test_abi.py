@@ -111,3 +111,13 @@ def test_binding_raises_with_detail():
     with pytest.raises(pa.PAError) as e:
         binding._check(-2)
     assert "PA_ERR_SHAPE" in str(e.value)
+
+
+def test_bw_probe_argument_errors():
+    L = pa.lib()
+    z = ctypes.c_void_p(0)
+    one = ctypes.c_void_p(1)
+    assert L.pa_bw_probe(z, 4096, z, 0, z, z) == 0          # nothing to read
+    assert L.pa_bw_probe(z, 4096, z, -1, z, z) == -2
+    assert L.pa_bw_probe(z, 4096, one, 4, one, z) == -1
+    assert L.pa_bw_probe(one, 100, one, 4, one, z) == -2    # no whole tile
