@@ -175,6 +175,47 @@ def bench_prefill(steps, warmup):
     }
 
 
+def bench_bulk_write(steps=5):
+    """pa_reshape_and_cache of a whole Llama-2-70B-shaped layer history in one
+    call: 256 sequences x 2048 tokens (524,288 tokens), 8 kv heads, d 128,
+    bf16, each sequence's tokens in order into its shuffled blocks (the shape
+    of a prefill's cache fill).  Random bits: the copy is value-blind."""
+    import torch
+
+    import paged_kv_cache_396_amd as pa
+
+    S, ctx, Hkv, D = 256, 2048, 8, 128
+    T = S * ctx
+    num_blocks = int(1.25 * T // 16)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(396_003)
+    k = torch.randint(-2 ** 15, 2 ** 15, (T, Hkv, D), dtype=torch.int16, device="cuda",
+                      generator=g).view(torch.bfloat16)
+    v = torch.randint(-2 ** 15, 2 ** 15, (T, Hkv, D), dtype=torch.int16, device="cuda",
+                      generator=g).view(torch.bfloat16)
+    perm = torch.randperm(num_blocks, device="cuda", generator=g)[: T // 16].to(torch.int64)
+    tok = torch.arange(T, device="cuda", dtype=torch.int64)
+    slots = perm[tok // 16] * 16 + tok % 16
+    desc = pa.cache_desc(num_blocks, Hkv, D, torch.bfloat16)
+    nbytes = pa.pa_cache_bytes(desc)
+    kc = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    vc = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    pa.pa_reshape_and_cache(k, v, slots, kc, vc, desc)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        pa.pa_reshape_and_cache(k, v, slots, kc, vc, desc)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    moved = 4 * T * Hkv * D * 2  # K and V read once and written once
+    return {"workload": "llama2_70b_layer_history_fill", "tokens": T, "bytes_moved": moved,
+            "call_ms": round(ms, 4), "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def read_ceiling(steps=10):
     """Read bandwidth of the streaming probe over 1 GiB of shuffled 4 KiB
     tiles: the practical ceiling for paged K/V reads on this device."""
@@ -354,6 +395,8 @@ def main():
         "cpu_baseline": None,
     }
     ceiling = read_ceiling()
+    if not args.no_prefill:
+        line["cache_write_bulk"] = bench_bulk_write()
     line["hbm_read_ceiling"] = ceiling
     line["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
     if not args.no_prefill:

@@ -5,75 +5,127 @@
 // negative slot marking a padding token that writes nothing.  The copy moves
 // raw bits (no conversion), so the result is bit-exact by construction.
 //
-// One thread moves one 16-byte chunk of a (token, kv head) row.  K rows land
-// as contiguous 16-byte stores; the V tile is dim-major (16 tokens of one dim
-// together), so each V element of the row goes out as its own 2- or 4-byte
-// store, 16 elements apart.
+// One workgroup takes 16 consecutive input tokens of one kv head.
+//  * When they fill one whole block in order (slots s0, s0+1, .., s0+15 with
+//    s0 a multiple of 16: the shape of a bulk fill or of a prefill chunk),
+//    the K tile is written row by row and the V tile, which is dim-major in
+//    the pool, is transposed through LDS, so every store is a full 16 bytes.
+//  * Otherwise (a decode step's scattered tokens, padding, partial blocks)
+//    every token is scattered on its own: its K row as 16-byte stores, its V
+//    elements one by one, 16 elements apart.
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
+constexpr int kCwThreads = 256;
+
 template <int EB>
-__global__ __launch_bounds__(256) void cache_write_kernel(
+__global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slots,
-    int64_t total_chunks, int chunks_per_row, int num_kv_heads, int head_dim, int64_t pool_slots,
-    uint4* __restrict__ k_cache, char* __restrict__ v_cache) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total_chunks) return;
-  const int64_t row = idx / chunks_per_row;  // token * Hkv + g
-  const int chunk = (int)(idx - row * chunks_per_row);
-  const int64_t tok = row / num_kv_heads;
-  const int g = (int)(row - tok * num_kv_heads);
-  // the row loads do not depend on the slot: issue all three together
-  const uint4 kv = k[idx];
-  const uint4 vv = v[idx];
-  const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= pool_slots) return;
-  const int64_t b = slot / kBlock;
-  const int o = (int)(slot - b * kBlock);
-  const int64_t base = tile_base(b, g, num_kv_heads, head_dim);  // elements
+    int num_tokens, int num_kv_heads, int head_dim, int64_t pool_slots, uint4* __restrict__ k_cache,
+    char* __restrict__ v_cache) {
+  // row = one token's D values of one kv head; RC 16-byte chunks per row
+  __shared__ int64_t sl[kBlock];
+  __shared__ int s_full;
+  // V rows of the group, token-major, padded by 16 bytes per row
+  extern __shared__ __attribute__((aligned(16))) char vstage[];
 
-  // K: element (b, g, o, x) at base + o * D + x
-  const int64_t kdst = (base + (int64_t)o * head_dim) * EB / 16 + chunk;
-  k_cache[kdst] = kv;
+  const int tid = threadIdx.x;
+  const int g = blockIdx.y;
+  const int64_t i0 = (int64_t)blockIdx.x * kBlock;
+  const int RB = head_dim * EB;  // bytes of one row
+  const int RC = RB / 16;        // 16-byte chunks per row
+  if (tid < kBlock) sl[tid] = i0 + tid < num_tokens ? slots[i0 + tid] : -1;
+  __syncthreads();
+  if (tid == 0) {
+    const int64_t s0 = sl[0];
+    bool full = s0 >= 0 && s0 % kBlock == 0 && s0 + kBlock <= pool_slots;
+    for (int j = 1; j < kBlock; ++j) full = full && sl[j] == s0 + j;
+    s_full = full;
+  }
+  __syncthreads();
 
-  // V: element (b, g, o, x) at base + x * 16 + o
-  constexpr int E = 16 / EB;  // elements in this chunk
-  const int x0 = chunk * E;
-  const int64_t vrow = base + (int64_t)x0 * kBlock + o;
-  if constexpr (EB == 2) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(v_cache) + vrow;
-    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const uint32_t word = w[e >> 1];
-      dst[e * kBlock] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
+  auto row_of = [&](int64_t tok) { return (tok * num_kv_heads + g) * RC; };  // in 16-byte chunks
+
+  if (s_full) {
+    const int64_t base = tile_base(sl[0] / kBlock, g, num_kv_heads, head_dim) * EB;  // bytes
+    const int stage_rb = RB + 16;
+    // K: the tile is the 16 rows one after another
+    for (int c = tid; c < kBlock * RC; c += kCwThreads) {
+      const int o = c / RC, x = c - o * RC;
+      k_cache[base / 16 + c] = k[row_of(i0 + o) + x];
+      *(uint4*)(vstage + o * stage_rb + x * 16) = v[row_of(i0 + o) + x];
     }
-  } else {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(v_cache) + vrow;
-    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    __syncthreads();
+    // V: chunk c of the tile is dim c / CPD, tokens TPC * (c % CPD) ..
+    constexpr int TPC = 16 / EB;       // tokens per 16-byte chunk
+    constexpr int CPD = kBlock / TPC;  // chunks per dim row
+    for (int c = tid; c < head_dim * CPD; c += kCwThreads) {
+      const int x = c / CPD, t0 = (c - x * CPD) * TPC;
+      uint32_t w[4];
+      if constexpr (EB == 2) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[e * kBlock] = w[e];
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = *(const uint16_t*)(vstage + (t0 + 2 * e) * stage_rb + x * 2);
+          const uint32_t hi = *(const uint16_t*)(vstage + (t0 + 2 * e + 1) * stage_rb + x * 2);
+          w[e] = lo | (hi << 16);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = *(const uint32_t*)(vstage + (t0 + e) * stage_rb + x * 4);
+      }
+      *(uint4*)(v_cache + base + (int64_t)c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return;
+  }
+
+  // scattered tokens: each token on its own
+  for (int c = tid; c < kBlock * RC; c += kCwThreads) {
+    const int j = c / RC, chunk = c - j * RC;
+    const int64_t slot = sl[j];
+    if (slot < 0 || slot >= pool_slots) continue;
+    const uint4 kv = k[row_of(i0 + j) + chunk];
+    const uint4 vv = v[row_of(i0 + j) + chunk];
+    const int64_t b = slot / kBlock;
+    const int o = (int)(slot - b * kBlock);
+    const int64_t base = tile_base(b, g, num_kv_heads, head_dim);  // elements
+    // K: element (b, g, o, x) at base + o * D + x
+    k_cache[(base + (int64_t)o * head_dim) * EB / 16 + chunk] = kv;
+    // V: element (b, g, o, x) at base + x * 16 + o
+    constexpr int E = 16 / EB;  // elements in this chunk
+    const int64_t vrow = base + (int64_t)(chunk * E) * kBlock + o;
+    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    if constexpr (EB == 2) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(v_cache) + vrow;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t word = w[e >> 1];
+        dst[e * kBlock] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
+      }
+    } else {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(v_cache) + vrow;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e * kBlock] = w[e];
+    }
   }
 }
 
 hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slots, int num_tokens,
                               void* k_cache, void* v_cache, const CacheGeom& g, hipStream_t stream) {
-  const int row_bytes = g.head_dim * g.elem_bytes;
-  const int cpr = row_bytes / 16;
-  const int64_t total = (int64_t)num_tokens * g.num_kv_heads * cpr;
-  if (total == 0) return hipSuccess;
-  const int threads = 256;
-  const int64_t blocks = (total + threads - 1) / threads;
+  if (num_tokens == 0) return hipSuccess;
+  const int64_t groups = ((int64_t)num_tokens + kBlock - 1) / kBlock;
+  if (groups >= ((int64_t)1 << 31) || g.num_kv_heads > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)groups, (unsigned)g.num_kv_heads);
+  const size_t lds = (size_t)kBlock * (g.head_dim * g.elem_bytes + 16);
   const int64_t pool_slots = (int64_t)g.num_blocks * kBlock;
   if (g.elem_bytes == 2) {
-    hipLaunchKernelGGL(cache_write_kernel<2>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       (const uint4*)k, (const uint4*)v, slots, total, cpr, g.num_kv_heads,
+    hipLaunchKernelGGL(cache_write_kernel<2>, grid, dim3(kCwThreads), lds, stream,
+                       (const uint4*)k, (const uint4*)v, slots, num_tokens, g.num_kv_heads,
                        g.head_dim, pool_slots, (uint4*)k_cache, (char*)v_cache);
   } else {
-    hipLaunchKernelGGL(cache_write_kernel<4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       (const uint4*)k, (const uint4*)v, slots, total, cpr, g.num_kv_heads,
+    hipLaunchKernelGGL(cache_write_kernel<4>, grid, dim3(kCwThreads), lds, stream,
+                       (const uint4*)k, (const uint4*)v, slots, num_tokens, g.num_kv_heads,
                        g.head_dim, pool_slots, (uint4*)k_cache, (char*)v_cache);
   }
   return hipGetLastError();

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import make_decode, make_tiny_decode
+from workloads import make_decode, make_tiny_decode, poison_bits
 
 from gpu_util import gpu_pool_for, log, oracle_pools
 
@@ -52,3 +52,51 @@ def test_cache_write_config2_full_pool():
     log("cache write config 2 (full pool)")
     wl = make_decode(2)
     _compare_pools(wl, gpu_pool_for(wl))
+
+
+def test_cache_write_block_aligned_runs_and_scattered_tokens_mixed():
+    """Groups of 16 input tokens that fill one block in order (written as whole
+    tiles) next to a misaligned run, a run with a padding token, scattered
+    tokens and a short last group: byte-exact either way."""
+    from gpu_util import GpuPool
+
+    log("cache write aligned runs + scattered tokens")
+    rng = np.random.default_rng(5)
+    for dtype, D, Hkv in (("bf16", 128, 8), ("f32", 64, 2), ("bf16", 64, 3)):
+        nb = 40
+        runs = [16 * 5 + np.arange(16),            # aligned run: whole block 5
+                16 * 2 + np.arange(16),            # aligned run: whole block 2
+                16 * 7 + 3 + np.arange(16),        # consecutive but misaligned (blocks 7, 8)
+                16 * 11 + np.arange(16),           # aligned run with a padding token
+                rng.choice(np.arange(16 * 20, 16 * 30), 16, replace=False),  # scattered
+                16 * 33 + np.arange(15)]           # short last group
+        slots = np.concatenate(runs).astype(np.int64)
+        slots[3 * 16 + 6] = -1
+        T = slots.shape[0]
+        raw = np.uint16 if dtype == "bf16" else np.uint32
+        k = rng.integers(0, 2 ** 15 if dtype == "bf16" else 2 ** 30, (T, Hkv, D)).astype(raw)
+        v = rng.integers(0, 2 ** 15 if dtype == "bf16" else 2 ** 30, (T, Hkv, D)).astype(raw)
+        pool = GpuPool(nb, Hkv, D, dtype)
+        pool.write(k, v, slots)
+        pk = oracle.new_pool(nb, Hkv, D, dtype, poison_bits(dtype))
+        pv = oracle.new_pool(nb, Hkv, D, dtype, poison_bits(dtype))
+        oracle.reshape_and_cache(pk, pv, k, v, slots)
+        assert np.array_equal(pool.k_bits(), oracle.k_pool_bytes(pk)), f"K pool {dtype} {D}"
+        assert np.array_equal(pool.v_bits(), oracle.v_pool_bytes(pv)), f"V pool {dtype} {D}"
+
+
+def test_cache_write_bulk_fill_config3_pool_sampled():
+    """The 70B layer's whole history written in one call (524,288 tokens,
+    every block a full aligned run): sampled blocks compared byte for byte."""
+    log("cache write bulk fill config 3 (sampled)")
+    wl = make_decode(3)
+    pool = gpu_pool_for(wl, with_new=False)
+    pk = oracle.new_pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype, poison_bits(wl.dtype))
+    pv = oracle.new_pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype, poison_bits(wl.dtype))
+    oracle.reshape_and_cache_fast(pk, pv, wl.hist_k, wl.hist_v, wl.hist_slots)
+    kb = pool.k_bits().reshape(wl.num_blocks, -1)
+    vb = pool.v_bits().reshape(wl.num_blocks, -1)
+    rng = np.random.default_rng(0)
+    for b in rng.choice(wl.num_blocks, 256, replace=False):
+        assert np.array_equal(kb[b], oracle.k_pool_bytes(pk[b:b + 1])), f"K block {b}"
+        assert np.array_equal(vb[b], oracle.v_pool_bytes(pv[b:b + 1])), f"V block {b}"
