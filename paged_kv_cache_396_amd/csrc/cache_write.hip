@@ -19,6 +19,7 @@
 namespace pa {
 
 constexpr int kCwThreads = 256;
+constexpr int kCwMaxChunks = 2;  // 16 tokens x (D * eb / 16) chunks <= 512 for D <= 128, eb <= 4
 
 template <int EB>
 __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
@@ -27,7 +28,6 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
     char* __restrict__ v_cache) {
   // row = one token's D values of one kv head; RC 16-byte chunks per row
   __shared__ int64_t sl[kBlock];
-  __shared__ int s_full;
   // V rows of the group, token-major, padded by 16 bytes per row
   extern __shared__ __attribute__((aligned(16))) char vstage[];
 
@@ -36,26 +36,45 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
   const int64_t i0 = (int64_t)blockIdx.x * kBlock;
   const int RB = head_dim * EB;  // bytes of one row
   const int RC = RB / 16;        // 16-byte chunks per row
-  if (tid < kBlock) sl[tid] = i0 + tid < num_tokens ? slots[i0 + tid] : -1;
-  __syncthreads();
-  if (tid == 0) {
-    const int64_t s0 = sl[0];
-    bool full = s0 >= 0 && s0 % kBlock == 0 && s0 + kBlock <= pool_slots;
-    for (int j = 1; j < kBlock; ++j) full = full && sl[j] == s0 + j;
-    s_full = full;
-  }
-  __syncthreads();
-
+  const int nch = kBlock * RC;   // chunks of the group
   auto row_of = [&](int64_t tok) { return (tok * num_kv_heads + g) * RC; };  // in 16-byte chunks
 
-  if (s_full) {
+  // The rows do not depend on the slots: load them together with the slots,
+  // so that the group waits on one memory round trip.
+  uint4 kr[kCwMaxChunks], vr[kCwMaxChunks];
+#pragma unroll
+  for (int u = 0; u < kCwMaxChunks; ++u) {
+    const int c = tid + u * kCwThreads;
+    const int j = c / RC, x = c - j * RC;
+    if (c < nch && i0 + j < num_tokens) {
+      kr[u] = k[row_of(i0 + j) + x];
+      vr[u] = v[row_of(i0 + j) + x];
+    }
+  }
+  // The group fills one whole block in order when slot j is s0 + j for all
+  // 16 tokens, s0 a multiple of 16 inside the pool.
+  bool in_order = true;
+  if (tid < kBlock) {
+    const bool real = i0 + tid < num_tokens;
+    const int64_t s0 = slots[i0];
+    const int64_t mine = real ? slots[i0 + tid] : -1;
+    sl[tid] = mine;
+    in_order = real && s0 >= 0 && s0 % kBlock == 0 && s0 + kBlock <= pool_slots && mine == s0 + tid;
+  }
+  const bool full = __syncthreads_and(in_order);
+
+  if (full) {
     const int64_t base = tile_base(sl[0] / kBlock, g, num_kv_heads, head_dim) * EB;  // bytes
     const int stage_rb = RB + 16;
     // K: the tile is the 16 rows one after another
-    for (int c = tid; c < kBlock * RC; c += kCwThreads) {
-      const int o = c / RC, x = c - o * RC;
-      k_cache[base / 16 + c] = k[row_of(i0 + o) + x];
-      *(uint4*)(vstage + o * stage_rb + x * 16) = v[row_of(i0 + o) + x];
+#pragma unroll
+    for (int u = 0; u < kCwMaxChunks; ++u) {
+      const int c = tid + u * kCwThreads;
+      if (c < nch) {
+        const int o = c / RC, x = c - o * RC;
+        k_cache[base / 16 + c] = kr[u];
+        *(uint4*)(vstage + o * stage_rb + x * 16) = vr[u];
+      }
     }
     __syncthreads();
     // V: chunk c of the tile is dim c / CPD, tokens TPC * (c % CPD) ..
@@ -81,21 +100,22 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
   }
 
   // scattered tokens: each token on its own
-  for (int c = tid; c < kBlock * RC; c += kCwThreads) {
+#pragma unroll
+  for (int u = 0; u < kCwMaxChunks; ++u) {
+    const int c = tid + u * kCwThreads;
+    if (c >= nch) continue;
     const int j = c / RC, chunk = c - j * RC;
-    const int64_t slot = sl[j];
+    const int64_t slot = sl[j];  // -1 for tokens past the end
     if (slot < 0 || slot >= pool_slots) continue;
-    const uint4 kv = k[row_of(i0 + j) + chunk];
-    const uint4 vv = v[row_of(i0 + j) + chunk];
     const int64_t b = slot / kBlock;
     const int o = (int)(slot - b * kBlock);
     const int64_t base = tile_base(b, g, num_kv_heads, head_dim);  // elements
     // K: element (b, g, o, x) at base + o * D + x
-    k_cache[(base + (int64_t)o * head_dim) * EB / 16 + chunk] = kv;
+    k_cache[(base + (int64_t)o * head_dim) * EB / 16 + chunk] = kr[u];
     // V: element (b, g, o, x) at base + x * 16 + o
     constexpr int E = 16 / EB;  // elements in this chunk
     const int64_t vrow = base + (int64_t)(chunk * E) * kBlock + o;
-    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    const uint32_t w[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
     if constexpr (EB == 2) {
       uint16_t* dst = reinterpret_cast<uint16_t*>(v_cache) + vrow;
 #pragma unroll
@@ -114,6 +134,8 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
 hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slots, int num_tokens,
                               void* k_cache, void* v_cache, const CacheGeom& g, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
+  if ((int64_t)kBlock * g.head_dim * g.elem_bytes / 16 > (int64_t)kCwMaxChunks * kCwThreads)
+    return hipErrorInvalidValue;
   const int64_t groups = ((int64_t)num_tokens + kBlock - 1) / kBlock;
   if (groups >= ((int64_t)1 << 31) || g.num_kv_heads > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)groups, (unsigned)g.num_kv_heads);

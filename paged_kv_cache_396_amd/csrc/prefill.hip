@@ -12,15 +12,17 @@
 // (same page, 3.2) and the softmax evaluated online (same page, 4.3.1).
 //
 // Mapping onto CDNA4:
-//  * one workgroup of 4 waves per (request, kv head, tile of query rows).
-//    A "column" is one (query, q head) pair; the G q heads of the kv head and
-//    QT consecutive queries give 128 * NCB columns, 32 * NCB per wave.
+//  * one workgroup of 8 waves (two per SIMD) per (request, kv head, tile of
+//    query rows).  A "column" is one (query, q head) pair; the G q heads of
+//    the kv head and QT consecutive queries give 256 columns, 32 per wave.
 //    Workgroup ids are mapped so that all tiles of one (request, kv head)
 //    run on the same XCD and share its L2 copy of the K/V tiles.
 //  * the workgroup walks the keys 64 at a time (four 16-token blocks).  The
-//    K and V tiles of the four blocks are copied from the pools into LDS
-//    (double buffered, the next tile's global loads in flight while the
-//    current one is computed).  Blocks past the context are never read.
+//    pool tiles are copied straight into LDS by buffer loads that write LDS
+//    (no registers, no LDS store instructions), into a ring of four stages,
+//    so the loads of a tile are issued three iterations before it is used.
+//    Each wave copies one block of every tile; a block past the context or
+//    with an id outside the pool reads as zeros (empty buffer range).
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16 (32 keys x 32 columns per instruction), so
 //    each lane holds one column's scores for 16 keys and the row max of the
@@ -28,8 +30,14 @@
 //    row -> key assignment is permuted so that the 8 fp32 scores a lane holds
 //    for one 16-key step are 8 consecutive keys: after conversion to bf16
 //    they are directly the B operand of the P V product.
+//  * the scores of tile t+1 are computed while the exponentials of tile t
+//    are evaluated (K runs one tile ahead of V), so every wave has matrix and
+//    vector work in flight together.
 //  * O^T = V^T P accumulates in fp32 (32 dims x 32 columns per instruction);
-//    the V tile in LDS is dim-major, so each A fragment is one 16-byte read.
+//    the V tiles are dim-major in the pool and in LDS, so each A fragment is
+//    one 16-byte read.
+//  * LDS rows are unpadded; 16-byte chunks are XOR-swizzled within a row so
+//    that the 16 rows one fragment read touches fall on distinct banks.
 //  * softmax state (running max in log2 units, running sum) is per lane;
 //    the max is raised only when a score exceeds it by more than 2^8 (the
 //    rescale is exact when it happens; any common reference max gives the
@@ -52,19 +60,22 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 #ifndef PA_PF_WAVES_PER_EU
 #define PA_PF_WAVES_PER_EU 2
 #endif
-
 #ifndef PA_PF_WAVES
-#define PA_PF_WAVES 4
+#define PA_PF_WAVES 8
 #endif
-#ifndef PA_PF_SCHED
-#define PA_PF_SCHED 0
+#ifndef PA_PF_STAGES
+#define PA_PF_STAGES 4
 #endif
 
-constexpr int kPfWaves = PA_PF_WAVES;  // waves per workgroup
-constexpr int kPfKT = 64;          // keys per iteration (four 16-token blocks)
+constexpr int kPfWaves = PA_PF_WAVES;    // waves per workgroup
+constexpr int kPfStages = PA_PF_STAGES;  // LDS ring depth (tiles)
+constexpr int kPfKT = 64;                // keys per iteration (four 16-token blocks)
 constexpr int kPfBlocks = kPfKT / kBlock;
-constexpr float kPfGap = 8.0f;     // log2 units a score may exceed the reference max
+constexpr float kPfGap = 8.0f;           // log2 units a score may exceed the reference max
 constexpr float kPfNegBig = -FLT_MAX;
+constexpr int kPfDma = 1024;             // bytes one LDS-writing load instruction moves
+static_assert(kPfStages == 2 || kPfStages == 4, "stage count: even, and a power of two");
+static_assert(kPfWaves % kPfBlocks == 0, "whole waves per block");
 
 template <int D>
 struct PrefillCfg {
@@ -72,19 +83,13 @@ struct PrefillCfg {
   static constexpr int KCH = RB / 16;          // 16-byte chunks per K row
   static constexpr int DS = D / 16;            // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;            // 32-dim blocks of O^T
-  static constexpr int VRB = kPfKT * 2;        // bytes of one V row (one dim) of a tile
-  // LDS rows are padded by 16 bytes: the 32 rows one MFMA fragment reads at
-  // a fixed 16-byte chunk then fall on distinct banks (row strides of 17 or
-  // 9 chunks are odd), whether the bank array is 128 or 256 bytes wide, and
-  // every fragment address is a per-lane base plus an immediate offset.
-  static constexpr int KRS = RB + 16;          // LDS stride of one K row
-  static constexpr int VRS = VRB + 16;         // LDS stride of one V row
-  static constexpr int K_LDS = kPfKT * KRS;    // one K stage
-  static constexpr int V_LDS = D * VRS;        // one V stage
-  static constexpr int STAGE = K_LDS + V_LDS;
-  static constexpr int NKL = kPfKT * KCH / (kPfWaves * kWave);  // K chunks per thread
-  static constexpr int NVL = 2 * D * kPfBlocks / (kPfWaves * kWave);  // V chunks per thread
-  static_assert(NKL >= 1 && NVL >= 1, "tile too small for the workgroup");
+  static constexpr int BLK = kBlock * RB;      // one pool tile (block, kv head) of K or V
+  static constexpr int TILE = kPfBlocks * BLK;  // K or V of one 64-key tile in LDS
+  static constexpr int DPB = BLK / kPfDma;     // load instructions per pool tile
+  static constexpr int WPB = kPfWaves / kPfBlocks;  // waves sharing one block
+  static constexpr int QPW = DPB / WPB;        // K (and V) instructions per wave per tile
+  static constexpr int RPI = kPfDma / RB;      // K rows one instruction fills
+  static_assert(QPW >= 1 && QPW * WPB == DPB, "load split");
 };
 
 struct PrefillParams {
@@ -105,15 +110,53 @@ struct PrefillParams {
   float scale_log2;
 };
 
-// Key (within a 32-key block) that MFMA row m of S^T stands for.  Rows are
-// permuted inside each group of 16 (quads 1 and 2 swapped) so that the
-// accumulator registers 8t..8t+7 of lane l hold keys 16t + 8(l/32) + 0..7.
-// The permutation is its own inverse; the K tile is stored in LDS in this
-// row order, so fragment lane m simply reads LDS row m.
-__device__ inline int pf_row_key(int m) {
+// Row order of a 16-key block in LDS: row m holds key pf_key16(m), i.e. the
+// rows of quads 1 and 2 are swapped.  With this order the accumulator
+// registers 8t..8t+7 of lane l of S^T = K Q^T hold keys 16t + 8(l/32) + 0..7.
+// The permutation is its own inverse.
+__device__ inline int pf_key16(int m) {
   const int quad = (m >> 2) & 3;
   const int sq = quad == 1 ? 2 : quad == 2 ? 1 : quad;
-  return (m & 16) + sq * 4 + (m & 3);
+  return (m & ~12) | (sq << 2);
+}
+
+// Chunk swizzle of K row m in LDS: chunk c sits at slot c ^ pf_ksw(m).  The
+// 16 rows a fragment read touches at one chunk then cover all 16 bank
+// groups of 16 bytes (rows of 256 bytes: slot = c ^ m; rows of 128 bytes:
+// two rows per 256 bytes, slot = c ^ (m / 2)).
+template <int RB>
+__device__ inline int pf_ksw(int m) {
+  return RB == 256 ? (m & 15) : ((m >> 1) & 7);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (export and LDS counters left alone).
+__host__ __device__ constexpr int pf_vmcnt(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
+
+typedef int pf_rsrc __attribute__((ext_vector_type(4)));
+
+__device__ inline unsigned pf_lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+}
+
+// One 1 KiB piece from a buffer range into LDS: lane l's 16 bytes at byte
+// offset voff of the range land at LDS address lds + 16 l (zeros when voff
+// is past the range).  Written as assembly so that the compiler, which
+// cannot see the copy, adds no waits of its own: the consumer waits on the
+// vector-memory counter and a barrier before reading the stage.  M0 carries
+// the LDS address and is not used by the compiler between these
+// statements (nothing in this kernel needs it).
+__device__ inline void pf_copy_to_lds(const pf_rsrc& rs, unsigned lds, int voff) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(lds), "v"(voff), "s"(rs)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
 template <int D, int G, int NCB>
@@ -122,9 +165,24 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   using C = PrefillCfg<D>;
   constexpr int COLS = kPfWaves * 32 * NCB;  // columns per workgroup
   constexpr int QT = COLS / G;               // queries per workgroup
+  constexpr int S = kPfStages;
   static_assert(COLS % G == 0, "group must divide the column tile");
 
-  __shared__ __attribute__((aligned(16))) char lds[2][C::STAGE];
+  // One array per ring stage (K tile, then V tile).  The stages are
+  // distinct objects, so the compiler can tell that a copy into one stage
+  // never feeds a read from another and adds no wait of its own between them.
+  __shared__ __attribute__((aligned(1024))) char st0[2 * C::TILE], st1[2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) char st2[kPfStages > 2 ? 2 * C::TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[kPfStages > 2 ? 2 * C::TILE : 16];
+  auto stage = [&](auto J) -> char* {
+    constexpr int j = decltype(J)::value % S;
+    if constexpr (j == 0) return st0;
+    else if constexpr (j == 1) return st1;
+    else if constexpr (j == 2) return st2;
+    else return st3;
+  };
+  auto kstage = [&](auto J) -> char* { return stage(J); };
+  auto vstage = [&](auto J) -> char* { return stage(J) + C::TILE; };
 
   // ---- which (request, kv head, query tile): tiles of one (request, kv
   // head) are consecutive in the "logical" order, and logical runs are
@@ -160,7 +218,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int half = lane >> 5;
   const int cw = lane & 31;
-  const int32_t* bt = p.block_tables + (int64_t)r * p.max_blocks_per_seq;
+  // block ids are read through the scalar cache (uniform addresses)
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)r * p.max_blocks_per_seq);
 
   // Scores are scaled by |scale|; a negative scale is applied by flipping the
   // sign of q, which is exact in bf16.
@@ -170,7 +230,6 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // ---- this lane's columns and their query positions
   int pos[NCB];
   uint4 qf[NCB][C::DS];
-  int wave_max_pos = -1, wave_min_pos = 0x7fffffff;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int c = 32 * (w * NCB + cb) + cw;
@@ -180,21 +239,12 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     pos[cb] = valid ? prior + qi : -1;
     const char* qrow = p.q + ((int64_t)(qs + (valid ? qi : 0)) * p.num_q_heads + g * G + hh) * C::RB;
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s)
-    {
+    for (int s = 0; s < C::DS; ++s) {
       uint4 v = valid ? *(const uint4*)(qrow + (2 * s + half) * 16) : make_uint4(0, 0, 0, 0);
       v.x ^= qsign; v.y ^= qsign; v.z ^= qsign; v.w ^= qsign;
       qf[cb][s] = v;
     }
-    // first and last query of this column block (columns are query-major)
-    const int qa = q0 + (32 * (w * NCB + cb)) / G;
-    const int qb = min(n_r - 1, q0 + (32 * (w * NCB + cb) + 31) / G);
-    if (qa < n_r) {
-      wave_max_pos = max(wave_max_pos, prior + qb);
-      wave_min_pos = min(wave_min_pos, prior + qa);
-    }
   }
-  if (q0 + (32 * (w * NCB + NCB - 1) + 31) / G >= n_r) wave_min_pos = -1;  // has padding columns
 
   f32x16_t acco[NCB][C::DB];
 #pragma unroll
@@ -210,144 +260,114 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     l_run[cb] = 0.f;
   }
 
-  // ---- global -> register -> LDS staging of one 64-key tile
-  // Each (block, kv head) tile is one contiguous run of 16 * RB bytes for K
-  // and for V, i.e. TPB 16-byte chunks (256 for D = 128).  Thread t loads
-  // chunk t % TPB of block NBP * u + t / TPB for u = 0 .. NKL-1, so every
-  // load instruction reads consecutive 16-byte pieces of one tile, and the
-  // block a wave loads is known per wave (t / TPB is uniform in a wave).
-  constexpr int TPB = kBlock * C::RB / 16;           // chunks per tile
-  constexpr int NBP = kPfWaves * kWave / TPB;        // blocks per load pass
-  static_assert(TPB % kWave == 0 && C::NKL * NBP == kPfBlocks && C::NVL == C::NKL, "staging map");
-  const int jt = tid % TPB;                          // chunk within the tile
-  const int bsub = NBP > 1 ? (w * kWave) / TPB : 0;  // uniform: which block of the pass
-  uint4 kreg[C::NKL], vreg[C::NVL];
-  // Byte offsets of the next tile's four (block, kv head) tiles in the pools
-  // (uniform).  A block past the context or an id outside the pool is read
-  // from block 0 instead (always in bounds) and flagged in `bad`; its K and
-  // V are replaced by zeros before they reach LDS, i.e. it is an empty block.
-  //
-  // The ids of a tile are loaded one iteration before they are needed, by
-  // one vector load (lane l reads block 4 it + l % 4); they are turned into
-  // scalar offsets just before the tile's loads are issued, when the load
-  // that fetched them has long completed, so no wait on the memory counter
-  // ever covers tile loads still in flight.
-  constexpr int64_t tile_bytes = (int64_t)kBlock * C::RB;
-  const char* kbase0 = p.k_cache + (int64_t)g * tile_bytes;
-  const char* vbase0 = p.v_cache + (int64_t)g * tile_bytes;
-  const int64_t bstride = (int64_t)p.num_kv_heads * tile_bytes;  // bytes per block
-  const unsigned jt16 = (unsigned)jt * 16u;
-  int idv = -1;  // lane l: raw id of block 4 * (tile) + l % 4 of the tile being fetched
-  auto issue_ids = [&](int it) {
-    const int jb = it * kPfBlocks + (lane & (kPfBlocks - 1));
-    idv = jb < nblk ? bt[jb] : -1;
-  };
-  int64_t off0 = 0, off1 = 0, off2 = 0, off3 = 0;
-  int bad_inflight = 0;
-  static_assert(kPfBlocks == 4, "four block ids per tile");
-  auto resolve_ids = [&]() {
-    int bad = 0;
-    auto one = [&](int b) -> int64_t {
-      const int id = __builtin_amdgcn_readlane(idv, b);
-      const bool ok = id >= 0 && id < p.num_blocks;
-      bad |= ok ? 0 : 1 << b;
-      return (int64_t)(ok ? id : 0) * bstride;
-    };
-    off0 = one(0);
-    off1 = one(1);
-    off2 = one(2);
-    off3 = one(3);
-    bad_inflight = bad;
-  };
-  auto off_of = [&](int b) { return b == 0 ? off0 : b == 1 ? off1 : b == 2 ? off2 : off3; };
-  auto global_load = [&]() {
+  // ---- pool -> LDS copies.  Wave w copies block w / WPB of every tile: the
+  // QPW 1 KiB pieces isub .. isub+QPW-1 of its K tile and of its V tile.
+  // Each lane's source offset inside the pool tile is fixed; the LDS side of
+  // a piece is 64 consecutive 16-byte slots (lane order).
+  //  * K piece i fills rows RPI i .. of the block (LDS row m holds key
+  //    pf_key16(m)); slot j of row m receives chunk j ^ pf_ksw(m).
+  //  * V piece i fills slots 64 i .. of the dim-major block (32 bytes per
+  //    dim); slot j of dim x receives chunk j ^ ((x / 8) % 2).
+  const int bsub = w / C::WPB;
+  const int isub = (w % C::WPB) * C::QPW;
+  int kvo[C::QPW], vvo[C::QPW];
 #pragma unroll
-    for (int u = 0; u < C::NKL; ++u) {
-      const int64_t o = off_of(NBP * u + bsub);
-      kreg[u] = *(const uint4*)(kbase0 + o + jt16);
-      vreg[u] = *(const uint4*)(vbase0 + o + jt16);
-    }
-  };
-  // LDS destinations of this thread's chunks (block b adds a constant):
-  // K chunk jt of block b is key 16 b + jt / KCH, stored in row
-  // 16 b + pf_row_key(jt / KCH); V chunk jt is dim jt / 2, keys 8 (jt % 2)..
-  const int kst = pf_row_key(jt / C::KCH) * C::KRS + (jt % C::KCH) * 16;
-  const int vst = C::K_LDS + (jt >> 1) * C::VRS + (jt & 1) * 16;
-  auto lds_store = [&](int it, char* st) {
-    // keys past the context hold whatever the pool has (possibly NaN): a
-    // zero probability must meet a finite value, so clear them here
-    const bool tail = it * kPfKT + kPfKT > ctx;  // uniform
-#pragma unroll
-    for (int u = 0; u < C::NKL; ++u) {
-      const int b = NBP * u + bsub;
-      if (bad_inflight & (1 << b)) {  // uniform, rare
-        kreg[u] = make_uint4(0, 0, 0, 0);
-        vreg[u] = make_uint4(0, 0, 0, 0);
-      }
-      *(uint4*)(st + kst + b * kBlock * C::KRS) = kreg[u];
-      uint4 v = vreg[u];
-      if (tail) {
-        const int key0 = it * kPfKT + b * kBlock + (jt & 1) * 8;
-        uint32_t* wv = (uint32_t*)&v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = key0 + 2 * e;
-          wv[e] &= t >= ctx ? 0u : (t + 1 >= ctx ? 0x0000ffffu : 0xffffffffu);
-        }
-      }
-      *(uint4*)(st + vst + b * 32) = v;
-    }
-  };
-
-  if (iters > 0) {
-    issue_ids(0);
-    resolve_ids();
-    if (iters > 1) issue_ids(1);
-    global_load();
-    lds_store(0, lds[0]);
+  for (int u = 0; u < C::QPW; ++u) {
+    const int i = isub + u;
+    const int m = C::RPI * i + lane / C::KCH;
+    const int kc = (lane % C::KCH) ^ pf_ksw<C::RB>(m);
+    kvo[u] = pf_key16(m) * C::RB + kc * 16;
+    const int sp = 64 * i + lane;
+    const int x = sp >> 1;
+    const int vc = (sp & 1) ^ ((x >> 3) & 1);
+    vvo[u] = x * 32 + vc * 16;
   }
-
-  // fragment read bases: K row cw (key pf_row_key(cw)) dims 8 half ..;
-  // V row (dim) cw keys 8 half ..
-  const int kfr = cw * C::KRS + half * 16;
-  const int vfr = C::K_LDS + cw * C::VRS + half * 16;
-
-  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P.  MASK
-  // selects the variant for tiles that reach past some column's position
-  // (the causal diagonal, the context end or padding columns).
-  auto tile_step = [&](const char* st, int k0, auto mask_c) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    // The two key blocks' accumulator chains alternate, and the K fragments
-    // of step s+1 are read while the products of step s run.
-    f32x16_t sacc[NCB][2];
-    uint4 ka[2][2];
-    auto kfrag = [&](int s, int kb) { return *(const uint4*)(st + kfr + kb * 32 * C::KRS + s * 32); };
-    ka[0][0] = kfrag(0, 0);
-    ka[0][1] = kfrag(0, 1);
+  const int64_t bstride = (int64_t)p.num_kv_heads * C::BLK;  // bytes per pool block
+  // id of this wave's block of tile n; -1 past the keys this workgroup needs
+  auto block_id = [&](int n) __attribute__((always_inline)) {
+    const int jb = n * kPfBlocks + bsub;
+    return n < iters && jb < nblk ? bt[jb] : -1;
+  };
+  // Buffer ranges of this wave's pool tiles of tile n.  An empty range (a
+  // block past the context, or an id outside the pool) reads as zeros; K
+  // rows past the context read as zeros too.
+  auto range = [&](const char* pool, int id, int bytes) __attribute__((always_inline)) {
+    const bool ok = id >= 0 && id < p.num_blocks;
+    const uint64_t base = (uint64_t)(pool + (ok ? (int64_t)id * bstride : 0) + (int64_t)g * C::BLK);
+    pf_rsrc rs;
+    rs.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    rs.y = __builtin_amdgcn_readfirstlane((int)((base >> 32) & 0xffffu));  // stride 0
+    rs.z = __builtin_amdgcn_readfirstlane(ok ? bytes : 0);
+    rs.w = 0x00020000;
+    return rs;
+  };
+  // LDS offset of piece u inside a K or V tile
+  auto piece_off = [&](int u) { return bsub * C::BLK + (isub + u) * kPfDma; };
+  auto copy_k = [&](char* stage, int id, int n) __attribute__((always_inline)) {
+    const int rows = min(kBlock, ctx - (n * kPfBlocks + bsub) * kBlock);
+    const pf_rsrc rk = range(p.k_cache, id, rows * C::RB);
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) {
-      if (s + 1 < C::DS) {
-        ka[(s + 1) & 1][0] = kfrag(s + 1, 0);
-        ka[(s + 1) & 1][1] = kfrag(s + 1, 1);
+    for (int u = 0; u < C::QPW; ++u) pf_copy_to_lds(rk, pf_lds_addr(stage + piece_off(u)), kvo[u]);
+  };
+  auto copy_v = [&](char* stage, int id) __attribute__((always_inline)) {
+    const pf_rsrc rv = range(p.v_cache, id, C::BLK);
+#pragma unroll
+    for (int u = 0; u < C::QPW; ++u) pf_copy_to_lds(rv, pf_lds_addr(stage + piece_off(u)), vvo[u]);
+  };
+  constexpr int kLoadsPerBatch = 2 * C::QPW;  // vector-memory instructions per batch
+  // wait until this wave has at most n batches in flight, then meet the
+  // workgroup: every wave's copies of the older batches are then in LDS
+  auto stage_barrier = [&](auto n_c) __attribute__((always_inline)) {
+    constexpr int n = decltype(n_c)::value;
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(pf_vmcnt(n * kLoadsPerBatch));
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  };
+
+  // fragment read bases.  K: MFMA row cw of key block kb is row cw % 16 of
+  // LDS block 2 kb + cw / 16; its chunk 2 s + half sits at slot
+  // (2 s + half) ^ sw, so the address of step s is kfb ^ (32 s).  V: dim
+  // 32 db + cw of 16-key step st, keys 8 half ..
+  const int ksw = pf_ksw<C::RB>(cw & 15);
+  const int kfb = (cw >> 4) * C::BLK + (cw & 15) * C::RB + 16 * (half ^ (ksw & 1)) + 32 * (ksw >> 1);
+  const int vfb = cw * 32 + 16 * (half ^ ((cw >> 3) & 1));
+
+  // S^T = K Q^T for one 64-key tile.  The two key blocks' accumulator chains
+  // alternate; each K fragment is read two products ahead of its use.
+#ifndef PA_PF_AHEAD
+#define PA_PF_AHEAD 2
+#endif
+  constexpr int kPfAhead = PA_PF_AHEAD;
+  auto scores = [&](const char* st, int kf, f32x16_t (&sacc)[NCB][2]) __attribute__((always_inline)) {
+    constexpr int NJ = C::DS * 2;  // product j: step j / 2 of key block j % 2
+    auto kfrag = [&](int j) {
+      return *(const uint4*)(st + (j & 1) * 2 * C::BLK + (kf ^ ((j >> 1) * 32)));
+    };
+    uint4 ka[kPfAhead + 1];
+#pragma unroll
+    for (int j = 0; j < kPfAhead; ++j) ka[j] = kfrag(j);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j + kPfAhead < NJ) ka[(j + kPfAhead) % (kPfAhead + 1)] = kfrag(j + kPfAhead);
+      const int s = j >> 1, kb = j & 1;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const f32x16_t zero = {};
+        sacc[cb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, ka[j % (kPfAhead + 1)]), __builtin_bit_cast(bf16x8_t, qf[cb][s]),
+            s == 0 ? zero : sacc[cb][kb], 0, 0, 0);
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const f32x16_t zero = {};
-          sacc[cb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, ka[s & 1][kb]), __builtin_bit_cast(bf16x8_t, qf[cb][s]),
-              s == 0 ? zero : sacc[cb][kb], 0, 0, 0);
-        }
     }
+  };
 
-    // register i of key block kb is key k0 + 32 kb + 16 (i / 8) + 8 half + i % 8.
-    // The max is taken on raw scores (the scale is >= 0 here); scale and max
-    // are then applied in one fma per score.  In masked tiles a hidden key's
-    // probability is selected to zero, which also discards any NaN from a
-    // poisoned slot past the context.
-    bf16x8_t pf[NCB][2][2];
-    float nm[NCB];
+  // Running max of one tile's scores, with the lazy rescale.  Register i of
+  // key block kb is key k0 + 32 kb + 16 (i / 8) + 8 half + i % 8.  The max is
+  // taken on raw scores (the scale is >= 0 here); scale and max are then
+  // applied in one fma per score.
+  float nm[NCB];
+  auto tile_max = [&](const f32x16_t (&sacc)[NCB][2], int k0, auto mask_c) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       auto visible = [&](int kb, int i) {
@@ -361,7 +381,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
           const float v = sacc[cb][kb][i];
           mraw = fmaxf(mraw, (MASK && !visible(kb, i)) ? -INFINITY : v);
         }
-      mraw = fmaxf(mraw, xor_lane<32>(mraw));
+      // the two lane halves hold the two 8-key halves of every 16 keys
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw), __float_as_uint(mraw),
+                                                        false, false);
+      mraw = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       const float mx = mraw == -INFINITY ? -INFINITY : mraw * sl;
       if (__builtin_amdgcn_ballot_w64(mx > m_run[cb] + kPfGap)) {
         const float m_new = fmaxf(m_run[cb], mx);
@@ -375,11 +398,16 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       }
       nm[cb] = -m_run[cb];
     }
+  };
 
-    // probabilities of key block kb -> bf16 B operands; then O^T += V^T P for
-    // that block.  Block 0's products are issued before block 1's
-    // exponentials so that the matrix cores and the VALU overlap.
-    auto probs = [&](int kb) {
+  // probabilities -> bf16 B operands.  In masked tiles a hidden key's
+  // probability is selected to zero, which also discards any NaN from a
+  // poisoned slot past the context.
+  bf16x8_t pf[NCB][2][2];
+  auto probs = [&](const f32x16_t (&sacc)[NCB][2], int k0, auto mask_c) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         float lsum = 0.f;
@@ -404,66 +432,107 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
         }
         l_run[cb] += lsum;
       }
+  };
+  // O^T += V^T P: the DB output chains alternate; each V fragment is read
+  // two products ahead of its use.  In the tile holding the context end the
+  // V values of keys past it (whatever the pool holds there, possibly NaN)
+  // are cleared in the fragment: a zero probability must meet a finite value.
+  auto pv = [&](const char* st, int vf, int k0, auto mask_c) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr int NJ = 4 * C::DB;  // product j: 16-key step j / DB, dim block j % DB
+    auto vfrag = [&](int j) {
+      const int step = j / C::DB, db = j % C::DB;
+      return *(const uint4*)(st + step * C::BLK + db * 32 * 32 + vf);
     };
-    // the DB output chains alternate; V fragments are read one step ahead
-    auto vfrag = [&](int kb, int t, int db) {
-      return *(const uint4*)(st + vfr + 32 * db * C::VRS + (4 * kb + 2 * t) * 16);
-    };
-    auto pv = [&](int kb) {
-      uint4 va[2][C::DB];
+    const bool tail = MASK && k0 + kPfKT > ctx;  // uniform
+    uint4 va[kPfAhead + 1];
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) va[0][db] = vfrag(kb, 0, db);
+    for (int j = 0; j < kPfAhead; ++j) va[j] = vfrag(j);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (t == 0) {
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) va[1][db] = vfrag(kb, 1, db);
+    for (int j = 0; j < NJ; ++j) {
+      if (j + kPfAhead < NJ) va[(j + kPfAhead) % (kPfAhead + 1)] = vfrag(j + kPfAhead);
+      const int step = j / C::DB, db = j % C::DB;
+      uint4 f = va[j % (kPfAhead + 1)];
+      if constexpr (MASK) {
+        if (tail) {
+          const int lim = ctx - (k0 + 16 * step + 8 * half);  // keys e < lim are real
+          auto keep = [&](int e) { return lim > e + 1 ? 0xffffffffu : (lim > e ? 0x0000ffffu : 0u); };
+          f.x &= keep(0);
+          f.y &= keep(2);
+          f.z &= keep(4);
+          f.w &= keep(6);
         }
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-            acco[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, va[t][db]), pf[cb][kb][t], acco[cb][db], 0, 0, 0);
       }
-    };
-    probs(0);
-    pv(0);
-    probs(1);
-    pv(1);
-#if PA_PF_SCHED == 1
-    // exponentials of block 1 between the products of block 0
 #pragma unroll
-    for (int i = 0; i < 2 * C::DB * NCB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      for (int cb = 0; cb < NCB; ++cb)
+        acco[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, f), pf[cb][step >> 1][step & 1], acco[cb][db], 0, 0, 0);
     }
-#endif
   };
 
-  // One pipelined iteration: wait for tile it in LDS, start the global
-  // loads of tile it+1, compute tile it, then park tile it+1 in the other
-  // LDS buffer.  Every wave of the workgroup runs every iteration.
-  auto iteration = [&](int it, auto mask_c) {
-    __syncthreads();
-    if (it + 1 < iters) {
-      resolve_ids();                      // tile it+1 (ids loaded last iteration)
-      if (it + 2 < iters) issue_ids(it + 2);
-      global_load();
+  // ---- the ring.  Batch n is K and V of tile n, copied into stage n % S.
+  // It is issued at iteration n - S + 1, after the barrier that ends every
+  // read of that stage (tile n - S, read at iteration n - S).
+  f32x16_t sacc[NCB][2];
+  int id_next = -1;  // id of this wave's block of the next tile to copy
+  auto copy_tile = [&](auto J, int n) __attribute__((always_inline)) {
+    copy_k(kstage(J), id_next, n);
+    copy_v(vstage(J), id_next);
+    id_next = block_id(n + 1);
+  };
+  if (iters > 0) {
+    id_next = block_id(0);
+    // batches 0 .. S-2
+    copy_tile(std::integral_constant<int, 0>{}, 0);
+    if constexpr (S > 2) {
+      copy_tile(std::integral_constant<int, 1>{}, 1);
+      copy_tile(std::integral_constant<int, 2>{}, 2);
     }
-    const int k0 = it * kPfKT;
-    if (k0 <= wave_max_pos)  // uniform: some column of this wave sees a key here
-      tile_step(lds[it & 1], k0, mask_c);
-    if (it + 1 < iters) lds_store(it + 1, lds[(it + 1) & 1]);
+  }
+
+  // One iteration: wait for tile t in LDS, start the copies of tile t+S-1,
+  // then S^T = K Q^T, online softmax, O^T += V^T P on tile t.  Every wave
+  // runs every iteration.
+  auto iteration = [&](auto J, int t, auto mask_c, auto last_c) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    stage_barrier(std::integral_constant<int, S - 2>{});  // batch t has landed
+    if constexpr (!LAST) copy_tile(std::integral_constant<int, j + S - 1>{}, t + S - 1);
+    // fresh copies of the fragment bases each iteration: the compiler would
+    // otherwise keep every stage's derived addresses live across the loop
+    int kf = kfb, vf = vfb;
+    __asm__ volatile("" : "+v"(kf), "+v"(vf));
+    const int k0 = t * kPfKT;
+    scores(kstage(J), kf, sacc);
+    tile_max(sacc, k0, mask_c);
+    probs(sacc, k0, mask_c);
+    pv(vstage(J), vf, k0, mask_c);
+  };
+  auto dispatch = [&](int t, auto mask_c, auto last_c) __attribute__((always_inline)) {
+    switch (t & (S - 1)) {
+      case 0: iteration(std::integral_constant<int, 0>{}, t, mask_c, last_c); break;
+      case 1: iteration(std::integral_constant<int, 1>{}, t, mask_c, last_c); break;
+      case 2: if constexpr (S > 2) iteration(std::integral_constant<int, 2>{}, t, mask_c, last_c); break;
+      default: if constexpr (S > 3) iteration(std::integral_constant<int, 3>{}, t, mask_c, last_c); break;
+    }
   };
   // Tiles that end before the workgroup's first query position need no
   // mask for any column; the rest (the causal diagonal, the context end and
-  // padding columns) take the masked variant.  Two plain loops keep the
-  // accumulators in fixed registers across iterations.
+  // padding columns) take the masked variant.  The last tile issues no copy.
   const int wg_min_pos = prior + q0;
   const int n_plain = wg_min_pos >= 0 ? min(iters, (wg_min_pos + 1) / kPfKT) : 0;
-  for (int it = 0; it < n_plain; ++it) iteration(it, std::false_type{});
-  for (int it = n_plain; it < iters; ++it) iteration(it, std::true_type{});
+  if (iters > 0) {
+    const int split = min(n_plain, iters - 1);
+    for (int t = 0; t < split; ++t) dispatch(t, std::false_type{}, std::false_type{});
+    for (int t = split; t < iters - 1; ++t) dispatch(t, std::true_type{}, std::false_type{});
+    if (n_plain >= iters)
+      dispatch(iters - 1, std::false_type{}, std::true_type{});
+    else
+      dispatch(iters - 1, std::true_type{}, std::true_type{});
+  }
+  // copies of tiles past the end may still be in flight: let them land
+  // before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(pf_vmcnt(0));
 
   // ---- normalise and store: register i of dim block db is dim
   // 32 db + 8 (i / 4) + 4 half + i % 4 of this lane's column
