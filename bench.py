@@ -152,14 +152,15 @@ def bench_prefill(steps, warmup):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a, b in evs:
-        a.record(stream)
+    # back-to-back launches between two events: the average is the kernel's
+    # own duration plus the small gap between consecutive launches
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
         call()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = a.elapsed_time(b) / steps
     fl = prefill_flops(wl)
     tf = fl / (ms * 1e-3) / 1e12
     return {
@@ -172,6 +173,92 @@ def bench_prefill(steps, warmup):
         "roofline": {"bound": "mfma", "kernel": "prefill_chunk_kernel", "achieved": round(tf, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+
+
+def bench_mixed_concurrent(steps=10, warmup=3):
+    """The long-context mixed batch as one step: its decode half (8 x 32768)
+    and its prefill half (4 x 512-token chunks over 4096 prior tokens) read
+    one shared pool.  Timed back to back on one stream, and concurrently on
+    two streams (default priority) so the prefill's matrix work can overlap
+    the decode's HBM reads."""
+    import torch
+
+    import paged_kv_cache_396_amd as pa
+    from workloads import make_mixed
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import GpuPool, to_dev  # noqa: E402
+
+    dec, pre = make_mixed(0)
+    pool = GpuPool(dec.num_blocks, dec.num_kv_heads, dec.head_dim, dec.dtype)
+    for wl in (dec, pre):
+        pool.write(wl.hist_k, wl.hist_v, wl.hist_slots)
+        pool.write(wl.new_k, wl.new_v, wl.new_slots)
+    dq = to_dev(dec.q, dec.dtype)
+    dout = torch.empty_like(dq)
+    dbt = torch.from_numpy(dec.block_tables).cuda()
+    dcl = torch.from_numpy(dec.context_lens).cuda()
+    S, Hq, D = dec.q.shape
+    max_ctx = int(dec.context_lens.max())
+    ws_bytes = pa.pa_decode_workspace_bytes(S, Hq, dec.num_kv_heads, D, max_ctx, 0)
+    ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device="cuda")
+    pq = to_dev(pre.q, pre.dtype)
+    pout = torch.empty_like(pq)
+    pbt = torch.from_numpy(pre.block_tables).cuda()
+    pqsl = torch.from_numpy(pre.query_start_loc).cuda()
+    pcl = torch.from_numpy(pre.context_lens).cuda()
+
+    def decode(stream=None):
+        pa.pa_decode(dout, dq, pool.k, pool.v, dbt, dcl, max_ctx, float(dec.scale), pool.desc,
+                     workspace=ws, stream=stream)
+
+    def prefill(stream=None):
+        pa.pa_prefill_chunk(pout, pq, pool.k, pool.v, pbt, pqsl, pcl, pre.max_q_len,
+                            float(pre.scale), pool.desc, stream=stream)
+
+    main = torch.cuda.current_stream()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def seq_step():
+        decode(main)
+        prefill(main)
+
+    def conc_step():
+        ev = torch.cuda.Event()
+        ev.record(main)
+        s1.wait_event(ev)
+        s2.wait_event(ev)
+        decode(s1)
+        prefill(s2)
+        e1, e2 = torch.cuda.Event(), torch.cuda.Event()
+        e1.record(s1)
+        e2.record(s2)
+        main.wait_event(e1)
+        main.wait_event(e2)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(main)
+        for _ in range(steps):
+            fn()
+        b.record(main)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms_dec = timed(lambda: decode(main))
+    ms_pre = timed(lambda: prefill(main))
+    ms_seq = timed(seq_step)
+    ms_conc = timed(conc_step)
+    return {
+        "workload": "long_mixed (8 x 32768 decode + 4 x 512-token prefill chunks, one pool)",
+        "decode_ms": round(ms_dec, 5), "prefill_ms": round(ms_pre, 5),
+        "sequential_ms": round(ms_seq, 5), "concurrent_ms": round(ms_conc, 5),
+        "overlap_gain": round(ms_seq / ms_conc, 3),
+        "decode_kv_gbs_in_concurrent_step": round(dec.kv_bytes / (ms_conc * 1e-3) / 1e9, 1),
     }
 
 
@@ -353,6 +440,28 @@ def main():
     dec_ms = [a.elapsed_time(b) for a, b in evs]
     dec_avg_ms = float(np.mean(dec_ms))
 
+    # the same call with the caches cold: an untimed 512 MiB write (larger
+    # than the L2s and the 256 MB last-level cache together) before each one
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(args.steps):
+        pa.pa_reshape_and_cache(new_k, new_v, new_slots, pool.k, pool.v, pool.desc)
+        scrub.fill_(7)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        decode()
+        b.record(stream)
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    cold_ms = [a.elapsed_time(b) for a, b in cold]
+    del scrub
+
+    def dist(ms):
+        p10, p50, p90 = np.percentile(ms, [10, 50, 90])
+        return {"median_ms": round(float(p50), 5), "p10_ms": round(float(p10), 5),
+                "p90_ms": round(float(p90), 5),
+                "median_gbs": round(wl.kv_bytes / (p50 * 1e-3) / 1e9, 1)}
+
     kv = wl.kv_bytes
     value = kv / (ms_step * 1e-3) / 1e9
     achieved = kv / (dec_avg_ms * 1e-3) / 1e9
@@ -382,6 +491,8 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": kv,
         "decode_call_ms": round(dec_avg_ms, 5),
+        "decode_call_hot": dist(dec_ms),
+        "decode_call_cold": dist(cold_ms),
         "wall_s": round(wall, 4),
         "roofline": {
             "bound": "hbm",
@@ -401,6 +512,7 @@ def main():
     line["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
     if not args.no_prefill:
         line["prefill_chunk"] = bench_prefill(min(args.steps, 20), min(args.warmup, 3))
+        line["long_mixed_step"] = bench_mixed_concurrent()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -22,7 +22,9 @@
 //    (no registers, no LDS store instructions), into a ring of four stages,
 //    so the loads of a tile are issued three iterations before it is used.
 //    Each wave copies one block of every tile; a block past the context or
-//    with an id outside the pool reads as zeros (empty buffer range).
+//    with an id outside the pool is an empty buffer range.  V values of keys
+//    past the context are cleared in registers in the tile that holds the
+//    context end.
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16 (32 keys x 32 columns per instruction), so
 //    each lane holds one column's scores for 16 keys and the row max of the
@@ -30,9 +32,9 @@
 //    row -> key assignment is permuted so that the 8 fp32 scores a lane holds
 //    for one 16-key step are 8 consecutive keys: after conversion to bf16
 //    they are directly the B operand of the P V product.
-//  * the scores of tile t+1 are computed while the exponentials of tile t
-//    are evaluated (K runs one tile ahead of V), so every wave has matrix and
-//    vector work in flight together.
+//  * each 64-key tile is taken as two 32-key blocks, each a full online
+//    softmax step, so that one block's vector work can overlap the other
+//    block's matrix products.
 //  * O^T = V^T P accumulates in fp32 (32 dims x 32 columns per instruction);
 //    the V tiles are dim-major in the pool and in LDS, so each A fragment is
 //    one 16-byte read.
@@ -136,6 +138,7 @@ __host__ __device__ constexpr int pf_vmcnt(int n) {
 }
 
 typedef int pf_rsrc __attribute__((ext_vector_type(4)));
+typedef unsigned pf_u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline unsigned pf_lds_addr(const char* p) {
   return __builtin_amdgcn_readfirstlane(
@@ -168,9 +171,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   constexpr int S = kPfStages;
   static_assert(COLS % G == 0, "group must divide the column tile");
 
-  // One array per ring stage (K tile, then V tile).  The stages are
-  // distinct objects, so the compiler can tell that a copy into one stage
-  // never feeds a read from another and adds no wait of its own between them.
+  // One array per ring stage: the K tile, then the V tile.
   __shared__ __attribute__((aligned(1024))) char st0[2 * C::TILE], st1[2 * C::TILE];
   __shared__ __attribute__((aligned(1024))) char st2[kPfStages > 2 ? 2 * C::TILE : 16];
   __shared__ __attribute__((aligned(1024))) char st3[kPfStages > 2 ? 2 * C::TILE : 16];
@@ -333,115 +334,134 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   const int kfb = (cw >> 4) * C::BLK + (cw & 15) * C::RB + 16 * (half ^ (ksw & 1)) + 32 * (ksw >> 1);
   const int vfb = cw * 32 + 16 * (half ^ ((cw >> 3) & 1));
 
-  // S^T = K Q^T for one 64-key tile.  The two key blocks' accumulator chains
-  // alternate; each K fragment is read two products ahead of its use.
+  // The tile is processed as two 32-key blocks, each a full online-softmax
+  // step, so that the vector work of one block overlaps the matrix products
+  // of the other: the scores of block 1 run while block 0's exponentials are
+  // evaluated, and block 0's P V products run while block 1's are.
+
+  // S^T = K Q^T for key block kb (a chain of DS products); each K fragment
+  // is read two products ahead of its use.
 #ifndef PA_PF_AHEAD
 #define PA_PF_AHEAD 2
 #endif
   constexpr int kPfAhead = PA_PF_AHEAD;
-  auto scores = [&](const char* st, int kf, f32x16_t (&sacc)[NCB][2]) __attribute__((always_inline)) {
-    constexpr int NJ = C::DS * 2;  // product j: step j / 2 of key block j % 2
-    auto kfrag = [&](int j) {
-      return *(const uint4*)(st + (j & 1) * 2 * C::BLK + (kf ^ ((j >> 1) * 32)));
-    };
+  auto scores = [&](const char* st, int kf, int kb, f32x16_t (&sacc)[NCB]) __attribute__((always_inline)) {
+    auto kfrag = [&](int s) { return *(const uint4*)(st + kb * 2 * C::BLK + (kf ^ (s * 32))); };
     uint4 ka[kPfAhead + 1];
 #pragma unroll
-    for (int j = 0; j < kPfAhead; ++j) ka[j] = kfrag(j);
+    for (int s = 0; s < kPfAhead; ++s) ka[s] = kfrag(s);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (j + kPfAhead < NJ) ka[(j + kPfAhead) % (kPfAhead + 1)] = kfrag(j + kPfAhead);
-      const int s = j >> 1, kb = j & 1;
+    for (int s = 0; s < C::DS; ++s) {
+      if (s + kPfAhead < C::DS) ka[(s + kPfAhead) % (kPfAhead + 1)] = kfrag(s + kPfAhead);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const f32x16_t zero = {};
-        sacc[cb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, ka[j % (kPfAhead + 1)]), __builtin_bit_cast(bf16x8_t, qf[cb][s]),
-            s == 0 ? zero : sacc[cb][kb], 0, 0, 0);
+        sacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, ka[s % (kPfAhead + 1)]), __builtin_bit_cast(bf16x8_t, qf[cb][s]),
+            s == 0 ? zero : sacc[cb], 0, 0, 0);
       }
     }
   };
 
-  // Running max of one tile's scores, with the lazy rescale.  Register i of
-  // key block kb is key k0 + 32 kb + 16 (i / 8) + 8 half + i % 8.  The max is
-  // taken on raw scores (the scale is >= 0 here); scale and max are then
-  // applied in one fma per score.
-  float nm[NCB];
-  auto tile_max = [&](const f32x16_t (&sacc)[NCB][2], int k0, auto mask_c) __attribute__((always_inline)) {
+  // One online-softmax step over key block kb (keys k0 + 32 kb ..).
+  // Register i is key k0 + 32 kb + 16 (i / 8) + 8 half + i % 8.  The
+  // reference max m_run is raised only when a score exceeds it by more than
+  // kPfGap; the factor alpha that brings earlier sums to the new max is
+  // returned (exactly 1 when the max stays), and l_run is updated here, O
+  // by rescale() before this block's P V products.  The max is taken on raw
+  // scores (the scale is >= 0 here); scale and max are then applied in one
+  // fma per score.  In masked tiles a hidden key's probability is selected
+  // to zero, which also discards any NaN from a poisoned slot past the
+  // context.
+  bf16x8_t pf[NCB][2][2];
+  auto softmax = [&](const f32x16_t (&sacc)[NCB], int k0, int kb, auto mask_c, float (&alpha)[NCB])
+      __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      auto visible = [&](int kb, int i) {
-        return k0 + 32 * kb + 16 * (i >> 3) + 8 * half + (i & 7) <= pos[cb];
-      };
-      float mraw = -INFINITY;
+      auto visible = [&](int i) { return k0 + 32 * kb + 16 * (i >> 3) + 8 * half + (i & 7) <= pos[cb]; };
+      float v[16];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 16; ++i) v[i] = (MASK && !visible(i)) ? -INFINITY : sacc[cb][i];
+      // max as a tree (short dependency chain)
+      float t5[6];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float v = sacc[cb][kb][i];
-          mraw = fmaxf(mraw, (MASK && !visible(kb, i)) ? -INFINITY : v);
-        }
+      for (int i = 0; i < 5; ++i) t5[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+      t5[5] = v[15];
+      float mraw = fmaxf(fmaxf(fmaxf(t5[0], t5[1]), t5[2]), fmaxf(fmaxf(t5[3], t5[4]), t5[5]));
       // the two lane halves hold the two 8-key halves of every 16 keys
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw), __float_as_uint(mraw),
                                                         false, false);
       mraw = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       const float mx = mraw == -INFINITY ? -INFINITY : mraw * sl;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run[cb] + kPfGap)) {
-        const float m_new = fmaxf(m_run[cb], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);
-        m_run[cb] = m_new;
-        l_run[cb] *= alpha;
+      const bool up = mx > m_run[cb] + kPfGap;
+      const float m_new = up ? mx : m_run[cb];
+      alpha[cb] = up ? __builtin_amdgcn_exp2f(m_run[cb] - m_new) : 1.f;
+      m_run[cb] = m_new;
+      const float nm = -m_new;
+      float lsum0 = 0.f, lsum1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t wds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i0 = 8 * t + 2 * e;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][i0], sl, nm));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][i0 + 1], sl, nm));
+          if (MASK) {
+            const int lim = pos[cb] - (k0 + 32 * kb + 16 * t + 8 * half);
+            p0 = 2 * e <= lim ? p0 : 0.f;
+            p1 = 2 * e + 1 <= lim ? p1 : 0.f;
+          }
+          wds[e] = pack_bf16(p0, p1);
+          // the sum runs over the bf16 weights the P V product applies
+          if (e & 1)
+            lsum1 = dot2_bf16(wds[e], 0x3f803f80u, lsum1);
+          else
+            lsum0 = dot2_bf16(wds[e], 0x3f803f80u, lsum0);
+        }
+        pf[cb][kb][t] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
+      }
+      l_run[cb] = fmaf(l_run[cb], alpha[cb], lsum0 + lsum1);
+    }
+  };
+  // Keeps a block's probabilities computed before the rescale branch that
+  // follows them (the compiler would otherwise sink the exponentials past it,
+  // away from the matrix products they are meant to overlap).
+  auto pin_probs = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        pf_u32x4 u = __builtin_bit_cast(pf_u32x4, pf[cb][kb][t]);
+        __asm__ volatile("" : "+v"(u));
+        pf[cb][kb][t] = __builtin_bit_cast(bf16x8_t, u);
+      }
+  };
+  // O *= alpha before a block's P V products (rare: only when the max rose)
+  auto rescale = [&](const float (&alpha)[NCB]) __attribute__((always_inline)) {
+    bool any = false;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) any = any || alpha[cb] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acco[cb][db][i] *= alpha;
-      }
-      nm[cb] = -m_run[cb];
+          for (int i = 0; i < 16; ++i) acco[cb][db][i] *= alpha[cb];
     }
   };
-
-  // probabilities -> bf16 B operands.  In masked tiles a hidden key's
-  // probability is selected to zero, which also discards any NaN from a
-  // poisoned slot past the context.
-  bf16x8_t pf[NCB][2][2];
-  auto probs = [&](const f32x16_t (&sacc)[NCB][2], int k0, auto mask_c) __attribute__((always_inline)) {
+  // O^T += V^T P for key block kb: the DB output chains alternate; each V
+  // fragment is read two products ahead of its use.  In the tile holding the
+  // context end the V values of keys past it (whatever the pool holds there,
+  // possibly NaN) are cleared in the fragment: a zero probability must meet
+  // a finite value.
+  auto pv = [&](const char* st, int vf, int k0, int kb, auto mask_c) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          uint32_t wds[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i0 = 8 * t + 2 * e;
-            float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i0], sl, nm[cb]));
-            float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i0 + 1], sl, nm[cb]));
-            if (MASK) {
-              const int lim = pos[cb] - (k0 + 32 * kb + 16 * t + 8 * half);
-              p0 = 2 * e <= lim ? p0 : 0.f;
-              p1 = 2 * e + 1 <= lim ? p1 : 0.f;
-            }
-            wds[e] = pack_bf16(p0, p1);
-            // the sum runs over the bf16 weights the P V product applies
-            lsum = dot2_bf16(wds[e], 0x3f803f80u, lsum);
-          }
-          pf[cb][kb][t] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
-        }
-        l_run[cb] += lsum;
-      }
-  };
-  // O^T += V^T P: the DB output chains alternate; each V fragment is read
-  // two products ahead of its use.  In the tile holding the context end the
-  // V values of keys past it (whatever the pool holds there, possibly NaN)
-  // are cleared in the fragment: a zero probability must meet a finite value.
-  auto pv = [&](const char* st, int vf, int k0, auto mask_c) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    constexpr int NJ = 4 * C::DB;  // product j: 16-key step j / DB, dim block j % DB
+    constexpr int NJ = 2 * C::DB;  // product j: 16-key step 2 kb + j / DB, dim block j % DB
     auto vfrag = [&](int j) {
-      const int step = j / C::DB, db = j % C::DB;
+      const int step = 2 * kb + j / C::DB, db = j % C::DB;
       return *(const uint4*)(st + step * C::BLK + db * 32 * 32 + vf);
     };
     const bool tail = MASK && k0 + kPfKT > ctx;  // uniform
@@ -451,7 +471,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (j + kPfAhead < NJ) va[(j + kPfAhead) % (kPfAhead + 1)] = vfrag(j + kPfAhead);
-      const int step = j / C::DB, db = j % C::DB;
+      const int t = j / C::DB, db = j % C::DB, step = 2 * kb + t;
       uint4 f = va[j % (kPfAhead + 1)];
       if constexpr (MASK) {
         if (tail) {
@@ -466,14 +486,14 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
         acco[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, f), pf[cb][step >> 1][step & 1], acco[cb][db], 0, 0, 0);
+            __builtin_bit_cast(bf16x8_t, f), pf[cb][kb][t], acco[cb][db], 0, 0, 0);
     }
   };
 
   // ---- the ring.  Batch n is K and V of tile n, copied into stage n % S.
   // It is issued at iteration n - S + 1, after the barrier that ends every
   // read of that stage (tile n - S, read at iteration n - S).
-  f32x16_t sacc[NCB][2];
+  f32x16_t s0[NCB], s1[NCB];  // scores of the two key blocks
   int id_next = -1;  // id of this wave's block of the next tile to copy
   auto copy_tile = [&](auto J, int n) __attribute__((always_inline)) {
     copy_k(kstage(J), id_next, n);
@@ -503,10 +523,17 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     int kf = kfb, vf = vfb;
     __asm__ volatile("" : "+v"(kf), "+v"(vf));
     const int k0 = t * kPfKT;
-    scores(kstage(J), kf, sacc);
-    tile_max(sacc, k0, mask_c);
-    probs(sacc, k0, mask_c);
-    pv(vstage(J), vf, k0, mask_c);
+    float a0[NCB], a1[NCB];
+    scores(kstage(J), kf, 0, s0);
+    scores(kstage(J), kf, 1, s1);
+    softmax(s0, k0, 0, mask_c, a0);
+    pin_probs(0);
+    rescale(a0);
+    pv(vstage(J), vf, k0, 0, mask_c);
+    softmax(s1, k0, 1, mask_c, a1);
+    pin_probs(1);
+    rescale(a1);
+    pv(vstage(J), vf, k0, 1, mask_c);
   };
   auto dispatch = [&](int t, auto mask_c, auto last_c) __attribute__((always_inline)) {
     switch (t & (S - 1)) {
@@ -521,10 +548,27 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // padding columns) take the masked variant.  The last tile issues no copy.
   const int wg_min_pos = prior + q0;
   const int n_plain = wg_min_pos >= 0 ? min(iters, (wg_min_pos + 1) / kPfKT) : 0;
+  // Tiles [from, to): single iterations up to the first tile of stage 0,
+  // then whole rounds of S tiles with the stage of every read and copy a
+  // constant (one register assignment for the body), then the rest.
+  auto run = [&](int from, int to, auto mask_c) __attribute__((always_inline)) {
+    using F = std::false_type;
+    int t = from;
+    while (t < to && (t & (S - 1)) != 0) dispatch(t++, mask_c, F{});
+    for (; t + S <= to; t += S) {
+      iteration(std::integral_constant<int, 0>{}, t, mask_c, F{});
+      iteration(std::integral_constant<int, 1>{}, t + 1, mask_c, F{});
+      if constexpr (S > 2) {
+        iteration(std::integral_constant<int, 2>{}, t + 2, mask_c, F{});
+        iteration(std::integral_constant<int, 3>{}, t + 3, mask_c, F{});
+      }
+    }
+    while (t < to) dispatch(t++, mask_c, F{});
+  };
   if (iters > 0) {
     const int split = min(n_plain, iters - 1);
-    for (int t = 0; t < split; ++t) dispatch(t, std::false_type{}, std::false_type{});
-    for (int t = split; t < iters - 1; ++t) dispatch(t, std::true_type{}, std::false_type{});
+    run(0, split, std::false_type{});
+    run(split, iters - 1, std::true_type{});
     if (n_plain >= iters)
       dispatch(iters - 1, std::false_type{}, std::true_type{});
     else
