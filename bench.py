@@ -262,6 +262,49 @@ def bench_mixed_concurrent(steps=10, warmup=3):
     }
 
 
+def bench_shared_prefix(wl, pool, q, bt, cl, max_ctx, steps, warmup):
+    """pa_decode_shared_prefix on a workload whose consecutive groups of
+    samples share their prompt blocks, beside pa_decode on the same inputs."""
+    import torch
+
+    import paged_kv_cache_396_amd as pa
+
+    prompt_of = wl.extra["prompt_of"]
+    group = int(np.sum(prompt_of == prompt_of[0]))
+    n_groups = wl.num_seqs // group
+    plen = int(wl.extra["prompt_len"])
+    S, Hq, D = wl.q.shape
+    prefix = torch.full((n_groups,), plen, dtype=torch.int32, device="cuda")
+    ws_bytes = pa.pa_decode_shared_prefix_workspace_bytes(S, Hq, wl.num_kv_heads, D, max_ctx, group,
+                                                          plen)
+    ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+
+    def call():
+        pa.pa_decode_shared_prefix(out, q, pool.k, pool.v, bt, cl, max_ctx, float(wl.scale), prefix,
+                                   group, plen, pool.desc, ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    a.record(stream)
+    for _ in range(steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    unique = (n_groups * plen + int(wl.context_lens.sum()) - S * plen) * 2 * wl.num_kv_heads * D * 2
+    return {
+        "group_size": group, "prefix_tokens": plen, "call_ms": round(ms, 5),
+        "logical_gbs": round(wl.kv_bytes / (ms * 1e-3) / 1e9, 1),
+        "unique_kv_bytes": unique,
+        "unique_gbs": round(unique / (ms * 1e-3) / 1e9, 1),
+        "unique_hbm_frac": round(unique / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def bench_bulk_write(steps=5):
     """pa_reshape_and_cache of a whole Llama-2-70B-shaped layer history in one
     call: 256 sequences x 2048 tokens (524,288 tokens), 8 kv heads, d 128,
@@ -505,6 +548,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if "prompt_len" in wl.extra:
+        line["shared_prefix_call"] = bench_shared_prefix(wl, pool, q, bt, cl, max_ctx, args.steps,
+                                                         args.warmup)
     ceiling = read_ceiling()
     if not args.no_prefill:
         line["cache_write_bulk"] = bench_bulk_write()

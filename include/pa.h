@@ -154,6 +154,43 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               size_t workspace_bytes, const pa_cache_desc* desc, void* stream);
 
 /*
+ * pa_decode_shared_prefix — pa_decode for sequences that share a prompt
+ * prefix (parallel sampling: several samples of one prompt point their block
+ * tables at the same prompt blocks; zihan-zhang.net vLLM study, 3.2.2, and
+ * plumephp.com vLLM deep dive, 4.2).  Same inputs and result as pa_decode
+ * (within rounding), but every shared block is read once per group instead
+ * of once per sequence.
+ *
+ *   group_size     sequences g*group_size .. g*group_size+group_size-1 form
+ *                  group g (num_seqs must be a multiple of it)
+ *   prefix_lens    device int32 [num_seqs / group_size]: the group's shared
+ *                  tokens, a multiple of 16 and at most every member's
+ *                  context; the first prefix_lens[g] / 16 entries of the
+ *                  members' block tables must be equal.  Values out of that
+ *                  contract give unspecified output (no out-of-range access).
+ *   max_prefix_len host bound on every prefix_lens entry (multiple of 16,
+ *                  at most max_context_len; sizes the grid)
+ *   workspace      device scratch of pa_decode_shared_prefix_workspace_bytes
+ *                  bytes; same rules as pa_decode's.
+ * The other arguments are pa_decode's.  Supported: bf16 pools, D in {64, 128},
+ * num_q_heads / Hkv in {1, 2, 4, 8}, group_size * (num_q_heads / Hkv) <= 256.
+ * The prefix part runs on bf16 MFMA (P rounded to bf16, as in
+ * pa_prefill_chunk); each sequence's own blocks run through the decode
+ * kernel; one merge kernel combines the partial softmax states.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_context_len, int32_t group_size,
+                                               int32_t max_prefix_len);
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len,
+                            int32_t num_seqs, int32_t num_q_heads, float scale,
+                            const int32_t* prefix_lens, int32_t group_size,
+                            int32_t max_prefix_len, void* workspace, size_t workspace_bytes,
+                            const pa_cache_desc* desc, void* stream);
+
+/*
  * pa_prefill_chunk — causal attention of query chunks against paged KV
  * (zihan-zhang.net vLLM study, 3.5: a long prompt is processed chunk by chunk;
  * batch metadata flattens all requests' tokens into one launch).

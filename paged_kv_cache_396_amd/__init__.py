@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     pa_cache_bytes,
     pa_decode,
     pa_decode_partition_size,
+    pa_decode_shared_prefix,
+    pa_decode_shared_prefix_workspace_bytes,
     pa_decode_workspace_bytes,
     pa_prefill_chunk,
     pa_reshape_and_cache,

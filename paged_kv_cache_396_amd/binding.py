@@ -69,6 +69,11 @@ def lib():
         L.pa_decode_workspace_bytes.restype = sz
         L.pa_decode.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, f32, i32, P, sz, D, P]
         L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.pa_decode_shared_prefix_workspace_bytes.restype = sz
+        L.pa_decode_shared_prefix.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, f32, P, i32, i32,
+                                              P, sz, D, P]
+        L.pa_decode_shared_prefix.restype = ctypes.c_int
         L.pa_prefill_chunk.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, i32, f32, D, P]
         L.pa_prefill_chunk.restype = ctypes.c_int
         L.pa_bw_probe.argtypes = [P, sz, P, i32, P, P]
@@ -170,6 +175,35 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
                            block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq,
                            float(scale), int(partition_size), _ptr(workspace), ws_bytes,
                            ctypes.byref(desc), _stream(stream)))
+
+
+def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            max_context_len, group_size, max_prefix_len) -> int:
+    return int(lib().pa_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, group_size, max_prefix_len))
+
+
+def pa_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens,
+                            max_context_len: int, scale: float, prefix_lens, group_size: int,
+                            max_prefix_len: int, desc: CacheDesc, workspace, stream=None):
+    """Decode for groups of ``group_size`` consecutive sequences sharing their
+    first ``prefix_lens[g]`` tokens (int32 [num_seqs // group_size])"""
+    torch = _torch()
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (prefix_lens, "prefix_lens"), (workspace, "workspace")):
+        _dev(t, n)
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (prefix_lens, "prefix_lens")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{n} must be int32")
+    S, Hq, _ = q.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_shared_prefix(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq, float(scale),
+        _ptr(prefix_lens), int(group_size), int(max_prefix_len), _ptr(workspace), ws_bytes,
+        ctypes.byref(desc), _stream(stream)))
 
 
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,

@@ -116,7 +116,26 @@ struct DecodeParams {
   int num_partitions;
   int partition_blocks;
   float scale_log2;
+  // shared-prefix decode only: the partial states of (seq, q head) row r sit
+  // in slots r * ws_stride + (0 .. npre-1) (the prefix partitions, written by
+  // the prefix kernel) and npre + part (the sequence's own blocks)
+  const int32_t* prefix_lens;  // shared tokens of each group (multiple of 16)
+  int group_size;              // sequences per group
+  int prefix_partition;        // tokens per prefix partition
+  int max_prefix;              // prefix tokens the prefix kernel covers at most
+  int ws_stride;               // partial slots per row
 };
+
+// Shared tokens of sequence s's group, clamped to its context and rounded
+// down to whole blocks.
+__device__ inline int prefix_of(const DecodeParams& p, int s, int ctx) {
+  const int cap = ctx < p.max_prefix ? ctx : p.max_prefix;
+  const int pl = p.prefix_lens[s / p.group_size];
+  return (pl < 0 ? 0 : (pl > cap ? cap : pl)) & ~(kBlock - 1);
+}
+__device__ inline int prefix_parts(const DecodeParams& p, int pl) {
+  return (pl + p.prefix_partition - 1) / p.prefix_partition;
+}
 
 // Context length actually processed: bounded by the table row and the grid.
 __device__ inline int clamp_ctx(int ctx, const DecodeParams& p) {
@@ -399,7 +418,10 @@ constexpr int decode_waves_per_eu() {
          : (EB == 4 && D == 64 && G <= 2) ? 3 : (EB == 4 && D == 128 && G >= 4) ? 1 : 2;
 }
 
-template <int EB, int D, int G>
+// CASC: shared-prefix decode.  The workgroup covers a partition of the
+// sequence's own blocks only (those after its group's shared prefix) and
+// always leaves a partial state for the merge.
+template <int EB, int D, int G, bool CASC = false>
 __global__ __launch_bounds__(kDecodeWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<EB, D, G>())))
 void decode_partition_kernel(DecodeParams p) {
@@ -424,22 +446,37 @@ void decode_partition_kernel(DecodeParams p) {
   WaveDecoder<EB, D, G> wd;
   wd.init(pbuf[w], p.scale_log2);
   const int lane = wd.lane;
-  const int b0 = part * p.partition_blocks;
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
 
-  // The first block ids of this wave and q do not depend on the context
-  // length: issue them together with its load, so the first KV tile waits on
-  // one memory round trip instead of two.
+  int b0, ctx, nblk, nparts, pre = 0;
   int my_ids;  // id of block b0 + w + NW*(c0 + lane) for the current chunk c0
-  {
+  if constexpr (!CASC) {
+    b0 = part * p.partition_blocks;
+    // The first block ids of this wave and q do not depend on the context
+    // length: issue them together with its load, so the first KV tile waits
+    // on one memory round trip instead of two.
+    {
+      const int jb = b0 + w + NW * lane;
+      my_ids = jb < min(p.max_blocks_per_seq, b0 + p.partition_blocks) ? bt[jb] : 0;
+    }
+    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::RB, wd.qv);
+    ctx = clamp_ctx(p.context_lens[s], p);
+    nblk = (ctx + kBlock - 1) / kBlock;
+    nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  } else {
+    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::RB, wd.qv);
+    ctx = max(0, min(p.context_lens[s], p.max_blocks_per_seq * kBlock));
+    const int pl = prefix_of(p, s, ctx);
+    pre = prefix_parts(p, pl);
+    // own blocks [pl / 16, nblk), cut into at most num_partitions partitions
+    nblk = min((ctx + kBlock - 1) / kBlock, pl / kBlock + p.num_partitions * p.partition_blocks);
+    ctx = min(ctx, nblk * kBlock);
+    const int own = nblk - pl / kBlock;
+    nparts = own == 0 ? 1 : (own + p.partition_blocks - 1) / p.partition_blocks;
+    b0 = pl / kBlock + part * p.partition_blocks;
     const int jb = b0 + w + NW * lane;
-    my_ids = jb < min(p.max_blocks_per_seq, b0 + p.partition_blocks) ? bt[jb] : 0;
+    my_ids = jb < min(nblk, b0 + p.partition_blocks) ? bt[jb] : 0;
   }
-  wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::RB, wd.qv);
-
-  const int ctx = clamp_ctx(p.context_lens[s], p);
-  const int nblk = (ctx + kBlock - 1) / kBlock;
-  const int nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
   if (part >= nparts) return;  // uniform over the workgroup
   const int b1 = min(nblk, b0 + p.partition_blocks);
   wd.reset();
@@ -498,7 +535,7 @@ void decode_partition_kernel(DecodeParams p) {
   __syncthreads();
 
   // ---- merge the waves
-  const bool single = nparts == 1;
+  const bool single = !CASC && nparts == 1;
   for (int e = threadIdx.x; e < G * D; e += NW * kWave) {
     const int h = e / D;
     const int x = e - h * D;
@@ -521,7 +558,7 @@ void decode_partition_kernel(DecodeParams p) {
       else
         ((float*)p.out)[row * D + x] = val;
     } else {
-      const int64_t slot = row * p.num_partitions + part;
+      const int64_t slot = CASC ? row * p.ws_stride + pre + part : row * p.num_partitions + part;
       p.ws_o[slot * D + x] = O;
       if (x == 0) {
         p.ws_m[slot] = M;
@@ -538,14 +575,17 @@ void decode_partition_kernel(DecodeParams p) {
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  out = sum_p O_p 2^(m_p - M) / L.
 // One wave per (sequence, query head); sequences with a single partition were
 // finished by the partition kernel.
-template <int EB, int D>
+// CASC: shared-prefix decode; a row's slots are its group's prefix
+// partitions followed by its own partitions, and every row is merged here.
+template <int EB, int D, bool CASC = false>
 __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
   const int s = blockIdx.x / p.num_q_heads;
   const int hq = blockIdx.x - s * p.num_q_heads;
   const int64_t row = (int64_t)s * p.num_q_heads + hq;
-  const float* wm = p.ws_m + row * p.num_partitions;
-  const float* wl = p.ws_l + row * p.num_partitions;
-  const float* wo = p.ws_o + row * p.num_partitions * D;
+  const int stride = CASC ? p.ws_stride : p.num_partitions;  // slots per row
+  const float* wm = p.ws_m + row * stride;
+  const float* wl = p.ws_l + row * stride;
+  const float* wo = p.ws_o + row * stride * D;
   const int lane = threadIdx.x;
 
   constexpr int XL = D / kWave;  // dims per lane
@@ -565,17 +605,26 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
     float mq[PG], lq[PG], oq[PG][XL];
 #pragma unroll
     for (int j = 0; j < PG; ++j) {
-      const int q = min(q0 + j, (q0 == 0 ? p.num_partitions : nparts) - 1);
+      const int q = min(q0 + j, (q0 == 0 ? stride : nparts) - 1);
       mq[j] = wm[q];
       lq[j] = wl[q];
 #pragma unroll
       for (int e = 0; e < XL; ++e) oq[j][e] = wo[(int64_t)q * D + lane + e * kWave];
     }
     if (q0 == 0) {
-      const int ctx = clamp_ctx(p.context_lens[s], p);
-      const int nblk = (ctx + kBlock - 1) / kBlock;
-      nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
-      if (nparts <= 1) return;  // finished by the partition kernel
+      if constexpr (!CASC) {
+        const int ctx = clamp_ctx(p.context_lens[s], p);
+        const int nblk = (ctx + kBlock - 1) / kBlock;
+        nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+        if (nparts <= 1) return;  // finished by the partition kernel
+      } else {
+        const int ctx = max(0, min(p.context_lens[s], p.max_blocks_per_seq * kBlock));
+        const int pl = prefix_of(p, s, ctx);
+        const int nblk = min((ctx + kBlock - 1) / kBlock,
+                             pl / kBlock + p.num_partitions * p.partition_blocks);
+        const int own = nblk - pl / kBlock;
+        nparts = prefix_parts(p, pl) + (own == 0 ? 1 : (own + p.partition_blocks - 1) / p.partition_blocks);
+      }
     }
     float Mg = M;
 #pragma unroll
@@ -623,8 +672,55 @@ bool decode_supported(int elem_bytes, int head_dim, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
+template <int EB, int D, int G>
+static hipError_t launch_own_and_merge_t(const DecodeParams& prm, hipStream_t stream) {
+  const int64_t grid = (int64_t)prm.num_partitions * prm.num_seqs * prm.num_kv_heads;
+  hipLaunchKernelGGL((decode_partition_kernel<EB, D, G, true>), dim3((unsigned)grid),
+                     dim3(kDecodeWaves * kWave), 0, stream, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_reduce_kernel<EB, D, true>),
+                     dim3((unsigned)(prm.num_seqs * prm.num_q_heads)), dim3(kWave), 0, stream, prm);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_own_and_merge(const SharedPrefixArgs& a, const CacheGeom& g,
+                                       hipStream_t stream) {
+  DecodeParams p = {};
+  p.out = a.d.out;
+  p.q = a.d.q;
+  p.k_cache = (const char*)a.d.k_cache;
+  p.v_cache = (const char*)a.d.v_cache;
+  p.block_tables = a.d.block_tables;
+  p.context_lens = a.d.context_lens;
+  const int64_t rows = (int64_t)a.d.num_seqs * a.d.num_q_heads;
+  p.ws_m = a.d.ws;
+  p.ws_l = a.d.ws + rows * a.ws_stride;
+  p.ws_o = a.d.ws + (2 * rows * a.ws_stride + 3) / 4 * 4;
+  p.max_blocks_per_seq = a.d.max_blocks_per_seq;
+  p.num_seqs = a.d.num_seqs;
+  p.num_q_heads = a.d.num_q_heads;
+  p.num_kv_heads = g.num_kv_heads;
+  p.num_blocks = g.num_blocks;
+  p.num_partitions = a.d.num_partitions;
+  p.partition_blocks = a.d.partition_blocks;
+  p.scale_log2 = a.d.scale * kLog2e;
+  p.prefix_lens = a.prefix_lens;
+  p.group_size = a.group_size;
+  p.prefix_partition = a.prefix_partition;
+  p.max_prefix = a.prefix_parts * a.prefix_partition;
+  p.ws_stride = a.ws_stride;
+  const int G = a.d.num_q_heads / g.num_kv_heads;
+#define PA_OWN_CASE(EB_, D_, G_) \
+  if (g.elem_bytes == EB_ && g.head_dim == D_ && G == G_) return launch_own_and_merge_t<EB_, D_, G_>(p, stream);
+  PA_OWN_CASE(2, 128, 1) PA_OWN_CASE(2, 128, 2) PA_OWN_CASE(2, 128, 4) PA_OWN_CASE(2, 128, 8)
+  PA_OWN_CASE(2, 64, 1) PA_OWN_CASE(2, 64, 2) PA_OWN_CASE(2, 64, 4) PA_OWN_CASE(2, 64, 8)
+#undef PA_OWN_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, const CacheGeom& g, hipStream_t stream) {
-  DecodeParams p;
+  DecodeParams p = {};
   p.out = a.out;
   p.q = a.q;
   p.k_cache = (const char*)a.k_cache;

@@ -218,6 +218,123 @@ PA_API int pa_decode(void* out, const void* q, const void* k_cache, const void* 
   return ok();
 }
 
+namespace {
+
+// Launch plan of a shared-prefix decode (host side, from host bounds only).
+struct SharedPrefixPlan {
+  int32_t prefix_partition;  // tokens per prefix partition
+  int32_t prefix_parts;      // partitions of the longest prefix
+  int32_t own_partition;     // tokens per partition of a sequence's own blocks
+  int32_t own_parts;
+  int32_t stride;            // partial slots per (seq, q head) row
+};
+
+SharedPrefixPlan plan_shared_prefix(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx,
+                                    int32_t group_size, int32_t max_prefix) {
+  SharedPrefixPlan pl;
+  // prefix: one workgroup per (group, kv head, partition) holds a compute
+  // unit on its own (its LDS ring fills most of one), so split towards one
+  // workgroup per compute unit, in pieces of at least 256 keys
+  const int64_t units = (int64_t)(num_seqs / group_size) * num_kv_heads;
+  const int64_t cus = device_cu_count();
+  const int64_t splits = units >= cus ? 1 : (cus + units - 1) / units;
+  int64_t pp = (max_prefix + splits - 1) / splits;
+  pp = (pp + 63) / 64 * 64;
+  if (pp < 256) pp = 256;
+  pl.prefix_partition = (int32_t)pp;
+  pl.prefix_parts = max_prefix > 0 ? (int32_t)((max_prefix + pp - 1) / pp) : 0;
+  // a sequence's own blocks: the plain decode rule over the longest context
+  pl.own_partition = resolve_partition(num_seqs, num_kv_heads, max_ctx, 0);
+  pl.own_parts = (int32_t)(((int64_t)max_ctx + pl.own_partition - 1) / pl.own_partition);
+  if (pl.own_parts < 1) pl.own_parts = 1;
+  pl.stride = pl.prefix_parts + pl.own_parts;
+  return pl;
+}
+
+}  // namespace
+
+PA_API size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                      int32_t num_kv_heads, int32_t head_dim,
+                                                      int32_t max_context_len, int32_t group_size,
+                                                      int32_t max_prefix_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0 || group_size < 1 || num_seqs % group_size != 0 || max_prefix_len < 0 ||
+      max_prefix_len % PA_BLOCK_SIZE != 0 || max_prefix_len > max_context_len)
+    return 0;
+  const SharedPrefixPlan pl =
+      plan_shared_prefix(num_seqs, num_kv_heads, max_context_len, group_size, max_prefix_len);
+  return pa::shared_prefix_ws_floats((int64_t)num_seqs * num_q_heads, pl.stride, head_dim) *
+         sizeof(float);
+}
+
+PA_API int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                   float scale, const int32_t* prefix_lens, int32_t group_size,
+                                   int32_t max_prefix_len, void* workspace, size_t workspace_bytes,
+                                   const pa_cache_desc* desc, void* stream) {
+  pa::CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 1 || num_q_heads < 1)
+    return fail(PA_ERR_SHAPE, "num_seqs %d, max_context_len %d, max_blocks_per_seq %d, num_q_heads %d",
+                (int)num_seqs, (int)max_context_len, (int)max_blocks_per_seq, (int)num_q_heads);
+  if (num_q_heads % g.num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                (int)num_q_heads, g.num_kv_heads);
+  if (group_size < 1 || num_seqs % group_size != 0)
+    return fail(PA_ERR_SHAPE, "num_seqs %d is not a multiple of group_size %d", (int)num_seqs,
+                (int)group_size);
+  if (max_prefix_len < 0 || max_prefix_len % PA_BLOCK_SIZE != 0 || max_prefix_len > max_context_len)
+    return fail(PA_ERR_SHAPE, "max_prefix_len %d must be a multiple of 16 in [0, max_context_len %d]",
+                (int)max_prefix_len, (int)max_context_len);
+  const int group = num_q_heads / g.num_kv_heads;
+  if (!pa::shared_prefix_supported(g.elem_bytes, g.head_dim, group, group_size))
+    return fail(PA_ERR_UNSUPPORTED,
+                "shared-prefix decode dtype=%d head_dim=%d group=%d group_size=%d is not built",
+                (int)desc->dtype, g.head_dim, group, (int)group_size);
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !prefix_lens)
+    return fail(PA_ERR_NULL, "out, q, k_cache, v_cache, block_tables, context_lens and prefix_lens "
+                             "must be non-NULL");
+  const SharedPrefixPlan pl =
+      plan_shared_prefix(num_seqs, g.num_kv_heads, max_context_len, group_size, max_prefix_len);
+  if ((int64_t)pl.own_parts * num_seqs * g.num_kv_heads >= ((int64_t)1 << 31) ||
+      (int64_t)pl.prefix_parts * num_seqs * g.num_kv_heads >= ((int64_t)1 << 31) ||
+      (int64_t)num_seqs * num_q_heads >= ((int64_t)1 << 31))
+    return fail(PA_ERR_OVERFLOW, "shared-prefix decode grid too large");
+  const size_t need =
+      pa::shared_prefix_ws_floats((int64_t)num_seqs * num_q_heads, pl.stride, g.head_dim) * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given (ptr %p)", need,
+                workspace_bytes, workspace);
+  pa::SharedPrefixArgs a;
+  a.d.out = out;
+  a.d.q = q;
+  a.d.k_cache = k_cache;
+  a.d.v_cache = v_cache;
+  a.d.block_tables = block_tables;
+  a.d.context_lens = context_lens;
+  a.d.ws = (float*)workspace;
+  a.d.max_blocks_per_seq = max_blocks_per_seq;
+  a.d.num_seqs = num_seqs;
+  a.d.num_q_heads = num_q_heads;
+  a.d.num_partitions = pl.own_parts;
+  a.d.partition_blocks = pl.own_partition / PA_BLOCK_SIZE;
+  a.d.scale = scale;
+  a.prefix_lens = prefix_lens;
+  a.group_size = group_size;
+  a.prefix_partition = pl.prefix_partition;
+  a.prefix_parts = pl.prefix_parts;
+  a.ws_stride = pl.stride;
+  hipError_t e = pa::launch_prefix_partials(a, g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "shared-prefix launch");
+  e = pa::launch_decode_own_and_merge(a, g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "shared-prefix decode launch");
+  return ok();
+}
+
 PA_API int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* query_start_loc, const int32_t* context_lens,

@@ -63,6 +63,32 @@ int prefill_queries_per_tile(int group);
 
 hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t stream);
 
+// Shared-prefix decode: pa_decode for groups of group_size consecutive
+// sequences whose block tables begin with the same prefix_lens[group] / 16
+// blocks.  The prefix kernel reads each shared block once per group and
+// leaves partial states; the decode kernel covers each sequence's own blocks;
+// the merge combines them.
+struct SharedPrefixArgs {
+  DecodeArgs d;               // num_partitions / partition_blocks: own blocks
+  const int32_t* prefix_lens; // [num_seqs / group_size] tokens, multiples of 16
+  int group_size;
+  int prefix_partition;       // tokens per prefix partition (multiple of 64)
+  int prefix_parts;           // prefix partitions of the longest prefix
+  int ws_stride;              // partial slots per row: prefix_parts + d.num_partitions
+};
+
+// Floats of the shared-prefix workspace: m and l of every slot, then o,
+// starting on a 16-byte boundary.
+inline size_t shared_prefix_ws_floats(int64_t rows, int stride, int head_dim) {
+  const int64_t ml = (2 * rows * stride + 3) / 4 * 4;
+  return (size_t)(ml + rows * stride * head_dim);
+}
+
+bool shared_prefix_supported(int elem_bytes, int head_dim, int group, int group_size);
+hipError_t launch_prefix_partials(const SharedPrefixArgs& a, const CacheGeom& g, hipStream_t stream);
+hipError_t launch_decode_own_and_merge(const SharedPrefixArgs& a, const CacheGeom& g,
+                                       hipStream_t stream);
+
 // Streaming-read probe over 4 KiB tiles in the given order.
 hipError_t launch_bw_probe(const void* buf, size_t bytes, const int32_t* order, int ntiles,
                            uint32_t* sink, hipStream_t stream);

@@ -110,6 +110,17 @@ struct PrefillParams {
   int num_blocks;
   int num_qtiles;
   float scale_log2;
+  // shared-prefix mode only: group p's sequences p * group_size .. are the
+  // queries; the workgroup covers prefix partition j (prefix_partition keys)
+  // and leaves its partial state in slot row * ws_stride + j
+  const int32_t* prefix_lens;
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int group_size;
+  int prefix_partition;
+  int prefix_parts;  // grid extent (partitions of the longest prefix)
+  int ws_stride;
 };
 
 // Row order of a 16-key block in LDS: row m holds key pf_key16(m), i.e. the
@@ -162,7 +173,12 @@ __device__ inline void pf_copy_to_lds(const pf_rsrc& rs, unsigned lds, int voff)
 #pragma clang diagnostic pop
 }
 
-template <int D, int G, int NCB>
+// PFX: shared-prefix mode.  The queries are the newest tokens of the
+// group_size sequences of one group (all G heads of one kv head), every
+// query sees every key of the partition (they all sit past the prefix), and
+// the result is a partial state (running max in log2 units, sum, unscaled
+// output) for the decode merge instead of a normalised row.
+template <int D, int G, int NCB, bool PFX = false>
 __global__ __launch_bounds__(kPfWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kernel(PrefillParams p) {
   using C = PrefillCfg<D>;
@@ -185,32 +201,53 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   auto kstage = [&](auto J) -> char* { return stage(J); };
   auto vstage = [&](auto J) -> char* { return stage(J) + C::TILE; };
 
-  // ---- which (request, kv head, query tile): tiles of one (request, kv
-  // head) are consecutive in the "logical" order, and logical runs are
-  // assigned to one XCD (workgroups go round-robin over the 8 XCDs)
-  const int N = p.num_qtiles * p.num_reqs * p.num_kv_heads;
+  // ---- which queries and which keys.  Chunk mode: (request, kv head, query
+  // tile); tiles of one (request, kv head) are consecutive in the "logical"
+  // order, and logical runs are assigned to one XCD (workgroups go
+  // round-robin over the 8 XCDs).  Shared-prefix mode: (group, kv head,
+  // prefix partition).
   const int L = blockIdx.x;
-  const int xcd = L & 7, slot = L >> 3;
-  const int per = N >> 3, rem = N & 7;
-  const int logical = xcd * per + min(xcd, rem) + slot;
-  const int tile = logical % p.num_qtiles;
-  const int pair = logical / p.num_qtiles;
-  const int g = pair % p.num_kv_heads;
-  const int r = pair / p.num_kv_heads;
-
-  int qs = p.query_start_loc[r];
-  int qe = p.query_start_loc[r + 1];
-  qs = max(0, min(qs, p.total_q_tokens));
-  qe = max(qs, min(qe, p.total_q_tokens));
-  const int n_r = qe - qs;
-  const int q0 = tile * QT;
-  if (q0 >= n_r) return;  // uniform
-  const int ctx_cap = p.max_blocks_per_seq * kBlock;
-  const int ctx = max(0, min(p.context_lens[r], ctx_cap));
-  const int prior = ctx - n_r;  // < 0 only for out-of-contract input
-  const int q_end = min(n_r, q0 + QT);
-  const int nk = max(0, min(ctx, prior + q_end));  // keys this workgroup needs
-  const int iters = (nk + kPfKT - 1) / kPfKT;
+  int g, r, qs, n_r, q0, ctx, kbeg, nk, part = 0, prior;
+  if constexpr (!PFX) {
+    const int N = p.num_qtiles * p.num_reqs * p.num_kv_heads;
+    const int xcd = L & 7, slot = L >> 3;
+    const int per = N >> 3, rem = N & 7;
+    const int logical = xcd * per + min(xcd, rem) + slot;
+    const int tile = logical % p.num_qtiles;
+    const int pair = logical / p.num_qtiles;
+    g = pair % p.num_kv_heads;
+    r = pair / p.num_kv_heads;
+    qs = p.query_start_loc[r];
+    int qe = p.query_start_loc[r + 1];
+    qs = max(0, min(qs, p.total_q_tokens));
+    qe = max(qs, min(qe, p.total_q_tokens));
+    n_r = qe - qs;
+    q0 = tile * QT;
+    if (q0 >= n_r) return;  // uniform
+    const int ctx_cap = p.max_blocks_per_seq * kBlock;
+    ctx = max(0, min(p.context_lens[r], ctx_cap));
+    prior = ctx - n_r;  // < 0 only for out-of-contract input
+    const int q_end = min(n_r, q0 + QT);
+    kbeg = 0;
+    nk = max(0, min(ctx, prior + q_end));  // keys this workgroup needs
+  } else {
+    part = L % p.prefix_parts;
+    const int pair = L / p.prefix_parts;
+    g = pair % p.num_kv_heads;
+    const int grp = pair / p.num_kv_heads;
+    r = grp * p.group_size;  // its first sequence holds the shared block table
+    qs = r;
+    n_r = p.group_size;
+    q0 = 0;
+    const int cap = min(p.max_blocks_per_seq * kBlock, p.prefix_parts * p.prefix_partition);
+    const int pl = max(0, min(p.prefix_lens[grp], cap)) & ~(kBlock - 1);
+    kbeg = part * p.prefix_partition;
+    if (kbeg >= pl) return;  // uniform
+    ctx = min(pl, kbeg + p.prefix_partition);  // keys past ctx belong elsewhere
+    nk = ctx;
+    prior = ctx - 1;  // every query sees every key of the partition
+  }
+  const int iters = (nk - kbeg + kPfKT - 1) / kPfKT;
   const int nblk = (ctx + kBlock - 1) / kBlock;
 
   const int tid = threadIdx.x;
@@ -237,7 +274,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     const int qi = q0 + c / G;
     const int hh = c % G;
     const bool valid = qi < n_r;
-    pos[cb] = valid ? prior + qi : -1;
+    pos[cb] = valid ? (PFX ? prior : prior + qi) : -1;
     const char* qrow = p.q + ((int64_t)(qs + (valid ? qi : 0)) * p.num_q_heads + g * G + hh) * C::RB;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
@@ -286,7 +323,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   const int64_t bstride = (int64_t)p.num_kv_heads * C::BLK;  // bytes per pool block
   // id of this wave's block of tile n; -1 past the keys this workgroup needs
   auto block_id = [&](int n) __attribute__((always_inline)) {
-    const int jb = n * kPfBlocks + bsub;
+    const int jb = kbeg / kBlock + n * kPfBlocks + bsub;
     return n < iters && jb < nblk ? bt[jb] : -1;
   };
   // Buffer ranges of this wave's pool tiles of tile n.  An empty range (a
@@ -305,7 +342,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // LDS offset of piece u inside a K or V tile
   auto piece_off = [&](int u) { return bsub * C::BLK + (isub + u) * kPfDma; };
   auto copy_k = [&](char* stage, int id, int n) __attribute__((always_inline)) {
-    const int rows = min(kBlock, ctx - (n * kPfBlocks + bsub) * kBlock);
+    const int rows = min(kBlock, ctx - (kbeg / kBlock + n * kPfBlocks + bsub) * kBlock);
     const pf_rsrc rk = range(p.k_cache, id, rows * C::RB);
 #pragma unroll
     for (int u = 0; u < C::QPW; ++u) pf_copy_to_lds(rk, pf_lds_addr(stage + piece_off(u)), kvo[u]);
@@ -494,6 +531,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // It is issued at iteration n - S + 1, after the barrier that ends every
   // read of that stage (tile n - S, read at iteration n - S).
   f32x16_t s0[NCB], s1[NCB];  // scores of the two key blocks
+  const bool wave_active = q0 + 32 * w * NCB / G < n_r;  // its first column is a real query
   int id_next = -1;  // id of this wave's block of the next tile to copy
   auto copy_tile = [&](auto J, int n) __attribute__((always_inline)) {
     copy_k(kstage(J), id_next, n);
@@ -522,18 +560,20 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     // otherwise keep every stage's derived addresses live across the loop
     int kf = kfb, vf = vfb;
     __asm__ volatile("" : "+v"(kf), "+v"(vf));
-    const int k0 = t * kPfKT;
-    float a0[NCB], a1[NCB];
-    scores(kstage(J), kf, 0, s0);
-    scores(kstage(J), kf, 1, s1);
-    softmax(s0, k0, 0, mask_c, a0);
-    pin_probs(0);
-    rescale(a0);
-    pv(vstage(J), vf, k0, 0, mask_c);
-    softmax(s1, k0, 1, mask_c, a1);
-    pin_probs(1);
-    rescale(a1);
-    pv(vstage(J), vf, k0, 1, mask_c);
+    const int k0 = kbeg + t * kPfKT;
+    if (wave_active) {  // uniform: a wave with no real column only copies
+      float a0[NCB], a1[NCB];
+      scores(kstage(J), kf, 0, s0);
+      scores(kstage(J), kf, 1, s1);
+      softmax(s0, k0, 0, mask_c, a0);
+      pin_probs(0);
+      rescale(a0);
+      pv(vstage(J), vf, k0, 0, mask_c);
+      softmax(s1, k0, 1, mask_c, a1);
+      pin_probs(1);
+      rescale(a1);
+      pv(vstage(J), vf, k0, 1, mask_c);
+    }
   };
   auto dispatch = [&](int t, auto mask_c, auto last_c) __attribute__((always_inline)) {
     switch (t & (S - 1)) {
@@ -546,8 +586,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // Tiles that end before the workgroup's first query position need no
   // mask for any column; the rest (the causal diagonal, the context end and
   // padding columns) take the masked variant.  The last tile issues no copy.
-  const int wg_min_pos = prior + q0;
-  const int n_plain = wg_min_pos >= 0 ? min(iters, (wg_min_pos + 1) / kPfKT) : 0;
+  const int wg_min_pos = PFX ? prior : prior + q0;
+  const int n_plain = wg_min_pos >= kbeg ? min(iters, (wg_min_pos + 1 - kbeg) / kPfKT) : 0;
   // Tiles [from, to): single iterations up to the first tile of stage 0,
   // then whole rounds of S tiles with the stage of every read and copy a
   // constant (one register assignment for the body), then the rest.
@@ -578,15 +618,33 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(pf_vmcnt(0));
 
-  // ---- normalise and store: register i of dim block db is dim
-  // 32 db + 8 (i / 4) + 4 half + i % 4 of this lane's column
+  // ---- normalise and store (or, in shared-prefix mode, leave the partial
+  // state): register i of dim block db is dim 32 db + 8 (i / 4) + 4 half +
+  // i % 4 of this lane's column
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const float lt = l_run[cb] + xor_lane<32>(l_run[cb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int c = 32 * (w * NCB + cb) + cw;
     const int qi = q0 + c / G;
     if (qi >= n_r) continue;
+    if constexpr (PFX) {
+      const int64_t slot = ((int64_t)(qs + qi) * p.num_q_heads + g * G + c % G) * p.ws_stride + part;
+      if (half == 0) {
+        p.ws_m[slot] = m_run[cb];
+        p.ws_l[slot] = lt;
+      }
+      float* orow = p.ws_o + slot * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x16_t& a = acco[cb][db];
+          *(float4*)(orow + 32 * db + 8 * i4 + 4 * half) =
+              make_float4(a[4 * i4 + 0], a[4 * i4 + 1], a[4 * i4 + 2], a[4 * i4 + 3]);
+        }
+      continue;
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
     char* orow = (char*)p.out + ((int64_t)(qs + qi) * p.num_q_heads + g * G + c % G) * C::RB;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -610,11 +668,58 @@ static hipError_t launch_prefill_t(const PrefillParams& prm, hipStream_t stream)
   return hipGetLastError();
 }
 
+template <int D, int G>
+static hipError_t launch_prefix_t(const PrefillParams& prm, int num_groups, hipStream_t stream) {
+  constexpr int NCB = PA_PF_NCB;
+  const int64_t grid = (int64_t)prm.prefix_parts * num_groups * prm.num_kv_heads;
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true>), dim3((unsigned)grid),
+                     dim3(kPfWaves * kWave), 0, stream, prm);
+  return hipGetLastError();
+}
+
 int prefill_queries_per_tile(int group) { return kPfWaves * 32 * PA_PF_NCB / group; }
+
+
+hipError_t launch_prefix_partials(const SharedPrefixArgs& a, const CacheGeom& g, hipStream_t stream) {
+  if (a.prefix_parts == 0) return hipSuccess;
+  PrefillParams p = {};
+  p.q = (const char*)a.d.q;
+  p.k_cache = (const char*)a.d.k_cache;
+  p.v_cache = (const char*)a.d.v_cache;
+  p.block_tables = a.d.block_tables;
+  p.context_lens = a.d.context_lens;
+  p.max_blocks_per_seq = a.d.max_blocks_per_seq;
+  p.num_q_heads = a.d.num_q_heads;
+  p.num_kv_heads = g.num_kv_heads;
+  p.num_blocks = g.num_blocks;
+  p.scale_log2 = a.d.scale * kLog2e;
+  p.prefix_lens = a.prefix_lens;
+  p.group_size = a.group_size;
+  p.prefix_partition = a.prefix_partition;
+  p.prefix_parts = a.prefix_parts;
+  p.ws_stride = a.ws_stride;
+  const int64_t rows = (int64_t)a.d.num_seqs * a.d.num_q_heads;
+  p.ws_m = a.d.ws;
+  p.ws_l = a.d.ws + rows * a.ws_stride;
+  p.ws_o = a.d.ws + (2 * rows * a.ws_stride + 3) / 4 * 4;
+  const int G = a.d.num_q_heads / g.num_kv_heads;
+  const int groups = a.d.num_seqs / a.group_size;
+#define PA_PREFIX_CASE(D_, G_) \
+  if (g.head_dim == D_ && G == G_) return launch_prefix_t<D_, G_>(p, groups, stream);
+  PA_PREFIX_CASE(128, 1) PA_PREFIX_CASE(128, 2) PA_PREFIX_CASE(128, 4) PA_PREFIX_CASE(128, 8)
+  PA_PREFIX_CASE(64, 1) PA_PREFIX_CASE(64, 2) PA_PREFIX_CASE(64, 4) PA_PREFIX_CASE(64, 8)
+#undef PA_PREFIX_CASE
+  return hipErrorInvalidValue;
+}
 
 bool prefill_supported(int elem_bytes, int head_dim, int group) {
   return elem_bytes == 2 && (head_dim == 64 || head_dim == 128) &&
          (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+bool shared_prefix_supported(int elem_bytes, int head_dim, int group, int group_size) {
+  return prefill_supported(elem_bytes, head_dim, group) && group_size >= 1 &&
+         group_size <= prefill_queries_per_tile(group);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t stream) {

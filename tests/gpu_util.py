@@ -157,3 +157,31 @@ def gpu_prefill(wl, pool, max_q_len=None, query_start_loc=None, context_lens=Non
     pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, mq, float(wl.scale), pool.desc)
     t.cuda.synchronize()
     return out
+
+
+def shared_prefix_workspace(S, Hq, Hkv, D, max_ctx, group_size, max_prefix):
+    t = torch()
+    ws_bytes = pa.pa_decode_shared_prefix_workspace_bytes(S, Hq, Hkv, D, max_ctx, group_size,
+                                                          max_prefix)
+    assert ws_bytes > 0
+    return t.zeros((ws_bytes + 3) // 4, dtype=t.float32, device="cuda")
+
+
+def gpu_shared_prefix(wl, pool, group_size, prefix_lens, max_prefix=None, workspace=None):
+    """pa_decode_shared_prefix on a DecodeWorkload whose consecutive groups of
+    ``group_size`` sequences share their first ``prefix_lens[g]`` tokens."""
+    t = torch()
+    q = to_dev(wl.q, wl.dtype)
+    out = t.empty_like(q)
+    bt = t.from_numpy(np.ascontiguousarray(wl.block_tables)).cuda()
+    cl = t.from_numpy(np.ascontiguousarray(wl.context_lens, dtype=np.int32)).cuda()
+    pl = t.from_numpy(np.ascontiguousarray(prefix_lens, dtype=np.int32)).cuda()
+    maxctx = int(wl.context_lens.max())
+    mp = int(np.max(prefix_lens)) if max_prefix is None else int(max_prefix)
+    S, Hq, D = wl.q.shape
+    ws = workspace if workspace is not None else shared_prefix_workspace(
+        S, Hq, wl.num_kv_heads, D, maxctx, group_size, mp)
+    pa.pa_decode_shared_prefix(out, q, pool.k, pool.v, bt, cl, maxctx, float(wl.scale), pl,
+                               group_size, mp, pool.desc, ws)
+    t.cuda.synchronize()
+    return out

@@ -121,3 +121,42 @@ def test_bw_probe_argument_errors():
     assert L.pa_bw_probe(z, 4096, z, -1, z, z) == -2
     assert L.pa_bw_probe(z, 4096, one, 4, one, z) == -1
     assert L.pa_bw_probe(one, 100, one, 4, one, z) == -2    # no whole tile
+
+
+def _shared_raw(desc, num_seqs=8, num_q_heads=8, max_ctx=100, mb=8, group_size=4, max_prefix=64,
+                ptr=1, ws_bytes=0):
+    L = pa.lib()
+    p = ctypes.c_void_p(ptr) if ptr else ctypes.c_void_p(0)
+    return L.pa_decode_shared_prefix(p, p, p, p, p, mb, p, max_ctx, num_seqs, num_q_heads, 0.125,
+                                     p, group_size, max_prefix, p, ws_bytes,
+                                     ctypes.byref(desc) if desc is not None else None,
+                                     ctypes.c_void_p(0))
+
+
+def test_shared_prefix_argument_errors():
+    bf = pa.cache_desc(16, 2, 128, pa.PA_BF16)
+    assert _shared_raw(None) == -1
+    assert _shared_raw(pa.cache_desc(16, 2, 128, pa.PA_F32)) == -4   # bf16 only
+    assert _shared_raw(bf, group_size=3) == -2                      # 8 seqs not in groups of 3
+    assert _shared_raw(bf, group_size=0) == -2
+    assert _shared_raw(bf, max_prefix=40) == -2                     # not a multiple of 16
+    assert _shared_raw(bf, max_prefix=112) == -2                    # beyond max_context_len
+    assert _shared_raw(bf, num_q_heads=7) == -2                     # Hq % Hkv
+    assert _shared_raw(bf, num_seqs=128, group_size=128) == -4      # 128 x G 4 > 256 columns
+    assert _shared_raw(bf, ptr=0) == -1
+    assert _shared_raw(bf, ws_bytes=16) == -5                       # workspace too small
+    assert b"workspace" in pa.lib().pa_last_error()
+    assert _shared_raw(bf, num_seqs=0, group_size=1) == 0
+
+
+def test_shared_prefix_workspace_size():
+    f = pa.pa_decode_shared_prefix_workspace_bytes
+    assert f(8, 8, 2, 128, 100, 3, 64) == 0      # bad group size
+    assert f(8, 8, 2, 128, 100, 4, 40) == 0      # prefix not a multiple of 16
+    n = f(8, 8, 2, 128, 100, 4, 64)
+    # m and l per slot (rounded up to 4 floats), then D floats per slot
+    rows = 8 * 8
+    assert n > 0 and n % 4 == 0
+    slots = (n // 4) // (128 + 2)
+    assert slots >= 2                             # at least one prefix and one own slot
+    assert n == 4 * (((2 * rows * (slots // rows) + 3) // 4) * 4 + rows * (slots // rows) * 128)
