@@ -305,6 +305,66 @@ def bench_shared_prefix(wl, pool, q, bt, cl, max_ctx, steps, warmup):
     }
 
 
+def bench_block_pool(steps=10):
+    """Copy-on-write machinery: pa_copy_blocks of 4096 block pairs of an
+    8B-layer pool (8 kv heads, d 128, bf16: 64 KiB per pair in K and V), and
+    the host pool's operation rate on a parallel-sampling pattern."""
+    import torch
+
+    import paged_kv_cache_396_amd as pa
+
+    nb, Hkv, D, npairs = 16384, 8, 128, 4096
+    desc = pa.cache_desc(nb, Hkv, D, pa.PA_BF16)
+    nbytes = pa.pa_cache_bytes(desc)
+    k = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    v = torch.empty_like(k)
+    k.fill_(1)
+    v.fill_(2)
+    perm = np.random.default_rng(7).permutation(nb)[: 2 * npairs].astype(np.int32)
+    pairs = torch.from_numpy(perm.reshape(npairs, 2).copy()).cuda()
+    for _ in range(2):
+        pa.pa_copy_blocks(k, v, pairs, desc)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    a.record(stream)
+    for _ in range(steps):
+        pa.pa_copy_blocks(k, v, pairs, desc)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    moved = npairs * 2 * Hkv * 16 * D * 2 * 2  # K and V, read and written
+    del k, v
+    # host pool: 256 prompts of 300 tokens, 4 samples each, 32 decode steps
+    t0 = time.perf_counter()
+    pool = pa.BlockPool(1 << 17)
+    ops = 0
+    rng = np.random.default_rng(3)
+    for p in range(256):
+        base = p * 8
+        prompt = rng.integers(0, 32000, size=300).tolist()
+        c = pool.add_request(base, prompt)
+        pool.allocate_slots(base, prompt[c:])
+        ops += 2
+        for s in range(1, 4):
+            pool.fork(base, base + s)
+            ops += 1
+        for _ in range(32):
+            for s in range(4):
+                pool.allocate_slots(base + s, [int(rng.integers(0, 32000))])
+                ops += 1
+        for s in range(4):
+            pool.free_request(base + s)
+            ops += 1
+    host_s = time.perf_counter() - t0
+    return {
+        "copy_pairs": npairs, "copy_ms": round(ms, 5), "copy_bytes_moved": moved,
+        "copy_gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+        "host_pool_ops": ops, "host_pool_ops_per_s": round(ops / host_s, 1),
+        "host_pool_note": "through the ctypes binding, one call per operation",
+    }
+
+
 def bench_bulk_write(steps=5):
     """pa_reshape_and_cache of a whole Llama-2-70B-shaped layer history in one
     call: 256 sequences x 2048 tokens (524,288 tokens), 8 kv heads, d 128,
@@ -559,6 +619,7 @@ def main():
     if not args.no_prefill:
         line["prefill_chunk"] = bench_prefill(min(args.steps, 20), min(args.warmup, 3))
         line["long_mixed_step"] = bench_mixed_concurrent()
+        line["block_pool"] = bench_block_pool()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)

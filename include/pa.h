@@ -65,7 +65,10 @@ typedef enum {
   PA_ERR_UNSUPPORTED = -4, /* valid but not built: head_dim, GQA group, block size */
   PA_ERR_WORKSPACE = -5,   /* workspace missing or too small */
   PA_ERR_OVERFLOW = -6,    /* a size product does not fit the index types */
-  PA_ERR_HIP = -7          /* the HIP runtime reported an error */
+  PA_ERR_HIP = -7,         /* the HIP runtime reported an error */
+  PA_ERR_NO_BLOCKS = -8,   /* block pool: not enough free blocks (nothing changed) */
+  PA_ERR_NO_REQUEST = -9,  /* block pool: unknown request id */
+  PA_ERR_REQUEST_EXISTS = -10 /* block pool: request id already in use */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -189,6 +192,67 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const
                             const int32_t* prefix_lens, int32_t group_size,
                             int32_t max_prefix_len, void* workspace, size_t workspace_bytes,
                             const pa_cache_desc* desc, void* stream);
+
+/*
+ * Block pool — the host-side bookkeeping that produces block tables and
+ * slot_mapping (zihan-zhang.net vLLM study, 3.2.2 sharing and copy-on-write,
+ * 3.6 prefix caching, 5.5 the block pool; plumephp.com vLLM deep dive, 4.2).
+ *
+ * A pool of num_blocks blocks of 16 tokens; block 0 is a placeholder that is
+ * never handed out.  Requests are named by caller-chosen int64 ids.
+ *   - Blocks are shared by reference count (pa_pool_fork: parallel sampling).
+ *   - A request that writes into a partly filled block others still hold
+ *     first gets a copy (copy-on-write): pa_pool_allocate_slots returns the
+ *     (src, dst) pair, which the caller applies with pa_copy_blocks before
+ *     writing the new tokens with pa_reshape_and_cache.
+ *   - Full blocks are indexed by a prefix-cumulative hash of their tokens;
+ *     pa_pool_add_request reuses the cached blocks of a prompt up to the
+ *     first miss (and never the block holding its last token).
+ *   - Freed blocks keep their index entry and join the tail of a free queue;
+ *     allocation takes the least recently used block and drops its old entry.
+ * All pool calls are host-only (no GPU work) and not thread-safe per pool.
+ * Host pointers throughout.
+ */
+typedef struct pa_block_pool pa_block_pool;
+
+/* A new pool (NULL if num_blocks < 2 or out of memory).  Free with
+ * pa_pool_destroy. */
+pa_block_pool* pa_pool_create(int32_t num_blocks);
+void pa_pool_destroy(pa_block_pool* pool);
+/* Blocks in the free queue (unreferenced; they may still be cached). */
+int32_t pa_pool_num_free(const pa_block_pool* pool);
+/* Registers request `req` with its prompt (n token ids); *num_cached gets
+ * the number of leading prompt tokens already held by cached blocks (a
+ * multiple of 16); they need no slots.  PA_ERR_REQUEST_EXISTS if the id is
+ * in use. */
+int pa_pool_add_request(pa_block_pool* pool, int64_t req, const int32_t* prompt, int32_t n,
+                        int32_t* num_cached);
+/* Slots for the request's next n tokens, whose ids are tokens[0..n-1] (the
+ * rest of a prompt past its cached part, or newly sampled tokens):
+ * slot_mapping[i] = block * 16 + offset, in pa_reshape_and_cache's format.
+ * copy[0..1] receives a (src, dst) copy-on-write pair when *num_copies is 1.
+ * PA_ERR_NO_BLOCKS leaves the pool unchanged. */
+int pa_pool_allocate_slots(pa_block_pool* pool, int64_t req, const int32_t* tokens, int32_t n,
+                           int64_t* slot_mapping, int32_t* copy, int32_t* num_copies);
+/* `child` shares every block of `parent` (reference counts + 1). */
+int pa_pool_fork(pa_block_pool* pool, int64_t parent, int64_t child);
+/* Releases the request's blocks (last block first). */
+int pa_pool_free_request(pa_block_pool* pool, int64_t req);
+/* The request's block table: row[0..*num_blocks-1] (at most capacity
+ * entries written; *num_blocks is the full count), and its token count. */
+int pa_pool_block_table(const pa_block_pool* pool, int64_t req, int32_t* row, int32_t capacity,
+                        int32_t* num_blocks);
+int pa_pool_num_tokens(const pa_block_pool* pool, int64_t req, int32_t* num_tokens);
+
+/*
+ * pa_copy_blocks — copies every kv head's K and V of block pairs[2i] to
+ * block pairs[2i+1], raw bits (the copy-on-write copy, zihan-zhang.net vLLM
+ * study, 3.2.2).  pairs: device int32 [num_pairs][2].  Pairs naming a block
+ * outside the pool, or src == dst, are skipped; a block must not be both a
+ * destination and a source in one call.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                   const pa_cache_desc* desc, void* stream);
 
 /*
  * pa_prefill_chunk — causal attention of query chunks against paged KV

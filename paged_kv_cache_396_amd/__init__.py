@@ -5,6 +5,8 @@ build step and a ctypes binding; torch supplies device memory and streams."""
 
 from .binding import (  # noqa: F401
     BLOCK_SIZE,
+    PA_ERR_NO_BLOCKS,
+    BlockPool,
     PA_BF16,
     PA_F32,
     CacheDesc,
@@ -13,6 +15,7 @@ from .binding import (  # noqa: F401
     lib,
     pa_bw_probe,
     pa_cache_bytes,
+    pa_copy_blocks,
     pa_decode,
     pa_decode_partition_size,
     pa_decode_shared_prefix,

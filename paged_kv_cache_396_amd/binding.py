@@ -25,6 +25,7 @@ BLOCK_SIZE = 16
 _STATUS = {
     0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
     -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_OVERFLOW", -7: "PA_ERR_HIP",
+    -8: "PA_ERR_NO_BLOCKS", -9: "PA_ERR_NO_REQUEST", -10: "PA_ERR_REQUEST_EXISTS",
 }
 
 
@@ -76,6 +77,27 @@ def lib():
         L.pa_decode_shared_prefix.restype = ctypes.c_int
         L.pa_prefill_chunk.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, i32, f32, D, P]
         L.pa_prefill_chunk.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        L.pa_pool_create.argtypes = [i32]
+        L.pa_pool_create.restype = P
+        L.pa_pool_destroy.argtypes = [P]
+        L.pa_pool_destroy.restype = None
+        L.pa_pool_num_free.argtypes = [P]
+        L.pa_pool_num_free.restype = i32
+        L.pa_pool_add_request.argtypes = [P, i64, P, i32, P]
+        L.pa_pool_add_request.restype = ctypes.c_int
+        L.pa_pool_allocate_slots.argtypes = [P, i64, P, i32, P, P, P]
+        L.pa_pool_allocate_slots.restype = ctypes.c_int
+        L.pa_pool_fork.argtypes = [P, i64, i64]
+        L.pa_pool_fork.restype = ctypes.c_int
+        L.pa_pool_free_request.argtypes = [P, i64]
+        L.pa_pool_free_request.restype = ctypes.c_int
+        L.pa_pool_block_table.argtypes = [P, i64, P, i32, P]
+        L.pa_pool_block_table.restype = ctypes.c_int
+        L.pa_pool_num_tokens.argtypes = [P, i64, P]
+        L.pa_pool_num_tokens.restype = ctypes.c_int
+        L.pa_copy_blocks.argtypes = [P, P, P, i32, D, P]
+        L.pa_copy_blocks.restype = ctypes.c_int
         L.pa_bw_probe.argtypes = [P, sz, P, i32, P, P]
         L.pa_bw_probe.restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
@@ -235,3 +257,78 @@ def pa_bw_probe(buf, tile_order, sink, stream=None):
         raise ValueError("tile_order must be int32")
     _check(lib().pa_bw_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(tile_order),
                              tile_order.numel(), _ptr(sink), _stream(stream)))
+
+
+PA_ERR_NO_BLOCKS = -8
+
+
+class BlockPool:
+    """The library's host block pool (``pa_pool_*``): block tables and
+    slot_mapping for requests that share blocks by reference count, with
+    copy-on-write and a prefix index.  Host data only; no GPU work."""
+
+    def __init__(self, num_blocks: int):
+        self._h = lib().pa_pool_create(int(num_blocks))
+        if not self._h:
+            raise PAError(-2, lib().pa_last_error().decode())
+
+    def close(self):
+        if self._h:
+            lib().pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+    def num_free(self) -> int:
+        return int(lib().pa_pool_num_free(self._h))
+
+    def add_request(self, req: int, prompt) -> int:
+        """Registers ``req``; returns the number of cached prompt tokens."""
+        arr = (ctypes.c_int32 * max(1, len(prompt)))(*[int(t) for t in prompt])
+        n = ctypes.c_int32(0)
+        _check(lib().pa_pool_add_request(self._h, int(req), arr, len(prompt), ctypes.byref(n)))
+        return n.value
+
+    def allocate_slots(self, req: int, tokens):
+        """(slots, copies) for the request's next tokens; raises PAError with
+        status PA_ERR_NO_BLOCKS (pool unchanged) when blocks run out."""
+        n = len(tokens)
+        arr = (ctypes.c_int32 * max(1, n))(*[int(t) for t in tokens])
+        slots = (ctypes.c_int64 * max(1, n))()
+        copy = (ctypes.c_int32 * 2)()
+        nc = ctypes.c_int32(0)
+        _check(lib().pa_pool_allocate_slots(self._h, int(req), arr, n, slots, copy, ctypes.byref(nc)))
+        return [int(slots[i]) for i in range(n)], ([(int(copy[0]), int(copy[1]))] if nc.value else [])
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib().pa_pool_fork(self._h, int(parent), int(child)))
+
+    def free_request(self, req: int) -> None:
+        _check(lib().pa_pool_free_request(self._h, int(req)))
+
+    def block_table(self, req: int) -> list:
+        nb = ctypes.c_int32(0)
+        _check(lib().pa_pool_block_table(self._h, int(req), None, 0, ctypes.byref(nb)))
+        row = (ctypes.c_int32 * max(1, nb.value))()
+        _check(lib().pa_pool_block_table(self._h, int(req), row, nb.value, ctypes.byref(nb)))
+        return [int(row[i]) for i in range(nb.value)]
+
+    def num_tokens(self, req: int) -> int:
+        n = ctypes.c_int32(0)
+        _check(lib().pa_pool_num_tokens(self._h, int(req), ctypes.byref(n)))
+        return n.value
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, desc: CacheDesc, stream=None):
+    """Copy blocks pairs[i, 0] -> pairs[i, 1] (device int32 [n, 2]) in both pools."""
+    torch = _torch()
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (pairs, "pairs")):
+        _dev(t, n)
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [n, 2]")
+    _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0],
+                                ctypes.byref(desc), _stream(stream)))

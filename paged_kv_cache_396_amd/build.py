@@ -2,7 +2,8 @@
 
     python -m paged_kv_cache_396_amd.build
 
-Every ``csrc/*.hip`` file is compiled to an object in parallel, then linked
+Every ``csrc/*.hip`` file (and host-only ``csrc/*.cpp``) is compiled to an
+object in parallel, then linked
 into ``paged_kv_cache_396_amd/libpa.so``.  Only the C-ABI symbols declared in
 ``include/pa.h`` are exported.
 """
@@ -24,6 +25,7 @@ LIB = os.path.join(PKG, "libpa.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -44,13 +46,17 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
     extra = os.environ.get("PA_EXTRA_FLAGS", "").split()
 
     def compile_one(pair):
         src, obj = pair
-        cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
+        if src.endswith(".cpp"):  # host-only code
+            cmd = [CXX, "-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"-I{INCLUDE}",
+                   f"-I{CSRC}", "-c", src, "-o", obj]
+        else:
+            cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd))
         _run(cmd)

@@ -9,6 +9,7 @@
 #include <mutex>
 #include <string>
 
+#include "block_pool.h"
 #include "pa_launch.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
@@ -395,6 +396,106 @@ PA_API int pa_bw_probe(const void* buf, size_t bytes, const int32_t* tile_order,
   return ok();
 }
 
+// ---- block pool (host only)
+
+struct pa_block_pool {
+  pa::BlockPool pool;
+  explicit pa_block_pool(int32_t n) : pool(n) {}
+};
+
+namespace {
+int pool_status(int s, int64_t req) {
+  switch (s) {
+    case 0: return ok();
+    case -1: return fail(PA_ERR_NO_REQUEST, "unknown request %lld", (long long)req);
+    case -2: return fail(PA_ERR_REQUEST_EXISTS, "request id %lld is in use", (long long)req);
+    default: return fail(PA_ERR_NO_BLOCKS, "not enough free blocks for request %lld", (long long)req);
+  }
+}
+}  // namespace
+
+PA_API pa_block_pool* pa_pool_create(int32_t num_blocks) {
+  if (num_blocks < 2 || (int64_t)num_blocks * PA_BLOCK_SIZE >= ((int64_t)1 << 31)) {
+    fail(PA_ERR_SHAPE, "num_blocks %d (2 .. 2^27-1)", (int)num_blocks);
+    return nullptr;
+  }
+  try {
+    pa_block_pool* p = new pa_block_pool(num_blocks);
+    ok();
+    return p;
+  } catch (...) {
+    fail(PA_ERR_OVERFLOW, "out of host memory for %d blocks", (int)num_blocks);
+    return nullptr;
+  }
+}
+
+PA_API void pa_pool_destroy(pa_block_pool* pool) { delete pool; }
+
+PA_API int32_t pa_pool_num_free(const pa_block_pool* pool) {
+  return pool ? pool->pool.num_free() : 0;
+}
+
+PA_API int pa_pool_add_request(pa_block_pool* pool, int64_t req, const int32_t* prompt, int32_t n,
+                               int32_t* num_cached) {
+  if (!pool || !num_cached || (n > 0 && !prompt)) return fail(PA_ERR_NULL, "pool, prompt and num_cached must be non-NULL");
+  if (n < 0) return fail(PA_ERR_SHAPE, "prompt length %d", (int)n);
+  return pool_status(pool->pool.add_request(req, prompt, n, num_cached), req);
+}
+
+PA_API int pa_pool_allocate_slots(pa_block_pool* pool, int64_t req, const int32_t* tokens, int32_t n,
+                                  int64_t* slot_mapping, int32_t* copy, int32_t* num_copies) {
+  if (!pool || !copy || !num_copies || (n > 0 && (!tokens || !slot_mapping)))
+    return fail(PA_ERR_NULL, "pool, tokens, slot_mapping, copy and num_copies must be non-NULL");
+  if (n < 0) return fail(PA_ERR_SHAPE, "token count %d", (int)n);
+  const int32_t have = pool->pool.num_tokens(req);
+  if (have >= 0 && (int64_t)have + n >= ((int64_t)1 << 31) - PA_BLOCK_SIZE)
+    return fail(PA_ERR_OVERFLOW, "request %lld would exceed 2^31 tokens", (long long)req);
+  return pool_status(pool->pool.allocate_slots(req, tokens, n, slot_mapping, copy, num_copies), req);
+}
+
+PA_API int pa_pool_fork(pa_block_pool* pool, int64_t parent, int64_t child) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  const int s = pool->pool.fork(parent, child);
+  return pool_status(s, s == -2 ? child : parent);
+}
+
+PA_API int pa_pool_free_request(pa_block_pool* pool, int64_t req) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  return pool_status(pool->pool.free_request(req), req);
+}
+
+PA_API int pa_pool_block_table(const pa_block_pool* pool, int64_t req, int32_t* row,
+                               int32_t capacity, int32_t* num_blocks) {
+  if (!pool || !num_blocks || (capacity > 0 && !row))
+    return fail(PA_ERR_NULL, "pool, row and num_blocks must be non-NULL");
+  const std::vector<int32_t>* t = pool->pool.table(req);
+  if (!t) return fail(PA_ERR_NO_REQUEST, "unknown request %lld", (long long)req);
+  *num_blocks = (int32_t)t->size();
+  for (int32_t i = 0; i < capacity && i < (int32_t)t->size(); ++i) row[i] = (*t)[i];
+  return ok();
+}
+
+PA_API int pa_pool_num_tokens(const pa_block_pool* pool, int64_t req, int32_t* num_tokens) {
+  if (!pool || !num_tokens) return fail(PA_ERR_NULL, "pool and num_tokens must be non-NULL");
+  const int32_t n = pool->pool.num_tokens(req);
+  if (n < 0) return fail(PA_ERR_NO_REQUEST, "unknown request %lld", (long long)req);
+  *num_tokens = n;
+  return ok();
+}
+
+PA_API int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                          const pa_cache_desc* desc, void* stream) {
+  pa::CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0 || num_pairs >= (1 << 30)) return fail(PA_ERR_SHAPE, "num_pairs %d", (int)num_pairs);
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !pairs) return fail(PA_ERR_NULL, "k_cache, v_cache and pairs must be non-NULL");
+  hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+  return ok();
+}
+
 PA_API const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";
@@ -405,6 +506,9 @@ PA_API const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_OVERFLOW: return "size overflow";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PA_ERR_NO_REQUEST: return "unknown request";
+    case PA_ERR_REQUEST_EXISTS: return "request id in use";
     default: return "unknown status";
   }
 }

@@ -89,6 +89,11 @@ hipError_t launch_prefix_partials(const SharedPrefixArgs& a, const CacheGeom& g,
 hipError_t launch_decode_own_and_merge(const SharedPrefixArgs& a, const CacheGeom& g,
                                        hipStream_t stream);
 
+// Copies every kv head's K and V of block pairs[2i] to block pairs[2i+1]
+// (device int32 pairs).
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
+                              const CacheGeom& g, hipStream_t stream);
+
 // Streaming-read probe over 4 KiB tiles in the given order.
 hipError_t launch_bw_probe(const void* buf, size_t bytes, const int32_t* order, int ntiles,
                            uint32_t* sink, hipStream_t stream);
