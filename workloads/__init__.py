@@ -9,6 +9,9 @@ without sharing any of the method's code.
 from .configs import (  # noqa: F401
     BLOCK_SIZE,
     CONFIG_NAMES,
+    FP8_K_SCALE,
+    FP8_POISON,
+    FP8_V_SCALE,
     DecodeWorkload,
     PrefillWorkload,
     bf16_bits_from_f32,
