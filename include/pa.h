@@ -20,7 +20,8 @@
  *     on `stream` (a hipStream_t, NULL = the null stream) and the call returns
  *     before the GPU finishes.
  *   - q, k, v and out are dense row-major [tokens][heads][head_dim] in the
- *     cache dtype (fp32 or bf16); out has the dtype of q.
+ *     cache dtype (fp32 or bf16; bf16 for PA_FP8_E4M3 pools); out has the
+ *     dtype of q.
  *   - Block tables are int32 [rows][max_blocks_per_seq]; entries past a
  *     sequence's ceil(len / 16) blocks are never read.
  *   - Argument errors detected on the host return a negative pa_status and
@@ -54,7 +55,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 #define PA_BLOCK_SIZE 16
 
 typedef enum {
@@ -71,7 +72,14 @@ typedef enum {
   PA_ERR_REQUEST_EXISTS = -10 /* block pool: request id already in use */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* Pool element types.  PA_FP8_E4M3 pools hold one 8-bit code per element
+ * (E4M3 of the OCP 8-bit floating-point format: 1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits, no infinities, largest magnitude 448) and
+ * one fp32 scale per pool; the activations that meet such a pool (k and v
+ * rows written, q, out) are bf16.  The pages name an fp8 KV cache for its
+ * doubled capacity and halved attention bytes (plumephp.com vLLM deep dive,
+ * 4.2.1) without fixing a format or scaling; these are the readings taken. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
 /* Describes one layer's K and V pools (both have the same shape). */
 typedef struct {
@@ -80,6 +88,9 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv >= 1 */
   int32_t head_dim;     /* D: 64 or 128 */
   int32_t dtype;        /* a pa_dtype */
+  float k_scale;        /* PA_FP8_E4M3 only (finite, > 0): K code c stands for
+                           value(c) * k_scale; ignored for other dtypes */
+  float v_scale;        /* the same for the V pool */
 } pa_cache_desc;
 
 /* PA_ABI_VERSION of the built library. */
@@ -93,14 +104,20 @@ size_t pa_cache_bytes(const pa_cache_desc* desc);
  * ("vLLM: from PagedAttention ...", 3.3: kernels address scattered blocks
  * through slot_mapping).
  *
- *   k, v          device, [num_tokens][Hkv][D] in the cache dtype
+ *   k, v          device, [num_tokens][Hkv][D] in the cache dtype (bf16 for
+ *                 PA_FP8_E4M3 pools)
  *   slot_mapping  device int64 [num_tokens]; token i goes to block
  *                 slot / 16, offset slot % 16.  A negative slot marks a
  *                 padding token and writes nothing.  Slots at or beyond
  *                 num_blocks * 16 are ignored.  Two tokens with the same slot
  *                 in one call give an unspecified winner.
  *   k_cache, v_cache  device pools laid out as described above.
- * The copy is bit-exact (no value conversion).  num_tokens == 0 is a no-op.
+ * For bf16 and fp32 pools the copy is bit-exact (no value conversion).  For
+ * PA_FP8_E4M3 pools each value x is stored as the E4M3 code nearest to
+ * x / scale (the quotient one correctly rounded fp32 division), ties to the
+ * even code; magnitudes beyond 448, infinities included, saturate to 448 with
+ * x's sign, and a NaN gives code 0x7F with x's sign bit.  num_tokens == 0 is
+ * a no-op.
  */
 int pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
                          int32_t num_tokens, void* k_cache, void* v_cache,
@@ -131,7 +148,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * block, score the 16 keys, then weight the 16 values; 4.3.1: online softmax).
  *
  *   out            device [num_seqs][num_q_heads][D], dtype of the cache
- *   q              device [num_seqs][num_q_heads][D]
+ *                  (bf16 for PA_FP8_E4M3 pools)
+ *   q              device [num_seqs][num_q_heads][D], same dtype as out
  *   block_tables   device int32 [num_seqs][max_blocks_per_seq]
  *   context_lens   device int32 [num_seqs]; counts the newest token, whose K/V
  *                  must already be in the pools (write it with
@@ -148,7 +166,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                  initialisation and are overwritten; two calls in flight at
  *                  the same time must not share a workspace.
  * Query head h reads kv head h / (num_q_heads / Hkv).  Supported:
- * D in {64, 128}, num_q_heads / Hkv in {1, 2, 4, 8}.  Accumulation is fp32.
+ * D in {64, 128}, num_q_heads / Hkv in {1, 2, 4, 8} (PA_FP8_E4M3 pools:
+ * D = 128).  Accumulation is fp32.  With PA_FP8_E4M3 pools every code is
+ * widened exactly to bf16 and attention runs over value(code) * scale: the
+ * K scale is folded into `scale`, the V scale into the final normalisation.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -86,12 +86,15 @@ def encode_f32(x: np.ndarray) -> np.ndarray:
 
 
 def quantize(raw: np.ndarray, dtype: str, scale) -> np.ndarray:
-    """Codes of raw bf16 (or fp32) values under ``scale``: x / scale in fp32,
-    then ``encode_f32``."""
+    """Codes of raw bf16 (or fp32) values under ``scale`` (> 0): x / scale in
+    fp32, then ``encode_f32``; a NaN input gives 0x7F with its own sign bit."""
     x = widen(raw, dtype).astype(np.float32)  # exact: the inputs are fp32-representable
     with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
         qt = x / np.float32(scale)
-    return encode_f32(qt)
+    codes = encode_f32(qt)
+    nan = np.isnan(x)
+    sign = ((x.view(np.uint32) >> np.uint32(31)).astype(np.uint8)) << np.uint8(7)
+    return np.where(nan, np.uint8(NAN_CODE) | sign, codes).astype(np.uint8)
 
 
 def dequantize(codes: np.ndarray, scale) -> np.ndarray:

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     BlockPool,
     PA_BF16,
     PA_F32,
+    PA_FP8_E4M3,
     CacheDesc,
     PAError,
     cache_desc,

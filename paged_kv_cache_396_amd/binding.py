@@ -18,8 +18,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # PA_LIB may name another build of the same library (e.g. a tuning variant)
 LIB_PATH = os.environ.get("PA_LIB") or os.path.join(PKG, "libpa.so")
 
+ABI_VERSION = 2  # the pa_cache_desc layout below
 PA_F32 = 0
 PA_BF16 = 1
+PA_FP8_E4M3 = 2
 BLOCK_SIZE = 16
 
 _STATUS = {
@@ -42,6 +44,8 @@ class CacheDesc(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -60,6 +64,9 @@ def lib():
         i32, f32, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
         D = ctypes.POINTER(CacheDesc)
         L.pa_abi_version.restype = ctypes.c_int
+        if L.pa_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.pa_abi_version()}, the binding "
+                               f"expects {ABI_VERSION}: rebuild it")
         L.pa_cache_bytes.argtypes = [D]
         L.pa_cache_bytes.restype = sz
         L.pa_reshape_and_cache.argtypes = [P, P, P, i32, P, P, D, P]
@@ -124,12 +131,18 @@ def dtype_code(torch_dtype) -> int:
         return PA_BF16
     if torch_dtype == torch.float32:
         return PA_F32
+    if torch_dtype in ("fp8", torch.float8_e4m3fn):
+        return PA_FP8_E4M3
     raise ValueError(f"unsupported dtype {torch_dtype}")
 
 
-def cache_desc(num_blocks: int, num_kv_heads: int, head_dim: int, dtype) -> CacheDesc:
+def cache_desc(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, k_scale: float = 1.0,
+               v_scale: float = 1.0) -> CacheDesc:
+    """Pool descriptor; ``k_scale`` / ``v_scale`` matter for fp8 pools only
+    (dtype ``"fp8"``, ``torch.float8_e4m3fn`` or ``PA_FP8_E4M3``)."""
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
-    return CacheDesc(num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, code)
+    return CacheDesc(num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, code, float(k_scale),
+                     float(v_scale))
 
 
 def pa_cache_bytes(desc: CacheDesc) -> int:

@@ -131,14 +131,115 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
   }
 }
 
+// ---- fp8 (E4M3) pools
+//
+// An fp8 pool stores one E4M3 code per element (1 sign, 4 exponent bits with
+// bias 7, 3 mantissa bits; no infinities, largest magnitude 448) and one fp32
+// scale per pool: code c stands for value(c) * scale.  The pages only say
+// that an fp8 KV cache doubles capacity and halves attention's bytes
+// (plumephp.com vLLM deep dive, 4.2.1); the format, the per-pool scale and
+// the rounding below are the readings taken for it.  An incoming bf16 value
+// x becomes the E4M3 code nearest to x / scale (one correctly rounded fp32
+// division), ties to the even code, magnitudes beyond 448 saturating; a NaN
+// becomes 0x7F with x's sign bit.
+
+// Four bf16 values (two words, element order lo, hi, lo, hi) -> one word of
+// four codes, element i in byte i.
+__device__ inline uint32_t quantize4(uint32_t w0, uint32_t w1, float scale) {
+  const float x[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(x[i] / scale, -448.f), 448.f);
+  // the conversion rounds to nearest even; the clamp keeps it in range
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], r, true);
+  uint32_t keep = 0xffffffffu, nan = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (x[i] != x[i]) {
+      keep &= ~(0xffu << (8 * i));
+      nan |= (0x7fu | ((__float_as_uint(x[i]) >> 31) << 7)) << (8 * i);
+    }
+  }
+  return ((uint32_t)r & keep) | nan;
+}
+
+// One workgroup takes 16 consecutive input tokens of one kv head, as the
+// bf16/fp32 kernel does.  Input chunk c (8 bf16 of one token) becomes 8 codes.
+__global__ __launch_bounds__(kCwThreads) void cache_write_fp8_kernel(
+    const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slots,
+    int num_tokens, int num_kv_heads, int head_dim, int64_t pool_slots, float k_scale,
+    float v_scale, char* __restrict__ k_cache, char* __restrict__ v_cache) {
+  __shared__ int64_t sl[kBlock];
+  // codes of the V tile, dim-major: byte (x, o) at x * 16 + o
+  __shared__ __attribute__((aligned(16))) uint8_t vt[128 * kBlock];
+
+  const int tid = threadIdx.x;
+  const int g = blockIdx.y;
+  const int64_t i0 = (int64_t)blockIdx.x * kBlock;
+  const int RC = head_dim / 8;   // 16-byte input chunks per row
+  const int nch = kBlock * RC;   // <= kCwThreads
+  const int j = tid / RC, x = tid - j * RC;
+  const bool mine = tid < nch && i0 + j < num_tokens;
+  uint2 kq = make_uint2(0, 0), vq = make_uint2(0, 0);
+  if (mine) {
+    const int64_t row = ((i0 + j) * num_kv_heads + g) * RC + x;
+    const uint4 kr = k[row], vr = v[row];
+    kq = make_uint2(quantize4(kr.x, kr.y, k_scale), quantize4(kr.z, kr.w, k_scale));
+    vq = make_uint2(quantize4(vr.x, vr.y, v_scale), quantize4(vr.z, vr.w, v_scale));
+  }
+  bool in_order = true;
+  if (tid < kBlock) {
+    const bool real = i0 + tid < num_tokens;
+    const int64_t s0 = slots[i0];
+    const int64_t s = real ? slots[i0 + tid] : -1;
+    sl[tid] = s;
+    in_order = real && s0 >= 0 && s0 % kBlock == 0 && s0 + kBlock <= pool_slots && s == s0 + tid;
+  }
+  const bool full = __syncthreads_and(in_order);
+  const uint8_t* vb = (const uint8_t*)&vq;
+
+  if (full) {
+    const int64_t base = tile_base(sl[0] / kBlock, g, num_kv_heads, head_dim);  // bytes
+    if (tid < nch) {
+      *(uint2*)(k_cache + base + j * head_dim + x * 8) = kq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[(x * 8 + e) * kBlock + j] = vb[e];
+    }
+    __syncthreads();
+    if (tid < head_dim) *(uint4*)(v_cache + base + tid * kBlock) = *(const uint4*)&vt[tid * kBlock];
+    return;
+  }
+
+  // scattered tokens: each token on its own
+  if (!mine) return;
+  const int64_t slot = sl[j];
+  if (slot < 0 || slot >= pool_slots) return;
+  const int64_t b = slot / kBlock;
+  const int o = (int)(slot - b * kBlock);
+  const int64_t base = tile_base(b, g, num_kv_heads, head_dim);
+  *(uint2*)(k_cache + base + o * head_dim + x * 8) = kq;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v_cache[base + (x * 8 + e) * kBlock + o] = (char)vb[e];
+}
+
 hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slots, int num_tokens,
                               void* k_cache, void* v_cache, const CacheGeom& g, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  if ((int64_t)kBlock * g.head_dim * g.elem_bytes / 16 > (int64_t)kCwMaxChunks * kCwThreads)
-    return hipErrorInvalidValue;
   const int64_t groups = ((int64_t)num_tokens + kBlock - 1) / kBlock;
   if (groups >= ((int64_t)1 << 31) || g.num_kv_heads > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)groups, (unsigned)g.num_kv_heads);
+  if (g.elem_bytes == 1) {
+    // bf16 input rows: 16 tokens x D / 8 chunks, one per thread
+    if (g.head_dim % 8 != 0 || g.head_dim > 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cache_write_fp8_kernel, grid, dim3(kCwThreads), 0, stream, (const uint4*)k,
+                       (const uint4*)v, slots, num_tokens, g.num_kv_heads, g.head_dim,
+                       (int64_t)g.num_blocks * kBlock, g.k_scale, g.v_scale, (char*)k_cache,
+                       (char*)v_cache);
+    return hipGetLastError();
+  }
+  if ((int64_t)kBlock * g.head_dim * g.elem_bytes / 16 > (int64_t)kCwMaxChunks * kCwThreads)
+    return hipErrorInvalidValue;
   const size_t lds = (size_t)kBlock * (g.head_dim * g.elem_bytes + 16);
   const int64_t pool_slots = (int64_t)g.num_blocks * kBlock;
   if (g.elem_bytes == 2) {

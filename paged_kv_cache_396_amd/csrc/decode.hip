@@ -74,10 +74,13 @@ __device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, int off) {
 template <int EB, int D, int G>
 struct DecodeCfg {
   static constexpr int RB = D * EB;                  // bytes of one K row
+  static constexpr int QB = EB == 4 ? 4 : 2;         // bytes of a q / out element (bf16 for fp8 pools)
+  static constexpr int QRB = D * QB;                 // bytes of one q row
   static constexpr int LPR = RB >= 256 ? 16 : 8;     // lanes per K row
   static constexpr int U = RB / 16 / LPR;            // 16-byte chunks per lane per row
   static constexpr int NR = LPR / 4;                 // K rows per lane per tile
   static constexpr int EPC = 16 / EB;                // elements per 16-byte chunk
+  static constexpr int QCH = EPC * QB / 16;          // 16-byte q chunks per K chunk
   static constexpr int N0 = NR * G;                  // partial dots per lane
   static constexpr int LOGL = ilog2(LPR);
   static constexpr int HALV = cmin(LOGL, ilog2(N0)); // halving steps of the reduce-scatter
@@ -93,9 +96,10 @@ struct DecodeCfg {
   static constexpr int VCPR = kBlock / VTPC;         // chunks per dim-row (= EB)
   static constexpr int NV = D * VCPR / kWave;        // V chunks (dims) per lane
   static constexpr int VPART_BITS = VCPR - 1;        // lanes holding other tokens of our dims
-  static constexpr int PWORDS = EB == 2 ? 1 : 2;     // 32-bit words per (pair, head) of P
+  static constexpr int PWORDS = EB == 4 ? 2 : 1;     // 32-bit words per (pair, head) of P
   static_assert(NF <= 2 && NF <= NR, "unsupported GQA group for this head size");
   static_assert(NV >= 1 && D * VCPR % kWave == 0, "V chunk mapping");
+  static_assert(U >= 1, "K row shorter than one chunk per lane");
 };
 
 struct DecodeParams {
@@ -116,6 +120,7 @@ struct DecodeParams {
   int num_partitions;
   int partition_blocks;
   float scale_log2;
+  float v_scale;  // fp8 pools: applied with the final normalisation
   // shared-prefix decode only: the partial states of (seq, q head) row r sit
   // in slots r * ws_stride + (0 .. npre-1) (the prefix partitions, written by
   // the prefix kernel) and npre + part (the sequence's own blocks)
@@ -196,7 +201,7 @@ struct WaveDecoder {
   int hh, tk0;  // this lane's scores: head hh, tokens tk0 (+1 if NF == 2)
   float scale_log2;
   uint32_t* pb;  // this wave's probability exchange buffer in LDS
-  uint4 qv[G][C::U];
+  uint4 qv[G][C::U * C::QCH];
   float o[G][C::NV];
   float m_mine;  // reference max (log2 units) of this lane's head
   float l_mine;  // sum of this lane's probabilities
@@ -223,13 +228,18 @@ struct WaveDecoder {
     l_mine = 0.f;
   }
 
-  // q chunks of the G heads of one kv head; qbase points at its first head's row
-  __device__ void load_q(const char* qbase, uint4 (&dst)[G][C::U]) const {
+  // q chunks of the G heads of one kv head; qbase points at its first head's
+  // row.  K chunk u of the lane holds elements (u * LPR + c) * EPC + 0..EPC-1;
+  // the matching q elements are QCH 16-byte chunks.
+  __device__ void load_q(const char* qbase, uint4 (&dst)[G][C::U * C::QCH]) const {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int u = 0; u < C::U; ++u)
-        dst[h][u] = *(const uint4*)(qbase + (int64_t)h * C::RB + (u * C::LPR + c) * 16);
+#pragma unroll
+        for (int j = 0; j < C::QCH; ++j)
+          dst[h][u * C::QCH + j] = *(const uint4*)(qbase + (int64_t)h * C::QRB +
+                                                   ((u * C::LPR + c) * C::QCH + j) * 16);
   }
 
   // One (block, kv head) tile through buffer descriptors of nrec bytes: a
@@ -253,6 +263,34 @@ struct WaveDecoder {
   __device__ void process(uint4 (&kc)[C::NR][C::U], uint4 (&vc)[C::NV], int nvalid) {
     // ---- partial dots
     float acc[C::N0];
+    if constexpr (EB == 1) {
+      // every code widens exactly to bf16: word w of a chunk gives the bf16
+      // pairs of elements 4w, 4w+1 and 4w+2, 4w+3
+      uint32_t kw[C::NR][C::U][8];
+#pragma unroll
+      for (int i = 0; i < C::NR; ++i)
+#pragma unroll
+        for (int u = 0; u < C::U; ++u) {
+          const uint32_t w4[4] = {kc[i][u].x, kc[i][u].y, kc[i][u].z, kc[i][u].w};
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            kw[i][u][2 * w] = fp8x2_to_bf16x2<false>(w4[w]);
+            kw[i][u][2 * w + 1] = fp8x2_to_bf16x2<true>(w4[w]);
+          }
+        }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < C::NR; ++i) {
+          float a = 0.f;
+#pragma unroll
+          for (int u = 0; u < C::U; ++u)
+#pragma unroll
+            for (int pr = 0; pr < 8; ++pr)
+              a = dot2_bf16(((const uint32_t*)&qv[h][u * 2 + (pr >> 2)])[pr & 3], kw[i][u][pr], a);
+          acc[h * C::NR + i] = a;
+        }
+    } else
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -290,7 +328,12 @@ struct WaveDecoder {
       uint32_t keep[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if constexpr (EB == 2) {
+        if constexpr (EB == 1) {
+          uint32_t m = 0;  // bytes 0..3 hold tokens 4e..4e+3
+#pragma unroll
+          for (int b = 0; b < 4; ++b) m |= (4 * e + b < nvalid ? 0xffu : 0u) << (8 * b);
+          keep[e] = m;
+        } else if constexpr (EB == 2) {
           const int t0 = vpart * C::VTPC + 2 * e;
           keep[e] = t0 >= nvalid ? 0u : (t0 + 1 >= nvalid ? 0x0000ffffu : 0xffffffffu);
         } else {
@@ -333,7 +376,7 @@ struct WaveDecoder {
     }
 
     // ---- probabilities -> LDS as [pair][head] (bf16 pairs or fp32 pairs)
-    if constexpr (EB == 2) {
+    if constexpr (EB <= 2) {
       if constexpr (C::NF == 2) {
         pb[(tk0 >> 1) * G + hh] = pack_bf16(pr[0], pr[1]);
       } else {
@@ -355,7 +398,32 @@ struct WaveDecoder {
     // or token e (fp32)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if constexpr (EB == 2) {
+      if constexpr (EB == 1) {
+        // word e of a V chunk holds the codes of tokens 4e..4e+3 (one dim)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int tp = 2 * e + half;  // token pair within the block
+          uint32_t pw[G];
+          if constexpr (G % 4 == 0) {
+#pragma unroll
+            for (int h4 = 0; h4 < G / 4; ++h4) {
+              const uint4 t4 = *(const uint4*)&pb[tp * G + h4 * 4];
+              pw[h4 * 4 + 0] = t4.x; pw[h4 * 4 + 1] = t4.y;
+              pw[h4 * 4 + 2] = t4.z; pw[h4 * 4 + 3] = t4.w;
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < G; ++h) pw[h] = pb[tp * G + h];
+          }
+#pragma unroll
+          for (int i = 0; i < C::NV; ++i) {
+            const uint32_t raw = ((const uint32_t*)&vc[i])[e];
+            const uint32_t wv = half ? fp8x2_to_bf16x2<true>(raw) : fp8x2_to_bf16x2<false>(raw);
+#pragma unroll
+            for (int h = 0; h < G; ++h) o[h][i] = dot2_bf16(pw[h], wv, o[h][i]);
+          }
+        }
+      } else if constexpr (EB == 2) {
         const int tp = vpart * (C::VTPC / 2) + e;  // token pair within the block
         uint32_t pw[G];
         if constexpr (G % 4 == 0) {
@@ -414,7 +482,8 @@ struct WaveDecoder {
 #endif
 template <int EB, int D, int G>
 constexpr int decode_waves_per_eu() {
-  return (EB == 2 && G <= 4) ? PA_DECODE_OCC_BF16_G4
+  return (EB == 1) ? (G <= 4 ? 3 : 2)
+         : (EB == 2 && G <= 4) ? PA_DECODE_OCC_BF16_G4
          : (EB == 4 && D == 64 && G <= 2) ? 3 : (EB == 4 && D == 128 && G >= 4) ? 1 : 2;
 }
 
@@ -459,12 +528,12 @@ void decode_partition_kernel(DecodeParams p) {
       const int jb = b0 + w + NW * lane;
       my_ids = jb < min(p.max_blocks_per_seq, b0 + p.partition_blocks) ? bt[jb] : 0;
     }
-    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::RB, wd.qv);
+    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::QRB, wd.qv);
     ctx = clamp_ctx(p.context_lens[s], p);
     nblk = (ctx + kBlock - 1) / kBlock;
     nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
   } else {
-    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::RB, wd.qv);
+    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::QRB, wd.qv);
     ctx = max(0, min(p.context_lens[s], p.max_blocks_per_seq * kBlock));
     const int pl = prefix_of(p, s, ctx);
     pre = prefix_parts(p, pl);
@@ -552,8 +621,9 @@ void decode_partition_kernel(DecodeParams p) {
     const int hq = g * G + h;
     const int64_t row = (int64_t)s * p.num_q_heads + hq;
     if (single) {
-      const float val = L > 0.f ? O / L : 0.f;
-      if constexpr (EB == 2)
+      float val = L > 0.f ? O / L : 0.f;
+      if constexpr (EB == 1) val *= p.v_scale;
+      if constexpr (EB <= 2)
         ((uint16_t*)p.out)[row * D + x] = to_bf16(val);
       else
         ((float*)p.out)[row * D + x] = val;
@@ -643,12 +713,13 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
     }
     M = Mg;
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float inv = L > 0.f ? 1.f / L : 0.f;
+  if constexpr (EB == 1) inv *= p.v_scale;
 #pragma unroll
   for (int e = 0; e < XL; ++e) {
     const float val = acc[e] * inv;
     const int x = lane + e * kWave;
-    if constexpr (EB == 2)
+    if constexpr (EB <= 2)
       ((uint16_t*)p.out)[row * D + x] = to_bf16(val);
     else
       ((float*)p.out)[row * D + x] = val;
@@ -668,8 +739,9 @@ static hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream) {
 }
 
 bool decode_supported(int elem_bytes, int head_dim, int group) {
-  return (elem_bytes == 2 || elem_bytes == 4) && (head_dim == 64 || head_dim == 128) &&
-         (group == 1 || group == 2 || group == 4 || group == 8);
+  const bool shape = elem_bytes == 1 ? head_dim == 128
+                                     : (elem_bytes == 2 || elem_bytes == 4) && (head_dim == 64 || head_dim == 128);
+  return shape && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 template <int EB, int D, int G>
@@ -738,7 +810,9 @@ hipError_t launch_decode(const DecodeArgs& a, const CacheGeom& g, hipStream_t st
   p.num_blocks = g.num_blocks;
   p.num_partitions = a.num_partitions;
   p.partition_blocks = a.partition_blocks;
-  p.scale_log2 = a.scale * kLog2e;
+  // fp8 pools: the K scale multiplies every score, the V scale the output
+  p.scale_log2 = a.scale * g.k_scale * kLog2e;
+  p.v_scale = g.v_scale;
   const int G = a.num_q_heads / g.num_kv_heads;
 
 #define PA_DECODE_CASE(EB_, D_, G_) \
@@ -749,6 +823,7 @@ hipError_t launch_decode(const DecodeArgs& a, const CacheGeom& g, hipStream_t st
   PA_DECODE_GROUPS(2, 64)
   PA_DECODE_GROUPS(4, 128)
   PA_DECODE_GROUPS(4, 64)
+  PA_DECODE_GROUPS(1, 128)
 #undef PA_DECODE_GROUPS
 #undef PA_DECODE_CASE
   return hipErrorInvalidValue;

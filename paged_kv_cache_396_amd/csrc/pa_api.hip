@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <mutex>
 #include <string>
 
@@ -40,6 +41,7 @@ int hip_fail(hipError_t e, const char* what) {
 int elem_bytes_of(int32_t dtype) {
   if (dtype == PA_F32) return 4;
   if (dtype == PA_BF16) return 2;
+  if (dtype == PA_FP8_E4M3) return 1;
   return 0;
 }
 
@@ -60,11 +62,17 @@ int check_desc(const pa_cache_desc* d, pa::CacheGeom* g) {
   // offsets times 16; keep num_blocks * 16 below 2^31
   if ((int64_t)d->num_blocks * PA_BLOCK_SIZE >= (int64_t)1 << 31)
     return fail(PA_ERR_OVERFLOW, "num_blocks %d * 16 slots exceeds 2^31", (int)d->num_blocks);
+  if (eb == 1 && !(std::isfinite(d->k_scale) && d->k_scale > 0.f && std::isfinite(d->v_scale) &&
+                   d->v_scale > 0.f))
+    return fail(PA_ERR_SHAPE, "fp8 pools need finite positive k_scale / v_scale (%g, %g)",
+                (double)d->k_scale, (double)d->v_scale);
   if (g) {
     g->num_blocks = d->num_blocks;
     g->num_kv_heads = d->num_kv_heads;
     g->head_dim = d->head_dim;
     g->elem_bytes = eb;
+    g->k_scale = eb == 1 ? d->k_scale : 1.f;
+    g->v_scale = eb == 1 ? d->v_scale : 1.f;
   }
   return PA_OK;
 }
@@ -130,7 +138,7 @@ PA_API int pa_reshape_and_cache(const void* k, const void* v, const int64_t* slo
   if (num_tokens == 0) return ok();
   if (!k || !v || !slot_mapping || !k_cache || !v_cache)
     return fail(PA_ERR_NULL, "k, v, slot_mapping, k_cache and v_cache must be non-NULL");
-  if ((int64_t)num_tokens * g.num_kv_heads * g.head_dim * g.elem_bytes / 16 >= ((int64_t)1 << 40))
+  if ((int64_t)num_tokens * g.num_kv_heads * g.head_dim * 4 / 16 >= ((int64_t)1 << 40))
     return fail(PA_ERR_OVERFLOW, "too many tokens for one call");
   hipError_t e = pa::launch_cache_write(k, v, slot_mapping, num_tokens, k_cache, v_cache, g,
                                         (hipStream_t)stream);

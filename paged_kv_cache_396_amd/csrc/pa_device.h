@@ -39,6 +39,13 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 
 __device__ inline uint16_t to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
+// Two E4M3 codes (the low or the high 16 bits of w) widened to a bf16 pair;
+// exact, since every E4M3 value is a bf16 value (scale 1.0 leaves it as is).
+template <bool HI>
+__device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // a.lo*b.lo + a.hi*b.hi + c with bf16 inputs and fp32 accumulation.
 __device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),

@@ -13,7 +13,11 @@ struct CacheGeom {
   int num_blocks;
   int num_kv_heads;
   int head_dim;
-  int elem_bytes;  // 2 (bf16) or 4 (fp32)
+  int elem_bytes;  // of a pool element: 1 (fp8 E4M3), 2 (bf16) or 4 (fp32)
+  // fp8 pools only: code c of the K (V) pool stands for value(c) * k_scale
+  // (v_scale); q, out and the rows written are bf16
+  float k_scale;
+  float v_scale;
 };
 
 hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slots, int num_tokens,

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = pa.lib()
-    assert L.pa_abi_version() == 1
+    assert L.pa_abi_version() == 2
     assert L.pa_status_string(0) == b"ok"
     assert L.pa_status_string(-5) == b"workspace too small"
     assert L.pa_status_string(123) == b"unknown status"
@@ -49,6 +49,25 @@ def test_cache_bytes():
                 pa.CacheDesc(0, 16, 8, 128, 1), pa.CacheDesc(10, 16, 8, 128, 7),
                 pa.CacheDesc(1 << 28, 16, 1, 64, 1)):
         assert pa.pa_cache_bytes(bad) == 0
+
+
+def test_fp8_cache_bytes_and_scales():
+    d = pa.cache_desc(10, 8, 128, pa.PA_FP8_E4M3, 0.5, 0.25)
+    assert pa.pa_cache_bytes(d) == 10 * 8 * 16 * 128
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0), (1.0, float("nan"))):
+        assert pa.pa_cache_bytes(pa.cache_desc(10, 8, 128, pa.PA_FP8_E4M3, ks, vs)) == 0
+    # scales of bf16 / fp32 pools are ignored
+    assert pa.pa_cache_bytes(pa.cache_desc(10, 8, 128, pa.PA_BF16, 0.0, float("nan"))) > 0
+
+
+def test_fp8_unsupported_variants_and_bad_scales():
+    L = pa.lib()
+    p = ctypes.c_void_p(1)
+    bad_scale = pa.cache_desc(16, 2, 128, pa.PA_FP8_E4M3, 0.0, 1.0)
+    assert L.pa_reshape_and_cache(p, p, p, 4, p, p, ctypes.byref(bad_scale), None) == -2
+    assert b"k_scale" in L.pa_last_error()
+    assert _decode_raw(pa.cache_desc(16, 2, 64, pa.PA_FP8_E4M3, 1.0, 1.0)) == -4   # D = 64
+    assert _decode_raw(pa.cache_desc(16, 2, 128, pa.PA_FP8_E4M3, 1.0, 1.0), ws=None) == -5
 
 
 def _decode_raw(desc, num_seqs=2, num_q_heads=8, partition=64, max_ctx=100, mb=8,
