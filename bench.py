@@ -135,6 +135,10 @@ def bench_prefill(steps, warmup):
     from gpu_util import GpuPool, to_dev  # noqa: E402
 
     wl = make_prefill(5)
+    if args.fp8_only:
+        print(json.dumps({"fp8_kv_step": bench_fp8_decode(wl, args.steps, args.warmup)}), flush=True)
+        return
+
     pool = GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
     pool.write(wl.hist_k, wl.hist_v, wl.hist_slots)
     pool.write(wl.new_k, wl.new_v, wl.new_slots)
@@ -305,6 +309,73 @@ def bench_shared_prefix(wl, pool, q, bt, cl, max_ctx, steps, warmup):
     }
 
 
+def bench_fp8_decode(wl, steps, warmup):
+    """The decode step (cache write + pa_decode) of the same workload with
+    fp8 (E4M3) pools: the same bf16 K/V rows are quantized into the pools
+    with per-pool scales, and attention reads half the bytes."""
+    import torch
+
+    import paged_kv_cache_396_amd as pa
+    from gpu_util import to_dev
+    from workloads import FP8_K_SCALE, FP8_V_SCALE
+
+    dev = "cuda"
+    desc = pa.cache_desc(wl.num_blocks, wl.num_kv_heads, wl.head_dim, pa.PA_FP8_E4M3,
+                         float(FP8_K_SCALE), float(FP8_V_SCALE))
+    nbytes = pa.pa_cache_bytes(desc)
+    pk = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=dev)
+    pv = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=dev)
+    hs = torch.from_numpy(wl.hist_slots).to(dev)
+    pa.pa_reshape_and_cache(to_dev(wl.hist_k, "bf16"), to_dev(wl.hist_v, "bf16"), hs, pk, pv, desc)
+    new_k, new_v = to_dev(wl.new_k, "bf16"), to_dev(wl.new_v, "bf16")
+    new_slots = torch.from_numpy(wl.new_slots).to(dev)
+    q = to_dev(wl.q, "bf16")
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    S, Hq, D = wl.q.shape
+    max_ctx = int(wl.context_lens.max())
+    ws_bytes = pa.pa_decode_workspace_bytes(S, Hq, wl.num_kv_heads, D, max_ctx, 0)
+    ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def decode():
+        pa.pa_decode(out, q, pk, pv, bt, cl, max_ctx, float(wl.scale), desc, workspace=ws)
+
+    def step():
+        pa.pa_reshape_and_cache(new_k, new_v, new_slots, pk, pv, desc)
+        decode()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        pa.pa_reshape_and_cache(new_k, new_v, new_slots, pk, pv, desc)
+        e0.record(stream)
+        decode()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    dec = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+    kv = wl.kv_bytes // 2  # one byte per element instead of two
+    return {
+        "kv_dtype": "fp8_e4m3", "k_scale": float(FP8_K_SCALE), "v_scale": float(FP8_V_SCALE),
+        "ms_per_step": round(ms_step, 5), "tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": kv, "step_gbs": round(kv / (ms_step * 1e-3) / 1e9, 1),
+        "decode_call_median_ms": round(dec, 5),
+        "decode_call_gbs": round(kv / (dec * 1e-3) / 1e9, 1),
+        "decode_call_hbm_frac": round(kv / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def bench_block_pool(steps=10):
     """Copy-on-write machinery: pa_copy_blocks of 4096 block pairs of an
     8B-layer pool (8 kv heads, d 128, bf16: 64 KiB per pair in K and V), and
@@ -446,6 +517,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk timing")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only pa_prefill_chunk (for profiling it alone)")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="time only the decode step over fp8 pools (for profiling)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of the bench, run N plain 1 GiB device copies (counter calibration)")
@@ -487,6 +560,10 @@ def main():
     wl = make_decode(cfg)
     print(f"[bench] workload {args.workload}: {wl.num_seqs} seqs, ctx sum {int(wl.context_lens.sum())}, "
           f"generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    if args.fp8_only:
+        print(json.dumps({"fp8_kv_step": bench_fp8_decode(wl, args.steps, args.warmup)}), flush=True)
+        return
 
     pool = GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
     pool.write(wl.hist_k, wl.hist_v, wl.hist_slots)
@@ -620,6 +697,10 @@ def main():
         line["prefill_chunk"] = bench_prefill(min(args.steps, 20), min(args.warmup, 3))
         line["long_mixed_step"] = bench_mixed_concurrent()
         line["block_pool"] = bench_block_pool()
+        if wl.dtype == "bf16" and D == 128:
+            line["fp8_kv_step"] = bench_fp8_decode(wl, args.steps, args.warmup)
+            line["fp8_kv_step"]["speedup_vs_bf16_step"] = round(
+                ms_step / line["fp8_kv_step"]["ms_per_step"], 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -480,9 +480,12 @@ struct WaveDecoder {
 #ifndef PA_DECODE_OCC_BF16_G4
 #define PA_DECODE_OCC_BF16_G4 3
 #endif
+#ifndef PA_DECODE_OCC_FP8_G4
+#define PA_DECODE_OCC_FP8_G4 3
+#endif
 template <int EB, int D, int G>
 constexpr int decode_waves_per_eu() {
-  return (EB == 1) ? (G <= 4 ? 3 : 2)
+  return (EB == 1) ? (G <= 4 ? PA_DECODE_OCC_FP8_G4 : 2)
          : (EB == 2 && G <= 4) ? PA_DECODE_OCC_BF16_G4
          : (EB == 4 && D == 64 && G <= 2) ? 3 : (EB == 4 && D == 128 && G >= 4) ? 1 : 2;
 }
