@@ -299,6 +299,42 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
                      int32_t num_q_heads, float scale, const pa_cache_desc* desc, void* stream);
 
 /*
+ * pa_rejection_sample — the verification step of speculative decoding
+ * (plumephp.com vLLM deep dive, 4.1.1; vLLM: from PagedAttention to
+ * Speculative Decoding, 5.3-5.4).  A drafter proposed num_draft = k tokens per
+ * request; the target model scored the k + 1 positions in one pass (its
+ * attention: pa_prefill_chunk with k + 1 query rows per request).  Candidate
+ * x_i is kept with probability min(1, p_i(x_i) / q_i(x_i)); the first
+ * rejection ends the round with a token drawn from the normalised
+ * (p_i - q_i)_+; if all k are kept a bonus token is drawn from p_k.  The
+ * emitted tokens follow the target distribution exactly.
+ *
+ *   target_probs  device fp32 [num_reqs][k+1][vocab]: p_0 .. p_k
+ *   draft_probs   device fp32 [num_reqs][k][vocab]: q_0 .. q_{k-1}, or NULL
+ *                 when drafts carry no distribution (q_i one-hot at x_i)
+ *   draft_tokens  device int32 [num_reqs][k]; a token outside [0, vocab) is
+ *                 never kept
+ *   uniforms      device fp32 [num_reqs][k+1], in [0, 1): u_i decides
+ *                 candidate i (kept iff u_i * q_i(x_i) <= p_i(x_i), exactly),
+ *                 u_k draws the final token.  u_i = 1 gives the deterministic
+ *                 rule "keep iff p(x) >= q(x)".
+ *   out_tokens    device int32 [num_reqs][k+1]: the kept drafts, then the
+ *                 drawn token, then -1 padding
+ *   num_out       device int32 [num_reqs]: tokens emitted (kept + 1)
+ * The final token is drawn by inverse CDF with u_k over integer weights
+ * floor(max(r_j, 0) * 2^32), r_j = p_j - q_j in fp32 (NaN counts as 0), so the
+ * choice is exact and independent of summation order; an empty residual draws
+ * from p_i instead, and an all-zero p_k gives token -1.  Probabilities need
+ * not be normalised.  Supported: k <= 32, vocab <= 2^21.
+ */
+#define PA_MAX_DRAFT 32
+#define PA_MAX_VOCAB (1 << 21)
+int pa_rejection_sample(const float* target_probs, const float* draft_probs,
+                        const int32_t* draft_tokens, const float* uniforms, int32_t num_reqs,
+                        int32_t num_draft, int32_t vocab, int32_t* out_tokens, int32_t* num_out,
+                        void* stream);
+
+/*
  * pa_bw_probe — measurement helper, not part of attention: reads num_tiles
  * 4 KiB tiles of `buf` once each, tile tile_order[i] for i = 0..num_tiles-1,
  * with the same non-temporal 16-byte loads the decode kernel uses for K/V

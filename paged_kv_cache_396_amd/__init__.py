@@ -1,5 +1,7 @@
-"""MI355X (gfx950) paged KV-cache attention: cache writes, paged decode with
-split-K, and chunked prefill, as hand-written HIP kernels behind a C ABI
+"""MI355X (gfx950) paged KV-cache attention: cache writes (bf16, fp32 and
+fp8 E4M3 pools), paged decode with split-K, shared-prefix decode, chunked
+prefill, block copies, a host block pool and speculative-decoding
+verification, as hand-written HIP kernels behind a C ABI
 (``include/pa.h``).  This package holds the kernels' sources (``csrc/``), the
 build step and a ctypes binding; torch supplies device memory and streams."""
 
@@ -23,5 +25,6 @@ from .binding import (  # noqa: F401
     pa_decode_shared_prefix_workspace_bytes,
     pa_decode_workspace_bytes,
     pa_prefill_chunk,
+    pa_rejection_sample,
     pa_reshape_and_cache,
 )

@@ -105,6 +105,8 @@ def lib():
         L.pa_pool_num_tokens.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [P, P, P, i32, D, P]
         L.pa_copy_blocks.restype = ctypes.c_int
+        L.pa_rejection_sample.argtypes = [P, P, P, P, i32, i32, i32, P, P, P]
+        L.pa_rejection_sample.restype = ctypes.c_int
         L.pa_bw_probe.argtypes = [P, sz, P, i32, P, P]
         L.pa_bw_probe.restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
@@ -345,3 +347,27 @@ def pa_copy_blocks(k_cache, v_cache, pairs, desc: CacheDesc, stream=None):
         raise ValueError("pairs must be int32 [n, 2]")
     _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0],
                                 ctypes.byref(desc), _stream(stream)))
+
+
+def pa_rejection_sample(target_probs, draft_probs, draft_tokens, uniforms, out_tokens, num_out,
+                        stream=None):
+    """Speculative-decoding verification: target_probs fp32 [B, k+1, V],
+    draft_probs fp32 [B, k, V] or None (one-hot drafts), draft_tokens int32
+    [B, k], uniforms fp32 [B, k+1]; writes out_tokens int32 [B, k+1] and
+    num_out int32 [B]."""
+    torch = _torch()
+    B, k1, V = target_probs.shape
+    checks = [(target_probs, "target_probs", torch.float32, (B, k1, V)),
+              (draft_tokens, "draft_tokens", torch.int32, (B, k1 - 1)),
+              (uniforms, "uniforms", torch.float32, (B, k1)),
+              (out_tokens, "out_tokens", torch.int32, (B, k1)),
+              (num_out, "num_out", torch.int32, (B,))]
+    if draft_probs is not None:
+        checks.append((draft_probs, "draft_probs", torch.float32, (B, k1 - 1, V)))
+    for t, n, dt, shape in checks:
+        _dev(t, n)
+        if t.dtype != dt or tuple(t.shape) != shape:
+            raise ValueError(f"{n} must be {dt} {shape}, got {t.dtype} {tuple(t.shape)}")
+    _check(lib().pa_rejection_sample(_ptr(target_probs), _ptr(draft_probs), _ptr(draft_tokens),
+                                     _ptr(uniforms), B, k1 - 1, V, _ptr(out_tokens), _ptr(num_out),
+                                     _stream(stream)))

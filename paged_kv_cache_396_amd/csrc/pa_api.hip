@@ -404,6 +404,37 @@ PA_API int pa_bw_probe(const void* buf, size_t bytes, const int32_t* tile_order,
   return ok();
 }
 
+PA_API int pa_rejection_sample(const float* target_probs, const float* draft_probs,
+                               const int32_t* draft_tokens, const float* uniforms,
+                               int32_t num_reqs, int32_t num_draft, int32_t vocab,
+                               int32_t* out_tokens, int32_t* num_out, void* stream) {
+  if (num_reqs < 0 || num_draft < 0 || vocab < 1)
+    return fail(PA_ERR_SHAPE, "num_reqs %d, num_draft %d, vocab %d", (int)num_reqs, (int)num_draft,
+                (int)vocab);
+  if (num_draft > PA_MAX_DRAFT)
+    return fail(PA_ERR_UNSUPPORTED, "num_draft %d (at most %d)", (int)num_draft, PA_MAX_DRAFT);
+  if (vocab > PA_MAX_VOCAB)
+    return fail(PA_ERR_UNSUPPORTED, "vocab %d (at most %d)", (int)vocab, PA_MAX_VOCAB);
+  if ((int64_t)num_reqs * (num_draft + 1) * vocab >= ((int64_t)1 << 40))
+    return fail(PA_ERR_OVERFLOW, "probability arrays too large");
+  if (num_reqs == 0) return ok();
+  if (!target_probs || !uniforms || !out_tokens || !num_out || (num_draft > 0 && !draft_tokens))
+    return fail(PA_ERR_NULL, "target_probs, draft_tokens, uniforms, out_tokens and num_out must be non-NULL");
+  pa::SpecVerifyArgs a;
+  a.target_probs = target_probs;
+  a.draft_probs = draft_probs;
+  a.draft_tokens = draft_tokens;
+  a.uniforms = uniforms;
+  a.out_tokens = out_tokens;
+  a.num_out = num_out;
+  a.num_reqs = num_reqs;
+  a.k = num_draft;
+  a.vocab = vocab;
+  hipError_t e = pa::launch_spec_verify(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rejection sampling launch");
+  return ok();
+}
+
 // ---- block pool (host only)
 
 struct pa_block_pool {

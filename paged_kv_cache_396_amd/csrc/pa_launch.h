@@ -98,6 +98,21 @@ hipError_t launch_decode_own_and_merge(const SharedPrefixArgs& a, const CacheGeo
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               const CacheGeom& g, hipStream_t stream);
 
+// Rejection sampling of drafted tokens (speculative decoding).
+struct SpecVerifyArgs {
+  const float* target_probs;   // [num_reqs][k+1][vocab]
+  const float* draft_probs;    // [num_reqs][k][vocab] or null
+  const int32_t* draft_tokens; // [num_reqs][k]
+  const float* uniforms;       // [num_reqs][k+1]
+  int32_t* out_tokens;         // [num_reqs][k+1]
+  int32_t* num_out;            // [num_reqs]
+  int num_reqs;
+  int k;
+  int vocab;
+};
+
+hipError_t launch_spec_verify(const SpecVerifyArgs& a, hipStream_t stream);
+
 // Streaming-read probe over 4 KiB tiles in the given order.
 hipError_t launch_bw_probe(const void* buf, size_t bytes, const int32_t* order, int ntiles,
                            uint32_t* sink, hipStream_t stream);

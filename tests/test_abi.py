@@ -179,3 +179,21 @@ def test_shared_prefix_workspace_size():
     slots = (n // 4) // (128 + 2)
     assert slots >= 2                             # at least one prefix and one own slot
     assert n == 4 * (((2 * rows * (slots // rows) + 3) // 4) * 4 + rows * (slots // rows) * 128)
+
+
+def test_rejection_sample_argument_errors():
+    L = pa.lib()
+    p = ctypes.c_void_p(1)
+    n = ctypes.c_void_p(0)
+
+    def call(B=2, k=4, V=100, tp=p, dt=p, u=p, out=p, num=p):
+        return L.pa_rejection_sample(tp, n, dt, u, B, k, V, out, num, None)
+
+    assert call(B=-1) == -2
+    assert call(V=0) == -2
+    assert call(k=33) == -4                       # more drafts than built
+    assert call(V=(1 << 21) + 1) == -4            # vocabulary too large
+    assert call(tp=n) == -1
+    assert call(dt=n) == -1                       # k > 0 needs draft tokens
+    assert call(u=n, B=0) == 0                    # nothing to do
+    assert call(B=1 << 20, k=32, V=1 << 21) == -6  # index range

@@ -1,0 +1,176 @@
+"""Speculative-decoding verification on the GPU against the oracle.
+
+The sampler's outputs are integers decided exactly on both sides, so they are
+compared bit for bit: every emitted token and every count.  The verification
+attention (k + 1 query rows per request through pa_prefill_chunk) is compared
+at the bf16 tolerance |gpu - ref| <= 2e-2 + 2e-2 |ref|.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.spec_decode as sd
+import paged_kv_cache_396_amd as pa
+from workloads import make_spec_verify
+
+from gpu_util import assert_close, gpu_pool_for, gpu_prefill, log, oracle_pools, to_f64, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_sample(target, draft, tokens, uniforms):
+    t = torch()
+    B, k1, V = target.shape
+    tp = t.from_numpy(np.ascontiguousarray(target, dtype=np.float32)).cuda()
+    dp = None if draft is None else t.from_numpy(np.ascontiguousarray(draft, dtype=np.float32)).cuda()
+    tk = t.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, k1 - 1)).cuda()
+    u = t.from_numpy(np.ascontiguousarray(uniforms, dtype=np.float32)).cuda()
+    out = t.full((B, k1), -7, dtype=t.int32, device="cuda")
+    n = t.full((B,), -7, dtype=t.int32, device="cuda")
+    pa.pa_rejection_sample(tp, dp, tk, u, out, n)
+    t.cuda.synchronize()
+    return out.cpu().numpy(), n.cpu().numpy()
+
+
+def check(target, draft, tokens, uniforms, what=""):
+    got_t, got_n = gpu_sample(target, draft, tokens, uniforms)
+    want_t, want_n = sd.rejection_sample(target, draft, np.asarray(tokens, dtype=np.int32).reshape(
+        target.shape[0], target.shape[1] - 1), uniforms)
+    bad = np.flatnonzero((got_t != want_t).any(axis=1) | (got_n != want_n))
+    assert bad.size == 0, (f"{what}: {bad.size} requests differ; first {bad[0]}: gpu "
+                           f"{got_t[bad[0]].tolist()} ({got_n[bad[0]]}) oracle "
+                           f"{want_t[bad[0]].tolist()} ({want_n[bad[0]]})")
+    return want_n
+
+
+def rand_probs(rng, shape, std=2.0):
+    z = rng.standard_normal(shape) * std
+    z -= z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def rand_case(rng, B, k, V, noise=0.7, with_draft=True):
+    p = rand_probs(rng, (B, k + 1, V))
+    q = None
+    if with_draft:
+        q = np.clip(p[:, :k] * np.exp(rng.standard_normal((B, k, V)) * noise), 0, None)
+        q = (q / q.sum(axis=-1, keepdims=True)).astype(np.float32)
+    src = q if q is not None else p[:, :k]
+    toks = np.zeros((B, k), dtype=np.int32)
+    for b in range(B):
+        for i in range(k):
+            toks[b, i] = min(int(np.searchsorted(np.cumsum(src[b, i]), rng.random())), V - 1)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    return p, q, toks, u
+
+
+# ----------------------------------------------------------------------------
+# the sampler
+
+
+@pytest.mark.parametrize("V", [1, 2, 7, 255, 256, 257, 1000, 4099, 32000])
+@pytest.mark.parametrize("k", [1, 4, 8])
+@pytest.mark.parametrize("with_draft", [True, False])
+def test_rejection_sample_matches_oracle(V, k, with_draft):
+    log(f"rejection sample V={V} k={k} draft={with_draft}")
+    rng = np.random.default_rng(V * 31 + k + with_draft)
+    p, q, toks, u = rand_case(rng, 48, k, V, with_draft=with_draft)
+    n = check(p, q, toks, u, f"V={V} k={k}")
+    if V > 2:
+        assert n.min() >= 1 and n.max() <= k + 1
+
+
+def test_rejection_sample_llama3_vocab_batch64():
+    """The verification round of the 64-sequence 8B decode batch: Llama-3
+    vocabulary (128256 entries), 4 drafts, draft and target distributions."""
+    log("rejection sample 64 x 128256 x k=4")
+    wl = make_spec_verify()
+    n = check(wl.target_probs, wl.draft_probs, wl.draft_tokens, wl.uniforms, "llama3 vocab")
+    log(f"  mean tokens per round {n.mean():.3f}")
+
+
+def test_rejection_sample_edge_cases():
+    log("rejection sample edge cases")
+    rng = np.random.default_rng(17)
+    B, k, V = 12, 4, 600
+    p, q, toks, u = rand_case(rng, B, k, V)
+    u[0] = 0.0                           # everything accepted: bonus from p_k
+    u[1] = 1.0                           # deterministic rule, last draw at the top end
+    u[2, :k] = np.float32(1e-30)         # tiny uniforms
+    toks[3, 1] = V                       # out-of-range drafts are rejected
+    toks[4, 0] = -5
+    p[5, 0] = q[5, 0]                    # identical rows: residual empty unless rejected ...
+    u[5, 0] = 1.0                        # ... which u = 1 never does (p == q keeps x)
+    q[6, 0] = np.float32(0)              # q(x) = 0 keeps x (0 <= p)
+    p[7, :, 100:] = 0                    # sparse target rows
+    p[8, 2, 17] = np.nan                 # NaN weights count as zero
+    p[9] *= np.float32(3.0)              # unnormalised rows
+    p[10, k] = 0                         # all-zero p_k: a bonus draw gives -1
+    u[10, :k] = 0.0
+    q[11, 1] = np.float32(1.0) / V       # flat draft row
+    check(p, q, toks, u, "edge cases")
+
+
+def test_zero_residual_falls_back_to_target():
+    log("rejection sample empty residual")
+    V = 300
+    p = np.full((2, 2, V), 1.0 / V, dtype=np.float32)
+    q = np.full((2, 1, V), 1.0 / V, dtype=np.float32)
+    q[:, 0, 5] = np.float32(1.0)         # out of contract: q(x) > p(x) and q >= p everywhere
+    toks = np.array([[5], [5]], dtype=np.int32)
+    u = np.array([[0.9, 0.25], [0.5, 0.999]], dtype=np.float32)
+    check(p, q, toks, u, "empty residual")
+
+
+def test_k_zero_samples_the_target():
+    log("rejection sample k = 0")
+    rng = np.random.default_rng(3)
+    p = rand_probs(rng, (32, 1, 5000))
+    u = rng.random((32, 1), dtype=np.float32)
+    check(p, None, np.zeros((32, 0), dtype=np.int32), u, "k = 0")
+
+
+def test_repeated_calls_are_deterministic():
+    log("rejection sample repeat")
+    rng = np.random.default_rng(4)
+    p, q, toks, u = rand_case(rng, 64, 6, 20000)
+    a = gpu_sample(p, q, toks, u)
+    b = gpu_sample(p, q, toks, u)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------
+# verification attention: k + 1 query rows per request
+
+
+@pytest.mark.parametrize("k", [1, 4, 8])
+def test_verification_attention_batch64(k):
+    """The target model's attention over the k + 1 appended positions of the
+    64-sequence 8B batch (contexts U[128, 4096)), through pa_prefill_chunk;
+    12 sampled requests checked against the oracle, all rows finite."""
+    log(f"verification attention k={k}")
+    wl = make_spec_verify(k=k, vocab=8).attn
+    out = to_f64(gpu_prefill(wl, gpu_pool_for(wl)))
+    assert np.isfinite(out).all()
+    reqs = list(range(0, 64, 6))
+    rows = [r for q in reqs for r in range(int(wl.query_start_loc[q]), int(wl.query_start_loc[q + 1]))]
+    pk, pv = oracle_pools(wl, oracle)
+    ref = oracle.prefill_chunk(wl.q, pk, pv, wl.block_tables, wl.query_start_loc, wl.context_lens,
+                               wl.scale, wl.dtype, rows=rows)
+    err = assert_close(out[rows], ref[rows], "bf16", f"k={k}")
+    log(f"  max abs err {err:.3g}")
+
+
+def test_verification_last_row_equals_decode():
+    """The last of the k + 1 rows sees the whole context: it matches the
+    oracle's decode attention of the same sequences."""
+    log("verification last row vs decode")
+    wl = make_spec_verify(batch=16, k=4, vocab=8).attn
+    pool = gpu_pool_for(wl)
+    out = to_f64(gpu_prefill(wl, pool))
+    last = wl.query_start_loc[1:] - 1
+    pk, pv = oracle_pools(wl, oracle)
+    dec = oracle.decode(wl.q[last], pk, pv, wl.block_tables, wl.context_lens, wl.scale, wl.dtype)
+    assert_close(out[last], dec, "bf16", "last rows")

@@ -14,10 +14,12 @@ from .configs import (  # noqa: F401
     FP8_V_SCALE,
     DecodeWorkload,
     PrefillWorkload,
+    SpecVerifyWorkload,
     bf16_bits_from_f32,
     make_decode,
     make_mixed,
     make_prefill,
+    make_spec_verify,
     make_tiny_decode,
     make_tiny_prefill,
     make_tiny_shared,

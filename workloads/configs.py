@@ -439,3 +439,54 @@ def make_tiny_shared(seed=21, n_prompts=2, samples=3, prompt_len=32, tails=(1, 5
     wl.extra["prompt_of"] = prompt_of
     wl.extra["prompt_len"] = prompt_len
     return wl
+
+
+@dataclass
+class SpecVerifyWorkload:
+    """One verification round of speculative decoding over a decode batch.
+
+    Every sequence has its last token and k drafted tokens appended: their
+    K/V go into the pool and the target's attention runs those k + 1
+    positions as a prefill chunk (``attn``).  The sampler's inputs are fp32
+    target distributions p [B, k+1, V], draft distributions q [B, k, V], the
+    drafted tokens (drawn from q) and uniforms in [0, 1) [B, k+1].
+    """
+
+    attn: PrefillWorkload
+    target_probs: np.ndarray
+    draft_probs: np.ndarray
+    draft_tokens: np.ndarray
+    uniforms: np.ndarray
+
+
+def _softmax32(logits: np.ndarray) -> np.ndarray:
+    z = logits.astype(np.float64)
+    z -= z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def make_spec_verify(batch=64, k=4, vocab=128256, Hq=32, Hkv=8, D=128, seed=396_400,
+                     ctx_lo=128, ctx_hi=4096, logit_std=2.5, draft_noise=0.8):
+    """A verification round on the Llama-3.1-8B-shaped decode batch: context
+    before the round U[ctx_lo, ctx_hi) tokens, k drafts per sequence, the
+    Llama-3 vocabulary size by default.  Target logits are N(0, logit_std);
+    draft logits add N(0, draft_noise) to them, so drafts are accepted often
+    but not always."""
+    rng = np.random.default_rng(seed)
+    prior = rng.integers(ctx_lo, ctx_hi, size=batch).tolist()
+    chunk = [k + 1] * batch
+    mb = max((p + k + 1 + BLOCK_SIZE - 1) // BLOCK_SIZE for p in prior)
+    attn = _build_prefill("spec_verify", "bf16", prior, chunk, Hq, Hkv, D, mb, seed,
+                          np.random.default_rng(seed + 1))
+    lp = rng.standard_normal((batch, k + 1, vocab), dtype=np.float32) * np.float32(logit_std)
+    target = _softmax32(lp)
+    lq = lp[:, :k] + rng.standard_normal((batch, k, vocab), dtype=np.float32) * np.float32(draft_noise)
+    draft = _softmax32(lq)
+    toks = np.zeros((batch, k), dtype=np.int32)
+    for b in range(batch):
+        for i in range(k):
+            c = np.cumsum(draft[b, i].astype(np.float64))
+            toks[b, i] = min(int(np.searchsorted(c, rng.random() * c[-1], side="right")), vocab - 1)
+    u = rng.random((batch, k + 1), dtype=np.float32)
+    return SpecVerifyWorkload(attn, target, draft, toks, u)
