@@ -40,6 +40,7 @@ Everything is plain Python / NumPy with exact integer arithmetic.
 
 from __future__ import annotations
 
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -63,9 +64,12 @@ def weights(r32: np.ndarray) -> np.ndarray:
 
 
 def threshold(u, total: int) -> int:
-    """T = min(floor(u * total), total - 1) with u an fp32 value, exact."""
-    t = int(Fraction(float(np.float32(u))) * total)  # int() of a non-negative Fraction floors
-    return min(t, total - 1)
+    """T = floor(u * total) for an fp32 u, exact, kept inside [0, total - 1]
+    (u <= 0 or NaN gives 0, u >= 1 gives total - 1)."""
+    uf = float(np.float32(u))
+    if not uf > 0:
+        return 0
+    return min(math.floor(Fraction(uf) * total), total - 1)
 
 
 def sample_index(w: np.ndarray, u) -> int:
