@@ -135,10 +135,6 @@ def bench_prefill(steps, warmup):
     from gpu_util import GpuPool, to_dev  # noqa: E402
 
     wl = make_prefill(5)
-    if args.fp8_only:
-        print(json.dumps({"fp8_kv_step": bench_fp8_decode(wl, args.steps, args.warmup)}), flush=True)
-        return
-
     pool = GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
     pool.write(wl.hist_k, wl.hist_v, wl.hist_slots)
     pool.write(wl.new_k, wl.new_v, wl.new_slots)
@@ -376,6 +372,96 @@ def bench_fp8_decode(wl, steps, warmup):
     }
 
 
+def bench_spec_verify(steps, warmup):
+    """One verification round of speculative decoding on the 64-sequence 8B
+    batch (contexts U[128, 4096), k = 4 drafts, Llama-3 vocabulary of 128256):
+    write the k + 1 new tokens' K/V, the target's attention over those k + 1
+    rows (pa_prefill_chunk), and rejection sampling (pa_rejection_sample)."""
+    import torch
+
+    import paged_kv_cache_396_amd as pa
+    from gpu_util import GpuPool, to_dev
+    from workloads import make_spec_verify
+
+    dev = "cuda"
+    w = make_spec_verify()
+    a = w.attn
+    pool = GpuPool(a.num_blocks, a.num_kv_heads, a.head_dim, a.dtype)
+    pool.write(a.hist_k, a.hist_v, a.hist_slots)
+    nk, nv = to_dev(a.new_k, a.dtype), to_dev(a.new_v, a.dtype)
+    ns = torch.from_numpy(a.new_slots).to(dev)
+    q = to_dev(a.q, a.dtype)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(a.block_tables).to(dev)
+    qsl = torch.from_numpy(a.query_start_loc).to(dev)
+    cl = torch.from_numpy(a.context_lens).to(dev)
+    k1 = int(w.target_probs.shape[1])
+    tp = torch.from_numpy(w.target_probs).to(dev)
+    dp = torch.from_numpy(w.draft_probs).to(dev)
+    tk = torch.from_numpy(w.draft_tokens).to(dev)
+    uu = torch.from_numpy(w.uniforms).to(dev)
+    sws = torch.empty(pa.pa_rejection_sample_workspace_bytes(a.num_reqs, int(w.target_probs.shape[2])),
+                      dtype=torch.uint8, device=dev)
+    ot = torch.empty((a.num_reqs, k1), dtype=torch.int32, device=dev)
+    on = torch.empty((a.num_reqs,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def write():
+        pa.pa_reshape_and_cache(nk, nv, ns, pool.k, pool.v, pool.desc)
+
+    def attend():
+        pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, k1, float(a.scale), pool.desc)
+
+    def sample():
+        pa.pa_rejection_sample(tp, dp, tk, uu, ot, on, workspace=sws)
+
+    def step():
+        write()
+        attend()
+        sample()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+
+    def per_call(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for x, y in evs:
+            x.record(stream)
+            fn()
+            y.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([x.elapsed_time(y) for x, y in evs]))
+
+    attn_ms = per_call(attend)
+    samp_ms = per_call(sample)
+    n = on.cpu().numpy()
+    V = int(w.target_probs.shape[2])
+    # rows the sampler streams: p_i and q_i after a rejection at i, p_k after k acceptances
+    samp_bytes = int(sum(V * 4 * (1 if int(c) == k1 else 2) for c in n))
+    kv = int(a.context_lens.astype(np.int64).sum()) * 2 * a.num_kv_heads * a.head_dim * 2
+    return {
+        "batch": a.num_reqs, "k": k1 - 1, "vocab": V,
+        "ms_per_round": round(ms_step, 5),
+        "tokens_per_round_mean": round(float(n.mean()), 4),
+        "tokens_per_s": round(float(n.sum()) / (ms_step * 1e-3), 1),
+        "verify_attention_ms": round(attn_ms, 5),
+        "verify_attention_kv_gbs": round(kv / (attn_ms * 1e-3) / 1e9, 1),
+        "verify_attention_hbm_frac": round(kv / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "rejection_sample_ms": round(samp_ms, 5),
+        "rejection_sample_bytes": samp_bytes,
+        "rejection_sample_gbs": round(samp_bytes / (samp_ms * 1e-3) / 1e9, 1),
+    }
+
+
 def bench_block_pool(steps=10):
     """Copy-on-write machinery: pa_copy_blocks of 4096 block pairs of an
     8B-layer pool (8 kv heads, d 128, bf16: 64 KiB per pair in K and V), and
@@ -519,6 +605,8 @@ def main():
                     help="time only pa_prefill_chunk (for profiling it alone)")
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the decode step over fp8 pools (for profiling)")
+    ap.add_argument("--spec-only", action="store_true",
+                    help="time only the speculative-decoding verification round (for profiling)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of the bench, run N plain 1 GiB device copies (counter calibration)")
@@ -561,6 +649,9 @@ def main():
     print(f"[bench] workload {args.workload}: {wl.num_seqs} seqs, ctx sum {int(wl.context_lens.sum())}, "
           f"generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
+    if args.spec_only:
+        print(json.dumps({"spec_verify_round": bench_spec_verify(args.steps, args.warmup)}), flush=True)
+        return
     if args.fp8_only:
         print(json.dumps({"fp8_kv_step": bench_fp8_decode(wl, args.steps, args.warmup)}), flush=True)
         return
@@ -697,6 +788,7 @@ def main():
         line["prefill_chunk"] = bench_prefill(min(args.steps, 20), min(args.warmup, 3))
         line["long_mixed_step"] = bench_mixed_concurrent()
         line["block_pool"] = bench_block_pool()
+        line["spec_verify_round"] = bench_spec_verify(min(args.steps, 20), min(args.warmup, 3))
         if wl.dtype == "bf16" and D == 128:
             line["fp8_kv_step"] = bench_fp8_decode(wl, args.steps, args.warmup)
             line["fp8_kv_step"]["speedup_vs_bf16_step"] = round(

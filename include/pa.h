@@ -321,18 +321,23 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
  *   out_tokens    device int32 [num_reqs][k+1]: the kept drafts, then the
  *                 drawn token, then -1 padding
  *   num_out       device int32 [num_reqs]: tokens emitted (kept + 1)
+ *   workspace     device scratch of pa_rejection_sample_workspace_bytes(
+ *                 num_reqs, vocab) bytes (one 64-bit weight sum per request
+ *                 and 256-entry vocabulary segment); needs no initialisation;
+ *                 two calls in flight at the same time must not share it
  * The final token is drawn by inverse CDF with u_k over integer weights
  * floor(max(r_j, 0) * 2^32), r_j = p_j - q_j in fp32 (NaN counts as 0), so the
  * choice is exact and independent of summation order; an empty residual draws
  * from p_i instead, and an all-zero p_k gives token -1.  Probabilities need
- * not be normalised.  Supported: k <= 32, vocab <= 2^21.
+ * not be normalised.  Supported: k <= 32, vocab <= 2^21, num_reqs <= 65535.
  */
 #define PA_MAX_DRAFT 32
 #define PA_MAX_VOCAB (1 << 21)
+size_t pa_rejection_sample_workspace_bytes(int32_t num_reqs, int32_t vocab);
 int pa_rejection_sample(const float* target_probs, const float* draft_probs,
                         const int32_t* draft_tokens, const float* uniforms, int32_t num_reqs,
                         int32_t num_draft, int32_t vocab, int32_t* out_tokens, int32_t* num_out,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_bw_probe — measurement helper, not part of attention: reads num_tiles

@@ -26,5 +26,6 @@ from .binding import (  # noqa: F401
     pa_decode_workspace_bytes,
     pa_prefill_chunk,
     pa_rejection_sample,
+    pa_rejection_sample_workspace_bytes,
     pa_reshape_and_cache,
 )

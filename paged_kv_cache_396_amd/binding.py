@@ -105,7 +105,9 @@ def lib():
         L.pa_pool_num_tokens.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [P, P, P, i32, D, P]
         L.pa_copy_blocks.restype = ctypes.c_int
-        L.pa_rejection_sample.argtypes = [P, P, P, P, i32, i32, i32, P, P, P]
+        L.pa_rejection_sample_workspace_bytes.argtypes = [i32, i32]
+        L.pa_rejection_sample_workspace_bytes.restype = sz
+        L.pa_rejection_sample.argtypes = [P, P, P, P, i32, i32, i32, P, P, P, sz, P]
         L.pa_rejection_sample.restype = ctypes.c_int
         L.pa_bw_probe.argtypes = [P, sz, P, i32, P, P]
         L.pa_bw_probe.restype = ctypes.c_int
@@ -349,14 +351,24 @@ def pa_copy_blocks(k_cache, v_cache, pairs, desc: CacheDesc, stream=None):
                                 ctypes.byref(desc), _stream(stream)))
 
 
+def pa_rejection_sample_workspace_bytes(num_reqs: int, vocab: int) -> int:
+    return int(lib().pa_rejection_sample_workspace_bytes(num_reqs, vocab))
+
+
 def pa_rejection_sample(target_probs, draft_probs, draft_tokens, uniforms, out_tokens, num_out,
-                        stream=None):
+                        workspace=None, stream=None):
     """Speculative-decoding verification: target_probs fp32 [B, k+1, V],
     draft_probs fp32 [B, k, V] or None (one-hot drafts), draft_tokens int32
     [B, k], uniforms fp32 [B, k+1]; writes out_tokens int32 [B, k+1] and
-    num_out int32 [B]."""
+    num_out int32 [B].  ``workspace`` (device, at least
+    pa_rejection_sample_workspace_bytes(B, V) bytes) is allocated per call
+    when omitted."""
     torch = _torch()
     B, k1, V = target_probs.shape
+    if workspace is None:
+        workspace = torch.empty(max(1, pa_rejection_sample_workspace_bytes(B, V)), dtype=torch.uint8,
+                                device=target_probs.device)
+    _dev(workspace, "workspace")
     checks = [(target_probs, "target_probs", torch.float32, (B, k1, V)),
               (draft_tokens, "draft_tokens", torch.int32, (B, k1 - 1)),
               (uniforms, "uniforms", torch.float32, (B, k1)),
@@ -370,4 +382,5 @@ def pa_rejection_sample(target_probs, draft_probs, draft_tokens, uniforms, out_t
             raise ValueError(f"{n} must be {dt} {shape}, got {t.dtype} {tuple(t.shape)}")
     _check(lib().pa_rejection_sample(_ptr(target_probs), _ptr(draft_probs), _ptr(draft_tokens),
                                      _ptr(uniforms), B, k1 - 1, V, _ptr(out_tokens), _ptr(num_out),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))

@@ -404,10 +404,16 @@ PA_API int pa_bw_probe(const void* buf, size_t bytes, const int32_t* tile_order,
   return ok();
 }
 
+PA_API size_t pa_rejection_sample_workspace_bytes(int32_t num_reqs, int32_t vocab) {
+  if (num_reqs <= 0 || vocab < 1 || vocab > PA_MAX_VOCAB) return 0;
+  return pa::spec_verify_workspace_bytes(num_reqs, vocab);
+}
+
 PA_API int pa_rejection_sample(const float* target_probs, const float* draft_probs,
                                const int32_t* draft_tokens, const float* uniforms,
                                int32_t num_reqs, int32_t num_draft, int32_t vocab,
-                               int32_t* out_tokens, int32_t* num_out, void* stream) {
+                               int32_t* out_tokens, int32_t* num_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (num_reqs < 0 || num_draft < 0 || vocab < 1)
     return fail(PA_ERR_SHAPE, "num_reqs %d, num_draft %d, vocab %d", (int)num_reqs, (int)num_draft,
                 (int)vocab);
@@ -417,9 +423,14 @@ PA_API int pa_rejection_sample(const float* target_probs, const float* draft_pro
     return fail(PA_ERR_UNSUPPORTED, "vocab %d (at most %d)", (int)vocab, PA_MAX_VOCAB);
   if ((int64_t)num_reqs * (num_draft + 1) * vocab >= ((int64_t)1 << 40))
     return fail(PA_ERR_OVERFLOW, "probability arrays too large");
+  if (num_reqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_reqs %d (at most 65535)", (int)num_reqs);
   if (num_reqs == 0) return ok();
   if (!target_probs || !uniforms || !out_tokens || !num_out || (num_draft > 0 && !draft_tokens))
     return fail(PA_ERR_NULL, "target_probs, draft_tokens, uniforms, out_tokens and num_out must be non-NULL");
+  const size_t need = pa::spec_verify_workspace_bytes(num_reqs, vocab);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given (ptr %p)", need,
+                workspace_bytes, workspace);
   pa::SpecVerifyArgs a;
   a.target_probs = target_probs;
   a.draft_probs = draft_probs;
@@ -427,6 +438,7 @@ PA_API int pa_rejection_sample(const float* target_probs, const float* draft_pro
   a.uniforms = uniforms;
   a.out_tokens = out_tokens;
   a.num_out = num_out;
+  a.workspace = workspace;
   a.num_reqs = num_reqs;
   a.k = num_draft;
   a.vocab = vocab;

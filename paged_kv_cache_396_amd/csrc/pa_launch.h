@@ -106,11 +106,13 @@ struct SpecVerifyArgs {
   const float* uniforms;       // [num_reqs][k+1]
   int32_t* out_tokens;         // [num_reqs][k+1]
   int32_t* num_out;            // [num_reqs]
+  void* workspace;             // spec_verify_workspace_bytes(num_reqs, vocab) bytes
   int num_reqs;
   int k;
   int vocab;
 };
 
+size_t spec_verify_workspace_bytes(int num_reqs, int vocab);
 hipError_t launch_spec_verify(const SpecVerifyArgs& a, hipStream_t stream);
 
 // Streaming-read probe over 4 KiB tiles in the given order.

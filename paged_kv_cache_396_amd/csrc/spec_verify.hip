@@ -19,10 +19,13 @@
 //    T held below W; integer sums do not depend on the order of summation.
 //    An empty residual (W = 0) draws from p_i instead.
 //
-// One workgroup per request.  The vocabulary is cut into 256-entry segments:
-// a first pass sums each segment's weights (one wave per segment, 4 entries
-// per lane), a scan over the segment sums finds the segment holding T, and
-// one wave re-reads that segment alone to find the token.
+// Two kernels.  The vocabulary is cut into 256-entry segments.  The first
+// kernel spreads every request's segments over many workgroups (16 segments
+// each, so a batch fills the chip) and stores each segment's weight sum in
+// the caller's workspace.  The second takes one workgroup per request: it
+// scans the segment sums for the segment that holds T and re-reads that
+// segment alone to find the token.  Every workgroup decides acceptance
+// itself (k scalar reads) rather than waiting for another kernel.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -30,7 +33,9 @@ namespace pa {
 
 constexpr int kSvThreads = 256;
 constexpr int kSvWaves = kSvThreads / kWave;
-constexpr int kSvSeg = 4 * kWave;  // vocabulary entries per segment
+constexpr int kSvSeg = 4 * kWave;        // vocabulary entries per segment
+constexpr int kSvSegsPerWave = 4;
+constexpr int kSvSegsPerGroup = kSvWaves * kSvSegsPerWave;
 
 struct SpecVerifyParams {
   const float* target;       // [B][k+1][V]
@@ -39,8 +44,10 @@ struct SpecVerifyParams {
   const float* uniforms;     // [B][k+1]
   int32_t* out_tokens;       // [B][k+1]
   int32_t* num_out;          // [B]
+  uint64_t* seg_ws;          // [B][nseg] segment weight sums
   int k;
   int vocab;
+  int nseg;
 };
 
 __device__ inline uint64_t sv_weight(float r) {
@@ -81,8 +88,112 @@ __device__ inline uint64_t wave_scan_u64(uint64_t v, int lane) {
   return v;
 }
 
-__global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SpecVerifyParams p) {
-  extern __shared__ uint64_t seg_sum[];  // one per 256-entry segment
+// The distribution request b draws its last token from, once the first
+// rejected position i (k if none) is known.
+struct SvRow {
+  const float* p;  // p_i
+  const float* q;  // q_i, or null
+  int onehot;      // q_i one-hot at this token (drafts without distribution), or -1
+  int V;
+  __device__ uint64_t weight(int j, bool use_q) const {
+    if (j >= V) return 0;
+    float r = p[j];
+    if (use_q) {
+      if (q) r = r - q[j];
+      else if (j == onehot) r = r - 1.f;
+    }
+    return sv_weight(r);
+  }
+};
+
+// First rejected candidate of request b (k if all are kept), for every
+// thread of the workgroup.
+__device__ inline int sv_first_rejection(const SpecVerifyParams& p, int b, int* s_first) {
+  const int k = p.k, V = p.vocab, tid = threadIdx.x;
+  const float* tp = p.target + (int64_t)b * (k + 1) * V;
+  const float* dp = p.draft ? p.draft + (int64_t)b * k * V : nullptr;
+  if (tid == 0) *s_first = k;
+  __syncthreads();
+  if (tid < k) {
+    const int x = p.tokens[(int64_t)b * k + tid];
+    bool keep = false;
+    if (x >= 0 && x < V) {
+      const double pv = tp[(int64_t)tid * V + x];
+      const double qv = dp ? (double)dp[(int64_t)tid * V + x] : 1.0;
+      keep = (double)p.uniforms[(int64_t)b * (k + 1) + tid] * qv <= pv;
+    }
+    if (!keep) atomicMin(s_first, tid);
+  }
+  __syncthreads();
+  return *s_first;
+}
+
+__device__ inline SvRow sv_row(const SpecVerifyParams& p, int b, int i) {
+  const int k = p.k, V = p.vocab;
+  SvRow r;
+  r.p = p.target + ((int64_t)b * (k + 1) + i) * V;
+  const int x = i < k ? p.tokens[(int64_t)b * k + i] : -1;
+  const bool x_ok = x >= 0 && x < V;
+  r.q = (i < k && p.draft && x_ok) ? p.draft + ((int64_t)b * k + i) * V : nullptr;
+  r.onehot = (i < k && !p.draft && x_ok) ? x : -1;
+  r.V = V;
+  return r;
+}
+
+// Weight sum of segment s: lane l adds entries s*256 + 64e + l, e = 0..3
+// (each load instruction reads 256 contiguous bytes).
+__device__ inline uint64_t sv_segment_sum(const SvRow& row, int s, bool use_q, int lane) {
+  uint64_t acc = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc += row.weight(s * kSvSeg + e * kWave + lane, use_q);
+  return wave_sum_u64(acc);
+}
+
+// ---- kernel 1: segment sums of (p_i - q_i)_+ or p_k, spread over the chip
+__global__ __launch_bounds__(kSvThreads) void spec_segments_kernel(SpecVerifyParams p) {
+  __shared__ int s_first;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int i = sv_first_rejection(p, b, &s_first);
+  const SvRow row = sv_row(p, b, i);
+  const bool use_q = i < p.k;
+  const int s0 = blockIdx.x * kSvSegsPerGroup + wv * kSvSegsPerWave;
+  // all loads of the wave's segments first, then the sums
+  float pv[kSvSegsPerWave][4], qv[kSvSegsPerWave][4];
+#pragma unroll
+  for (int t = 0; t < kSvSegsPerWave; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = (s0 + t) * kSvSeg + e * kWave + lane;
+      const bool in = j < row.V;
+      pv[t][e] = in ? row.p[j] : 0.f;
+      qv[t][e] = (in && use_q && row.q) ? row.q[j] : 0.f;
+    }
+#pragma unroll
+  for (int t = 0; t < kSvSegsPerWave; ++t) {
+    const int s = s0 + t;
+    if (s >= p.nseg) break;  // uniform over the wave
+    uint64_t acc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = s * kSvSeg + e * kWave + lane;
+      float r = pv[t][e];
+      if (use_q) {
+        if (row.q) r = r - qv[t][e];
+        else if (j == row.onehot) r = r - 1.f;
+      }
+      acc += j < row.V ? sv_weight(r) : 0;
+    }
+    acc = wave_sum_u64(acc);
+    if (lane == 0) p.seg_ws[(int64_t)b * p.nseg + s] = acc;
+  }
+}
+
+// ---- kernel 2: one workgroup per request finds the token and writes the
+// outputs.  A residual without weight is redone here from p_i alone.
+__global__ __launch_bounds__(kSvThreads) void spec_select_kernel(SpecVerifyParams p) {
+  extern __shared__ uint64_t seg_sum[];  // fallback pass only
   __shared__ uint64_t chunk_sum[kSvThreads];
   __shared__ int s_first;
   __shared__ int s_token;
@@ -92,66 +203,30 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SpecVerifyParam
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int k = p.k;
-  const int V = p.vocab;
-  const float* tp = p.target + (int64_t)b * (k + 1) * V;
-  const float* dp = p.draft ? p.draft + (int64_t)b * k * V : nullptr;
-  const int32_t* toks = p.tokens + (int64_t)b * k;
-  const float* u = p.uniforms + (int64_t)b * (k + 1);
-
-  // ---- acceptance of every candidate; the first rejection ends the round
-  if (tid == 0) s_first = k;
-  __syncthreads();
-  if (tid < k) {
-    const int x = toks[tid];
-    bool keep = false;
-    if (x >= 0 && x < V) {
-      const double pv = tp[(int64_t)tid * V + x];
-      const double qv = dp ? (double)dp[(int64_t)tid * V + x] : 1.0;
-      keep = (double)u[tid] * qv <= pv;
-    }
-    if (!keep) atomicMin(&s_first, tid);
-  }
-  __syncthreads();
-  const int i = s_first;
-
-  // ---- the distribution the last token comes from: (p_i - q_i)_+ after a
-  // rejection at i, p_k after k acceptances
-  const float* prow = tp + (int64_t)i * V;
-  const int xi = i < k ? toks[i] : -1;
-  const bool x_ok = xi >= 0 && xi < V;
-  const float* qrow = (i < k && dp && x_ok) ? dp + (int64_t)i * V : nullptr;
-  const int onehot = (i < k && !dp && x_ok) ? xi : -1;  // q one-hot at the draft token
-  const int nseg = (V + kSvSeg - 1) / kSvSeg;
-  const float ui = u[k];
+  const int nseg = p.nseg;
+  const int i = sv_first_rejection(p, b, &s_first);
+  const SvRow row = sv_row(p, b, i);
+  const float ui = p.uniforms[(int64_t)b * (k + 1) + k];
+  const uint64_t* ws = p.seg_ws + (int64_t)b * nseg;
 
   int token = -1;
-  for (int pass = 0; pass < 2 && token < 0; ++pass) {
+  for (int pass = 0; pass < 2; ++pass) {
     const bool use_q = pass == 0 && i < k;
-    if (pass == 1 && !(i < k)) break;  // p_k had no weight: nothing to fall back to
-    auto weight_at = [&](int j) -> uint64_t {
-      if (j >= V) return 0;
-      float r = prow[j];
-      if (use_q) {
-        if (qrow) r = r - qrow[j];
-        else if (j == onehot) r = r - 1.f;
+    // pass 0 reads the first kernel's sums; pass 1 (p_i alone) makes its own
+    const uint64_t* sums = ws;
+    if (pass == 1) {
+      for (int s = wv; s < nseg; s += kSvWaves) {
+        const uint64_t v = sv_segment_sum(row, s, false, lane);
+        if (lane == 0) seg_sum[s] = v;
       }
-      return sv_weight(r);
-    };
-    // segment sums, one wave per segment
-    for (int s = wv; s < nseg; s += kSvWaves) {
-      const int j0 = s * kSvSeg + lane * 4;
-      uint64_t acc = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc += weight_at(j0 + e);
-      acc = wave_sum_u64(acc);
-      if (lane == 0) seg_sum[s] = acc;
+      __syncthreads();
+      sums = seg_sum;
     }
-    __syncthreads();
     // thread t owns segments [t * C, t * C + C)
     const int C = (nseg + kSvThreads - 1) / kSvThreads;
     {
       uint64_t acc = 0;
-      for (int s = tid * C; s < min(nseg, tid * C + C); ++s) acc += seg_sum[s];
+      for (int s = tid * C; s < min(nseg, tid * C + C); ++s) acc += sums[s];
       chunk_sum[tid] = acc;
     }
     __syncthreads();
@@ -168,21 +243,22 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SpecVerifyParam
       int tok = -1;
       if (W > 0) {
         const uint64_t T = sv_threshold(ui, W);
-        // first lane whose running sum passes T
+        // first lane whose running sum passes T, then its chunk
         const uint64_t hit = __ballot(incl > T);
         const int L = __ffsll((unsigned long long)hit) - 1;
-        uint64_t base = __shfl(incl - lsum, L, kWave);  // weight before lane L's chunks
+        uint64_t base = __shfl(incl - lsum, L, kWave);
         int chunk = -1;
         for (int e = 0; e < 4; ++e) {
           const uint64_t ce = __shfl(c4[e], L, kWave);
           if (chunk < 0 && base + ce > T) chunk = L * 4 + e;
           else if (chunk < 0) base += ce;
         }
-        // segments of that chunk, at most 64 of them per pass over the lanes
+        // the chunk's segments, 64 at a time
+        const int cend = min(nseg, chunk * C + C);
         int seg = -1;
-        for (int s0 = chunk * C; seg < 0 && s0 < min(nseg, chunk * C + C); s0 += kWave) {
+        for (int s0 = chunk * C; seg < 0 && s0 < cend; s0 += kWave) {
           const int s = s0 + lane;
-          const uint64_t v = s < min(nseg, chunk * C + C) ? seg_sum[s] : 0;
+          const uint64_t v = s < cend ? sums[s] : 0;
           const uint64_t in2 = wave_scan_u64(v, lane) + base;
           const uint64_t h2 = __ballot(in2 > T);
           if (h2) {
@@ -193,40 +269,34 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SpecVerifyParam
             base = __shfl(in2, kWave - 1, kWave);
           }
         }
-        // entries of that segment: lane l holds 4l .. 4l+3
-        const int j0 = seg * kSvSeg + lane * 4;
-        uint64_t w4[4], l4 = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w4[e] = weight_at(j0 + e);
-          l4 += w4[e];
+        // the segment's entries in order, 64 at a time
+        for (int e = 0; tok < 0 && e < 4; ++e) {
+          const int j = seg * kSvSeg + e * kWave + lane;
+          const uint64_t v = row.weight(j, use_q);
+          const uint64_t in3 = wave_scan_u64(v, lane) + base;
+          const uint64_t h3 = __ballot(in3 > T);
+          if (h3) tok = seg * kSvSeg + e * kWave + __ffsll((unsigned long long)h3) - 1;
+          else base = __shfl(in3, kWave - 1, kWave);
         }
-        const uint64_t in3 = wave_scan_u64(l4, lane) + base;
-        const uint64_t h3 = __ballot(in3 > T);
-        const int L3 = __ffsll((unsigned long long)h3) - 1;
-        if (lane == L3) {
-          uint64_t run = in3 - l4;
-          for (int e = 0; e < 4; ++e) {
-            run += w4[e];
-            if (run > T) {
-              tok = j0 + e;
-              break;
-            }
-          }
-        }
-        tok = __shfl(tok, L3, kWave);
       }
       if (lane == 0) s_token = tok;
     }
     __syncthreads();
     token = s_token;
-    __syncthreads();  // seg_sum / chunk_sum are rewritten by a second pass
+    if (token >= 0 || !(i < k)) break;  // uniform: an empty p_k has nothing to fall back to
+    __syncthreads();                    // chunk_sum is rewritten by the second pass
   }
 
   // ---- outputs: kept drafts, the drawn token, -1 padding
   int32_t* out = p.out_tokens + (int64_t)b * (k + 1);
+  const int32_t* toks = p.tokens + (int64_t)b * k;
   for (int t = tid; t <= k; t += kSvThreads) out[t] = t < i ? toks[t] : (t == i ? token : -1);
   if (tid == 0) p.num_out[b] = i + 1;
+}
+
+size_t spec_verify_workspace_bytes(int num_reqs, int vocab) {
+  const int64_t nseg = ((int64_t)vocab + kSvSeg - 1) / kSvSeg;
+  return (size_t)((int64_t)num_reqs * nseg * (int64_t)sizeof(uint64_t));
 }
 
 hipError_t launch_spec_verify(const SpecVerifyArgs& a, hipStream_t stream) {
@@ -238,11 +308,18 @@ hipError_t launch_spec_verify(const SpecVerifyArgs& a, hipStream_t stream) {
   p.uniforms = a.uniforms;
   p.out_tokens = a.out_tokens;
   p.num_out = a.num_out;
+  p.seg_ws = (uint64_t*)a.workspace;
   p.k = a.k;
   p.vocab = a.vocab;
-  const int nseg = (a.vocab + kSvSeg - 1) / kSvSeg;
-  hipLaunchKernelGGL(spec_verify_kernel, dim3((unsigned)a.num_reqs), dim3(kSvThreads),
-                     (size_t)nseg * sizeof(uint64_t), stream, p);
+  p.nseg = (a.vocab + kSvSeg - 1) / kSvSeg;
+  const int groups = (p.nseg + kSvSegsPerGroup - 1) / kSvSegsPerGroup;
+  if (a.num_reqs > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(spec_segments_kernel, dim3((unsigned)groups, (unsigned)a.num_reqs),
+                     dim3(kSvThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(spec_select_kernel, dim3((unsigned)a.num_reqs), dim3(kSvThreads),
+                     (size_t)p.nseg * sizeof(uint64_t), stream, p);
   return hipGetLastError();
 }
 

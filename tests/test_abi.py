@@ -186,8 +186,8 @@ def test_rejection_sample_argument_errors():
     p = ctypes.c_void_p(1)
     n = ctypes.c_void_p(0)
 
-    def call(B=2, k=4, V=100, tp=p, dt=p, u=p, out=p, num=p):
-        return L.pa_rejection_sample(tp, n, dt, u, B, k, V, out, num, None)
+    def call(B=2, k=4, V=100, tp=p, dt=p, u=p, out=p, num=p, ws=p, ws_bytes=1 << 20):
+        return L.pa_rejection_sample(tp, n, dt, u, B, k, V, out, num, ws, ws_bytes, None)
 
     assert call(B=-1) == -2
     assert call(V=0) == -2
@@ -197,3 +197,8 @@ def test_rejection_sample_argument_errors():
     assert call(dt=n) == -1                       # k > 0 needs draft tokens
     assert call(u=n, B=0) == 0                    # nothing to do
     assert call(B=1 << 20, k=32, V=1 << 21) == -6  # index range
+    assert call(B=70000, V=10) == -4               # grid limit
+    assert call(ws=n) == -5                        # workspace missing
+    assert call(B=64, V=128256, ws_bytes=64 * 501 * 8 - 1) == -5
+    assert L.pa_rejection_sample_workspace_bytes(64, 128256) == 64 * 501 * 8
+    assert L.pa_rejection_sample_workspace_bytes(0, 10) == 0

@@ -141,6 +141,26 @@ def test_repeated_calls_are_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_workspace_needs_no_initialisation_and_is_reusable():
+    """One workspace filled with garbage, then reused by calls of different
+    shapes: every call matches the oracle."""
+    log("rejection sample workspace reuse")
+    t = torch()
+    rng = np.random.default_rng(8)
+    ws = t.full((pa.pa_rejection_sample_workspace_bytes(64, 50000),), 0xA5, dtype=t.uint8,
+                device="cuda")
+    for B, k, V in ((64, 4, 50000), (7, 2, 301), (33, 8, 12345)):
+        p, q, toks, u = rand_case(rng, B, k, V)
+        dev = lambda a, dt: t.from_numpy(np.ascontiguousarray(a)).cuda()
+        out = t.empty((B, k + 1), dtype=t.int32, device="cuda")
+        n = t.empty((B,), dtype=t.int32, device="cuda")
+        pa.pa_rejection_sample(dev(p, None), dev(q, None), dev(toks, None), dev(u, None), out, n,
+                               workspace=ws)
+        t.cuda.synchronize()
+        want_t, want_n = sd.rejection_sample(p, q, toks, u)
+        assert np.array_equal(out.cpu().numpy(), want_t) and np.array_equal(n.cpu().numpy(), want_n)
+
+
 # ----------------------------------------------------------------------------
 # verification attention: k + 1 query rows per request
 
