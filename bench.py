@@ -305,7 +305,7 @@ def bench_shared_prefix(wl, pool, q, bt, cl, max_ctx, steps, warmup):
     }
 
 
-def bench_fp8_decode(wl, steps, warmup):
+def bench_fp8_decode(wl, steps, warmup, partition=0):
     """The decode step (cache write + pa_decode) of the same workload with
     fp8 (E4M3) pools: the same bf16 K/V rows are quantized into the pools
     with per-pool scales, and attention reads half the bytes."""
@@ -331,12 +331,13 @@ def bench_fp8_decode(wl, steps, warmup):
     cl = torch.from_numpy(wl.context_lens).to(dev)
     S, Hq, D = wl.q.shape
     max_ctx = int(wl.context_lens.max())
-    ws_bytes = pa.pa_decode_workspace_bytes(S, Hq, wl.num_kv_heads, D, max_ctx, 0)
+    ws_bytes = pa.pa_decode_workspace_bytes(S, Hq, wl.num_kv_heads, D, max_ctx, partition)
     ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def decode():
-        pa.pa_decode(out, q, pk, pv, bt, cl, max_ctx, float(wl.scale), desc, workspace=ws)
+        pa.pa_decode(out, q, pk, pv, bt, cl, max_ctx, float(wl.scale), desc,
+                     partition_size=partition, workspace=ws)
 
     def step():
         pa.pa_reshape_and_cache(new_k, new_v, new_slots, pk, pv, desc)
@@ -653,7 +654,8 @@ def main():
         print(json.dumps({"spec_verify_round": bench_spec_verify(args.steps, args.warmup)}), flush=True)
         return
     if args.fp8_only:
-        print(json.dumps({"fp8_kv_step": bench_fp8_decode(wl, args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"fp8_kv_step": bench_fp8_decode(wl, args.steps, args.warmup, args.partition)}),
+              flush=True)
         return
 
     pool = GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)

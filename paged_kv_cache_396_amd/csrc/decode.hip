@@ -490,6 +490,16 @@ constexpr int decode_waves_per_eu() {
          : (EB == 4 && D == 64 && G <= 2) ? 3 : (EB == 4 && D == 128 && G >= 4) ? 1 : 2;
 }
 
+// Register tile slots per wave (one computed, the others in flight).  A
+// third slot for the half-size fp8 tiles measured the same as two.
+#ifndef PA_DECODE_SLOTS_FP8
+#define PA_DECODE_SLOTS_FP8 2
+#endif
+template <int EB>
+constexpr int decode_slots() {
+  return EB == 1 ? PA_DECODE_SLOTS_FP8 : 2;
+}
+
 // CASC: shared-prefix decode.  The workgroup covers a partition of the
 // sequence's own blocks only (those after its group's shared prefix) and
 // always leaves a partial state for the merge.
@@ -561,7 +571,8 @@ void decode_partition_kernel(DecodeParams p) {
     my_ids = jb < b1 ? bt[jb] : 0;
   };
 
-  uint4 kb[2][C::NR][C::U], vb[2][C::NV];  // two tile slots
+  constexpr int NS = decode_slots<EB>();
+  uint4 kb[NS][C::NR][C::U], vb[NS][C::NV];  // tile slots: NS - 1 tiles in flight
   auto load_tile = [&](int id, bool real, uint4 (&kk)[C::NR][C::U], uint4 (&vv)[C::NV]) {
     const int64_t base = ((int64_t)id * p.num_kv_heads + g) * tile_bytes;
     wd.load_tile(p.k_cache + base, p.v_cache + base, real ? (int)tile_bytes : 0, kk, vv);
@@ -575,20 +586,23 @@ void decode_partition_kernel(DecodeParams p) {
     wd.process(kc, vc, nvalid);
   };
 
-  // Blocks are taken in chunks of 64 (one block id per lane).  Two register
-  // slots alternate: while one tile is computed the next is in flight.  The
-  // loads are unconditional (a tile past the chunk's end is an empty
+  // Blocks are taken in chunks of 64 (one block id per lane).  NS register
+  // slots rotate: while one tile is computed the next NS - 1 are in flight.
+  // The loads are unconditional (a tile past the chunk's end is an empty
   // descriptor), so the wait before each tile is a static count.
   for (int c0 = 0; c0 < nmine; c0 += 64) {
     const int cnt = min(64, nmine - c0);
     if (c0 > 0) fetch_ids(c0);
     auto id_at = [&](int i) { return __builtin_amdgcn_readlane(my_ids, min(i, cnt - 1)); };
-    load_tile(id_at(0), id_ok(id_at(0)), kb[0], vb[0]);
-    for (int n = 0; n < cnt; n += 2) {
-      load_tile(id_at(n + 1), n + 1 < cnt && id_ok(id_at(n + 1)), kb[1], vb[1]);
-      process(kb[0], vb[0], id_at(n), c0 + n);
-      load_tile(id_at(n + 2), n + 2 < cnt && id_ok(id_at(n + 2)), kb[0], vb[0]);
-      if (n + 1 < cnt) process(kb[1], vb[1], id_at(n + 1), c0 + n + 1);
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) load_tile(id_at(t), t < cnt && id_ok(id_at(t)), kb[t], vb[t]);
+    for (int n = 0; n < cnt; n += NS) {
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        const int t = n + sl + NS - 1;  // tile whose load goes out now
+        load_tile(id_at(t), t < cnt && id_ok(id_at(t)), kb[(sl + NS - 1) % NS], vb[(sl + NS - 1) % NS]);
+        if (n + sl < cnt) process(kb[sl], vb[sl], id_at(n + sl), c0 + n + sl);
+      }
     }
   }
 
