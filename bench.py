@@ -407,11 +407,32 @@ def bench_spec_verify(steps, warmup):
     on = torch.empty((a.num_reqs,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
+    # the same attention as shared-prefix decode: the k + 1 rows of a request
+    # are a group of "sequences" with identical block tables whose contexts
+    # end at their own positions; the blocks before the first row's position
+    # are the group's shared prefix, read once per group
+    ctx = a.context_lens.astype(np.int64)
+    rows_ctx = (ctx[:, None] - (k1 - 1) + np.arange(k1)[None, :]).reshape(-1).astype(np.int32)
+    rows_bt = torch.from_numpy(np.repeat(a.block_tables, k1, axis=0)).to(dev)
+    rows_cl = torch.from_numpy(rows_ctx).to(dev)
+    prefix_np = ((ctx - (k1 - 1)) // 16 * 16).astype(np.int32)
+    prefix = torch.from_numpy(prefix_np).to(dev)
+    max_ctx = int(ctx.max())
+    max_prefix = int(prefix_np.max())
+    sp_ws = torch.empty(pa.pa_decode_shared_prefix_workspace_bytes(
+        a.num_reqs * k1, a.num_q_heads, a.num_kv_heads, a.head_dim, max_ctx, k1, max_prefix) // 4 + 1,
+        dtype=torch.float32, device=dev)
+    out_sp = torch.empty_like(q)
+
     def write():
         pa.pa_reshape_and_cache(nk, nv, ns, pool.k, pool.v, pool.desc)
 
     def attend():
         pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, k1, float(a.scale), pool.desc)
+
+    def attend_grouped():
+        pa.pa_decode_shared_prefix(out_sp, q, pool.k, pool.v, rows_bt, rows_cl, max_ctx,
+                                   float(a.scale), prefix, k1, max_prefix, pool.desc, sp_ws)
 
     def sample():
         pa.pa_rejection_sample(tp, dp, tk, uu, ot, on, workspace=sws)
@@ -443,6 +464,7 @@ def bench_spec_verify(steps, warmup):
         return float(np.median([x.elapsed_time(y) for x, y in evs]))
 
     attn_ms = per_call(attend)
+    grouped_ms = per_call(attend_grouped)
     samp_ms = per_call(sample)
     n = on.cpu().numpy()
     V = int(w.target_probs.shape[2])
@@ -457,6 +479,8 @@ def bench_spec_verify(steps, warmup):
         "verify_attention_ms": round(attn_ms, 5),
         "verify_attention_kv_gbs": round(kv / (attn_ms * 1e-3) / 1e9, 1),
         "verify_attention_hbm_frac": round(kv / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "verify_attention_grouped_ms": round(grouped_ms, 5),
+        "verify_attention_grouped_kv_gbs": round(kv / (grouped_ms * 1e-3) / 1e9, 1),
         "rejection_sample_ms": round(samp_ms, 5),
         "rejection_sample_bytes": samp_bytes,
         "rejection_sample_gbs": round(samp_bytes / (samp_ms * 1e-3) / 1e9, 1),
