@@ -76,10 +76,13 @@ constexpr int kPfBlocks = kPfKT / kBlock;
 constexpr float kPfGap = 8.0f;           // log2 units a score may exceed the reference max
 constexpr float kPfNegBig = -FLT_MAX;
 constexpr int kPfDma = 1024;             // bytes one LDS-writing load instruction moves
-static_assert(kPfStages == 2 || kPfStages == 4, "stage count: even, and a power of two");
-static_assert(kPfWaves % kPfBlocks == 0, "whole waves per block");
+// Narrow shape for chunks of a few query rows (speculative verification,
+// shared-prefix groups): with 4 waves and 2 stages a workgroup needs half
+// the LDS, so two share a compute unit and twice as many waves compute.
+constexpr int kPfNarrowWaves = 4;
+constexpr int kPfNarrowStages = 2;
 
-template <int D>
+template <int D, int W = kPfWaves>
 struct PrefillCfg {
   static constexpr int RB = D * 2;             // bytes of one K row (bf16)
   static constexpr int KCH = RB / 16;          // 16-byte chunks per K row
@@ -88,9 +91,10 @@ struct PrefillCfg {
   static constexpr int BLK = kBlock * RB;      // one pool tile (block, kv head) of K or V
   static constexpr int TILE = kPfBlocks * BLK;  // K or V of one 64-key tile in LDS
   static constexpr int DPB = BLK / kPfDma;     // load instructions per pool tile
-  static constexpr int WPB = kPfWaves / kPfBlocks;  // waves sharing one block
+  static constexpr int WPB = W / kPfBlocks;    // waves sharing one block
   static constexpr int QPW = DPB / WPB;        // K (and V) instructions per wave per tile
   static constexpr int RPI = kPfDma / RB;      // K rows one instruction fills
+  static_assert(W % kPfBlocks == 0, "whole waves per block");
   static_assert(QPW >= 1 && QPW * WPB == DPB, "load split");
 };
 
@@ -178,19 +182,19 @@ __device__ inline void pf_copy_to_lds(const pf_rsrc& rs, unsigned lds, int voff)
 // query sees every key of the partition (they all sit past the prefix), and
 // the result is a partial state (running max in log2 units, sum, unscaled
 // output) for the decode merge instead of a normalised row.
-template <int D, int G, int NCB, bool PFX = false>
-__global__ __launch_bounds__(kPfWaves * kWave)
+template <int D, int G, int NCB, bool PFX = false, int W = kPfWaves, int S = kPfStages>
+__global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kernel(PrefillParams p) {
-  using C = PrefillCfg<D>;
-  constexpr int COLS = kPfWaves * 32 * NCB;  // columns per workgroup
-  constexpr int QT = COLS / G;               // queries per workgroup
-  constexpr int S = kPfStages;
+  using C = PrefillCfg<D, W>;
+  constexpr int COLS = W * 32 * NCB;  // columns per workgroup
+  constexpr int QT = COLS / G;        // queries per workgroup
+  static_assert(S == 2 || S == 4, "stage count: even, and a power of two");
   static_assert(COLS % G == 0, "group must divide the column tile");
 
   // One array per ring stage: the K tile, then the V tile.
   __shared__ __attribute__((aligned(1024))) char st0[2 * C::TILE], st1[2 * C::TILE];
-  __shared__ __attribute__((aligned(1024))) char st2[kPfStages > 2 ? 2 * C::TILE : 16];
-  __shared__ __attribute__((aligned(1024))) char st3[kPfStages > 2 ? 2 * C::TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char st2[S > 2 ? 2 * C::TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[S > 2 ? 2 * C::TILE : 16];
   auto stage = [&](auto J) -> char* {
     constexpr int j = decltype(J)::value % S;
     if constexpr (j == 0) return st0;
@@ -251,7 +255,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   const int nblk = (ctx + kBlock - 1) / kBlock;
 
   const int tid = threadIdx.x;
-  __builtin_assume(tid < kPfWaves * kWave);
+  __builtin_assume(tid < W * kWave);
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int half = lane >> 5;
@@ -659,9 +663,25 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   }
 }
 
+// Query rows one workgroup of W waves covers for GQA group size G.
+constexpr int pf_queries(int W, int G) { return W * 32 * PA_PF_NCB / G; }
+
+// The narrow shape when every request's rows (or a group's sequences) fit
+// one narrow workgroup: its other waves would have no column to compute.
+inline bool pf_narrow(int rows, int G) { return rows <= pf_queries(kPfNarrowWaves, G); }
+
 template <int D, int G>
-static hipError_t launch_prefill_t(const PrefillParams& prm, hipStream_t stream) {
+static hipError_t launch_prefill_t(PrefillParams prm, int max_q_len, hipStream_t stream) {
   constexpr int NCB = PA_PF_NCB;
+  if (pf_narrow(max_q_len, G)) {
+    prm.num_qtiles = 1;
+    const int64_t grid = (int64_t)prm.num_reqs * prm.num_kv_heads;
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, false, kPfNarrowWaves, kPfNarrowStages>),
+                       dim3((unsigned)grid), dim3(kPfNarrowWaves * kWave), 0, stream, prm);
+    return hipGetLastError();
+  }
+  const int qt = pf_queries(kPfWaves, G);
+  prm.num_qtiles = (max_q_len + qt - 1) / qt;
   const int64_t grid = (int64_t)prm.num_qtiles * prm.num_reqs * prm.num_kv_heads;
   hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB>), dim3((unsigned)grid),
                      dim3(kPfWaves * kWave), 0, stream, prm);
@@ -672,12 +692,17 @@ template <int D, int G>
 static hipError_t launch_prefix_t(const PrefillParams& prm, int num_groups, hipStream_t stream) {
   constexpr int NCB = PA_PF_NCB;
   const int64_t grid = (int64_t)prm.prefix_parts * num_groups * prm.num_kv_heads;
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true>), dim3((unsigned)grid),
-                     dim3(kPfWaves * kWave), 0, stream, prm);
+  if (pf_narrow(prm.group_size, G)) {
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true, kPfNarrowWaves, kPfNarrowStages>),
+                       dim3((unsigned)grid), dim3(kPfNarrowWaves * kWave), 0, stream, prm);
+  } else {
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true>), dim3((unsigned)grid),
+                       dim3(kPfWaves * kWave), 0, stream, prm);
+  }
   return hipGetLastError();
 }
 
-int prefill_queries_per_tile(int group) { return kPfWaves * 32 * PA_PF_NCB / group; }
+int prefill_queries_per_tile(int group) { return pf_queries(kPfWaves, group); }
 
 
 hipError_t launch_prefix_partials(const SharedPrefixArgs& a, const CacheGeom& g, hipStream_t stream) {
@@ -739,11 +764,9 @@ hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t 
   p.num_blocks = g.num_blocks;
   p.scale_log2 = a.scale * kLog2e;
   const int G = a.num_q_heads / g.num_kv_heads;
-  const int qt = prefill_queries_per_tile(G);
-  p.num_qtiles = (a.max_q_len + qt - 1) / qt;
 
 #define PA_PREFILL_CASE(D_, G_) \
-  if (g.head_dim == D_ && G == G_) return launch_prefill_t<D_, G_>(p, stream);
+  if (g.head_dim == D_ && G == G_) return launch_prefill_t<D_, G_>(p, a.max_q_len, stream);
   PA_PREFILL_CASE(128, 1) PA_PREFILL_CASE(128, 2) PA_PREFILL_CASE(128, 4) PA_PREFILL_CASE(128, 8)
   PA_PREFILL_CASE(64, 1) PA_PREFILL_CASE(64, 2) PA_PREFILL_CASE(64, 4) PA_PREFILL_CASE(64, 8)
 #undef PA_PREFILL_CASE
