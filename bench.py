@@ -124,8 +124,34 @@ def prefill_flops(wl):
     return tot * wl.num_q_heads * 4 * wl.head_dim
 
 
-def bench_prefill(steps, warmup):
-    """Time pa_prefill_chunk on the long-context mixed batch's prefill half."""
+class _Fp8Pool:
+    """fp8 (E4M3) K and V pools filled through the library's quantizing write."""
+
+    def __init__(self, wl):
+        import torch
+
+        import paged_kv_cache_396_amd as pa
+        from workloads import FP8_K_SCALE, FP8_V_SCALE
+
+        self.desc = pa.cache_desc(wl.num_blocks, wl.num_kv_heads, wl.head_dim, pa.PA_FP8_E4M3,
+                                  float(FP8_K_SCALE), float(FP8_V_SCALE))
+        n = pa.pa_cache_bytes(self.desc)
+        self.k = torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda")
+        self.v = torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda")
+
+    def write(self, k_raw, v_raw, slots):
+        import torch
+
+        import paged_kv_cache_396_amd as pa
+        from gpu_util import to_dev
+
+        pa.pa_reshape_and_cache(to_dev(k_raw, "bf16"), to_dev(v_raw, "bf16"),
+                                torch.from_numpy(slots).cuda(), self.k, self.v, self.desc)
+
+
+def bench_prefill(steps, warmup, fp8=False):
+    """Time pa_prefill_chunk on the long-context mixed batch's prefill half
+    (bf16 pools, or fp8 pools holding the same rows quantized)."""
     import torch
 
     import paged_kv_cache_396_amd as pa
@@ -135,7 +161,7 @@ def bench_prefill(steps, warmup):
     from gpu_util import GpuPool, to_dev  # noqa: E402
 
     wl = make_prefill(5)
-    pool = GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
+    pool = _Fp8Pool(wl) if fp8 else GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
     pool.write(wl.hist_k, wl.hist_v, wl.hist_slots)
     pool.write(wl.new_k, wl.new_v, wl.new_slots)
     q = to_dev(wl.q, wl.dtype)
@@ -164,7 +190,7 @@ def bench_prefill(steps, warmup):
     fl = prefill_flops(wl)
     tf = fl / (ms * 1e-3) / 1e12
     return {
-        "workload": "long_mixed_prefill",
+        "workload": "long_mixed_prefill", "kv_dtype": "fp8_e4m3" if fp8 else "bf16",
         "num_reqs": wl.num_reqs, "chunk_tokens": int(wl.max_q_len),
         "prior_tokens": int(wl.context_lens[0]) - int(wl.max_q_len),
         "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
@@ -665,7 +691,9 @@ def main():
         return
 
     if args.prefill_only:
-        print(json.dumps({"prefill_chunk": bench_prefill(args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"prefill_chunk": bench_prefill(args.steps, args.warmup),
+                          "fp8_prefill_chunk": bench_prefill(args.steps, args.warmup, fp8=True)}),
+              flush=True)
         return
 
     cfg = WORKLOADS[args.workload]
@@ -812,6 +840,7 @@ def main():
     line["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
     if not args.no_prefill:
         line["prefill_chunk"] = bench_prefill(min(args.steps, 20), min(args.warmup, 3))
+        line["fp8_prefill_chunk"] = bench_prefill(min(args.steps, 20), min(args.warmup, 3), fp8=True)
         line["long_mixed_step"] = bench_mixed_concurrent()
         line["block_pool"] = bench_block_pool()
         line["spec_verify_round"] = bench_spec_verify(min(args.steps, 20), min(args.warmup, 3))

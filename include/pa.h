@@ -280,7 +280,8 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n
  * (zihan-zhang.net vLLM study, 3.5: a long prompt is processed chunk by chunk;
  * batch metadata flattens all requests' tokens into one launch).
  *
- *   q, out           device [total_q_tokens][num_q_heads][D] (bf16 only)
+ *   q, out           device [total_q_tokens][num_q_heads][D], bf16 (pools bf16,
+ *                    or PA_FP8_E4M3 with D = 128)
  *   query_start_loc  device int32 [num_reqs + 1]; request r owns query rows
  *                    query_start_loc[r] .. query_start_loc[r+1]-1 (n_r rows)
  *   context_lens     device int32 [num_reqs]; ctx_r counts the chunk, whose
@@ -290,7 +291,10 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n
  *   block_tables     device int32 [num_reqs][max_blocks_per_seq]
  *   max_q_len        host bound on every n_r (sizes the grid)
  * Uses bf16 MFMA for Q K^T and P V with fp32 accumulation and an fp32
- * online-softmax state; P is rounded to bf16 before the P V product.
+ * online-softmax state; P is rounded to bf16 before the P V product.  fp8
+ * codes are widened exactly to bf16 after the LDS read; the K scale is folded
+ * into `scale` and the V scale into the normalisation.  With k + 1 rows per
+ * request this is the verification attention of speculative decoding.
  */
 int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,

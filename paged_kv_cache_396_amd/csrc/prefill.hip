@@ -82,11 +82,14 @@ constexpr int kPfDma = 1024;             // bytes one LDS-writing load instructi
 constexpr int kPfNarrowWaves = 4;
 constexpr int kPfNarrowStages = 2;
 
-template <int D, int W = kPfWaves>
+// KB: bytes of a pool element, 2 (bf16) or 1 (fp8 E4M3 codes, widened to
+// bf16 in registers after the LDS read).
+template <int D, int W = kPfWaves, int KB = 2>
 struct PrefillCfg {
-  static constexpr int RB = D * 2;             // bytes of one K row (bf16)
+  static constexpr int QRB = D * 2;            // bytes of one q / out row (bf16)
+  static constexpr int RB = D * KB;            // bytes of one K row in the pool
   static constexpr int KCH = RB / 16;          // 16-byte chunks per K row
-  static constexpr int DS = D / 16;            // k-steps of S^T = K Q^T
+  static constexpr int DS = D / 16;            // k-steps of S^T = K Q^T (16 dims each)
   static constexpr int DB = D / 32;            // 32-dim blocks of O^T
   static constexpr int BLK = kBlock * RB;      // one pool tile (block, kv head) of K or V
   static constexpr int TILE = kPfBlocks * BLK;  // K or V of one 64-key tile in LDS
@@ -114,6 +117,7 @@ struct PrefillParams {
   int num_blocks;
   int num_qtiles;
   float scale_log2;
+  float v_scale;  // fp8 pools: applied with the final normalisation
   // shared-prefix mode only: group p's sequences p * group_size .. are the
   // queries; the workgroup covers prefix partition j (prefix_partition keys)
   // and leaves its partial state in slot row * ws_stride + j
@@ -182,10 +186,11 @@ __device__ inline void pf_copy_to_lds(const pf_rsrc& rs, unsigned lds, int voff)
 // query sees every key of the partition (they all sit past the prefix), and
 // the result is a partial state (running max in log2 units, sum, unscaled
 // output) for the decode merge instead of a normalised row.
-template <int D, int G, int NCB, bool PFX = false, int W = kPfWaves, int S = kPfStages>
+template <int D, int G, int NCB, bool PFX = false, int W = kPfWaves, int S = kPfStages, int KB = 2>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kernel(PrefillParams p) {
-  using C = PrefillCfg<D, W>;
+  using C = PrefillCfg<D, W, KB>;
+  static_assert(KB == 2 || (KB == 1 && !PFX), "fp8 pools: chunk mode only");
   constexpr int COLS = W * 32 * NCB;  // columns per workgroup
   constexpr int QT = COLS / G;        // queries per workgroup
   static_assert(S == 2 || S == 4, "stage count: even, and a power of two");
@@ -279,10 +284,14 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     const int hh = c % G;
     const bool valid = qi < n_r;
     pos[cb] = valid ? (PFX ? prior : prior + qi) : -1;
-    const char* qrow = p.q + ((int64_t)(qs + (valid ? qi : 0)) * p.num_q_heads + g * G + hh) * C::RB;
+    const char* qrow = p.q + ((int64_t)(qs + (valid ? qi : 0)) * p.num_q_heads + g * G + hh) * C::QRB;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
-      uint4 v = valid ? *(const uint4*)(qrow + (2 * s + half) * 16) : make_uint4(0, 0, 0, 0);
+      // k-step s, lane half h: dims 16 s + 8 h .. (bf16 pools); with fp8
+      // pools the dims follow the 16-code chunks a lane reads, 32 (s / 2) +
+      // 16 h + 8 (s % 2) .. (the same order on both sides of the product)
+      const int qoff = KB == 2 ? (2 * s + half) * 16 : 64 * (s >> 1) + 32 * half + 16 * (s & 1);
+      uint4 v = valid ? *(const uint4*)(qrow + qoff) : make_uint4(0, 0, 0, 0);
       v.x ^= qsign; v.y ^= qsign; v.z ^= qsign; v.w ^= qsign;
       qf[cb][s] = v;
     }
@@ -309,7 +318,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   //  * K piece i fills rows RPI i .. of the block (LDS row m holds key
   //    pf_key16(m)); slot j of row m receives chunk j ^ pf_ksw(m).
   //  * V piece i fills slots 64 i .. of the dim-major block (32 bytes per
-  //    dim); slot j of dim x receives chunk j ^ ((x / 8) % 2).
+  //    dim); slot j of dim x receives chunk j ^ ((x / 8) % 2).  fp8 pools:
+  //    16 bytes per dim, copied in order.
   const int bsub = w / C::WPB;
   const int isub = (w % C::WPB) * C::QPW;
   int kvo[C::QPW], vvo[C::QPW];
@@ -320,9 +330,13 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     const int kc = (lane % C::KCH) ^ pf_ksw<C::RB>(m);
     kvo[u] = pf_key16(m) * C::RB + kc * 16;
     const int sp = 64 * i + lane;
-    const int x = sp >> 1;
-    const int vc = (sp & 1) ^ ((x >> 3) & 1);
-    vvo[u] = x * 32 + vc * 16;
+    if constexpr (KB == 2) {
+      const int x = sp >> 1;
+      const int vc = (sp & 1) ^ ((x >> 3) & 1);
+      vvo[u] = x * 32 + vc * 16;
+    } else {
+      vvo[u] = sp * 16;
+    }
   }
   const int64_t bstride = (int64_t)p.num_kv_heads * C::BLK;  // bytes per pool block
   // id of this wave's block of tile n; -1 past the keys this workgroup needs
@@ -373,7 +387,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // 32 db + cw of 16-key step st, keys 8 half ..
   const int ksw = pf_ksw<C::RB>(cw & 15);
   const int kfb = (cw >> 4) * C::BLK + (cw & 15) * C::RB + 16 * (half ^ (ksw & 1)) + 32 * (ksw >> 1);
-  const int vfb = cw * 32 + 16 * (half ^ ((cw >> 3) & 1));
+  // fp8 V: dim 32 db + cw, keys 8 half .. of a block are 8 bytes at
+  // (32 db + cw) * 16 + 8 half
+  const int vfb = KB == 2 ? cw * 32 + 16 * (half ^ ((cw >> 3) & 1)) : cw * 16 + 8 * half;
 
   // The tile is processed as two 32-key blocks, each a full online-softmax
   // step, so that the vector work of one block overlaps the matrix products
@@ -388,6 +404,32 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   constexpr int kPfAhead = PA_PF_AHEAD;
   auto scores = [&](const char* st, int kf, int kb, f32x16_t (&sacc)[NCB]) __attribute__((always_inline)) {
     auto kfrag = [&](int s) { return *(const uint4*)(st + kb * 2 * C::BLK + (kf ^ (s * 32))); };
+    if constexpr (KB == 1) {
+      // one 16-code chunk per lane feeds two k-steps once widened to bf16
+      constexpr int NP = C::DS / 2;
+      uint4 ka[2];
+      ka[0] = kfrag(0);
+#pragma unroll
+      for (int sp = 0; sp < NP; ++sp) {
+        if (sp + 1 < NP) ka[(sp + 1) & 1] = kfrag(sp + 1);
+        const uint4 raw = ka[sp & 1];
+        const uint4 w0 = make_uint4(fp8x2_to_bf16x2<false>(raw.x), fp8x2_to_bf16x2<true>(raw.x),
+                                    fp8x2_to_bf16x2<false>(raw.y), fp8x2_to_bf16x2<true>(raw.y));
+        const uint4 w1 = make_uint4(fp8x2_to_bf16x2<false>(raw.z), fp8x2_to_bf16x2<true>(raw.z),
+                                    fp8x2_to_bf16x2<false>(raw.w), fp8x2_to_bf16x2<true>(raw.w));
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const f32x16_t zero = {};
+          sacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, w0), __builtin_bit_cast(bf16x8_t, qf[cb][2 * sp]),
+              sp == 0 ? zero : sacc[cb], 0, 0, 0);
+          sacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, w1), __builtin_bit_cast(bf16x8_t, qf[cb][2 * sp + 1]),
+              sacc[cb], 0, 0, 0);
+        }
+      }
+      return;
+    }
     uint4 ka[kPfAhead + 1];
 #pragma unroll
     for (int s = 0; s < kPfAhead; ++s) ka[s] = kfrag(s);
@@ -503,7 +545,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     constexpr int NJ = 2 * C::DB;  // product j: 16-key step 2 kb + j / DB, dim block j % DB
     auto vfrag = [&](int j) {
       const int step = 2 * kb + j / C::DB, db = j % C::DB;
-      return *(const uint4*)(st + step * C::BLK + db * 32 * 32 + vf);
+      if constexpr (KB == 2) return *(const uint4*)(st + step * C::BLK + db * 32 * 32 + vf);
+      const uint2 raw = *(const uint2*)(st + step * C::BLK + db * 32 * 16 + vf);
+      return make_uint4(fp8x2_to_bf16x2<false>(raw.x), fp8x2_to_bf16x2<true>(raw.x),
+                        fp8x2_to_bf16x2<false>(raw.y), fp8x2_to_bf16x2<true>(raw.y));
     };
     const bool tail = MASK && k0 + kPfKT > ctx;  // uniform
     uint4 va[kPfAhead + 1];
@@ -648,8 +693,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
         }
       continue;
     }
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    char* orow = (char*)p.out + ((int64_t)(qs + qi) * p.num_q_heads + g * G + c % G) * C::RB;
+    float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if constexpr (KB == 1) inv *= p.v_scale;
+    char* orow = (char*)p.out + ((int64_t)(qs + qi) * p.num_q_heads + g * G + c % G) * C::QRB;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -670,21 +716,21 @@ constexpr int pf_queries(int W, int G) { return W * 32 * PA_PF_NCB / G; }
 // one narrow workgroup: its other waves would have no column to compute.
 inline bool pf_narrow(int rows, int G) { return rows <= pf_queries(kPfNarrowWaves, G); }
 
-template <int D, int G>
+template <int D, int G, int KB>
 static hipError_t launch_prefill_t(PrefillParams prm, int max_q_len, hipStream_t stream) {
   constexpr int NCB = PA_PF_NCB;
   if (pf_narrow(max_q_len, G)) {
     prm.num_qtiles = 1;
     const int64_t grid = (int64_t)prm.num_reqs * prm.num_kv_heads;
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, false, kPfNarrowWaves, kPfNarrowStages>),
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, false, kPfNarrowWaves, kPfNarrowStages, KB>),
                        dim3((unsigned)grid), dim3(kPfNarrowWaves * kWave), 0, stream, prm);
     return hipGetLastError();
   }
   const int qt = pf_queries(kPfWaves, G);
   prm.num_qtiles = (max_q_len + qt - 1) / qt;
   const int64_t grid = (int64_t)prm.num_qtiles * prm.num_reqs * prm.num_kv_heads;
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB>), dim3((unsigned)grid),
-                     dim3(kPfWaves * kWave), 0, stream, prm);
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, false, kPfWaves, kPfStages, KB>),
+                     dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, prm);
   return hipGetLastError();
 }
 
@@ -738,12 +784,13 @@ hipError_t launch_prefix_partials(const SharedPrefixArgs& a, const CacheGeom& g,
 }
 
 bool prefill_supported(int elem_bytes, int head_dim, int group) {
-  return elem_bytes == 2 && (head_dim == 64 || head_dim == 128) &&
-         (group == 1 || group == 2 || group == 4 || group == 8);
+  const bool shape = elem_bytes == 2 ? (head_dim == 64 || head_dim == 128)
+                                     : elem_bytes == 1 && head_dim == 128;
+  return shape && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 bool shared_prefix_supported(int elem_bytes, int head_dim, int group, int group_size) {
-  return prefill_supported(elem_bytes, head_dim, group) && group_size >= 1 &&
+  return elem_bytes == 2 && prefill_supported(elem_bytes, head_dim, group) && group_size >= 1 &&
          group_size <= prefill_queries_per_tile(group);
 }
 
@@ -762,13 +809,17 @@ hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t 
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = g.num_kv_heads;
   p.num_blocks = g.num_blocks;
-  p.scale_log2 = a.scale * kLog2e;
+  // fp8 pools: the K scale multiplies every score, the V scale the output
+  p.scale_log2 = a.scale * g.k_scale * kLog2e;
+  p.v_scale = g.v_scale;
   const int G = a.num_q_heads / g.num_kv_heads;
 
-#define PA_PREFILL_CASE(D_, G_) \
-  if (g.head_dim == D_ && G == G_) return launch_prefill_t<D_, G_>(p, a.max_q_len, stream);
-  PA_PREFILL_CASE(128, 1) PA_PREFILL_CASE(128, 2) PA_PREFILL_CASE(128, 4) PA_PREFILL_CASE(128, 8)
-  PA_PREFILL_CASE(64, 1) PA_PREFILL_CASE(64, 2) PA_PREFILL_CASE(64, 4) PA_PREFILL_CASE(64, 8)
+#define PA_PREFILL_CASE(KB_, D_, G_)                  \
+  if (g.elem_bytes == KB_ && g.head_dim == D_ && G == G_) \
+    return launch_prefill_t<D_, G_, KB_>(p, a.max_q_len, stream);
+  PA_PREFILL_CASE(2, 128, 1) PA_PREFILL_CASE(2, 128, 2) PA_PREFILL_CASE(2, 128, 4) PA_PREFILL_CASE(2, 128, 8)
+  PA_PREFILL_CASE(2, 64, 1) PA_PREFILL_CASE(2, 64, 2) PA_PREFILL_CASE(2, 64, 4) PA_PREFILL_CASE(2, 64, 8)
+  PA_PREFILL_CASE(1, 128, 1) PA_PREFILL_CASE(1, 128, 2) PA_PREFILL_CASE(1, 128, 4) PA_PREFILL_CASE(1, 128, 8)
 #undef PA_PREFILL_CASE
   return hipErrorInvalidValue;
 }

@@ -15,7 +15,7 @@ import oracle
 import oracle.fp8 as f8
 import paged_kv_cache_396_amd as pa
 from workloads import (FP8_K_SCALE, FP8_POISON, FP8_V_SCALE, bf16_bits_from_f32, make_decode,
-                       make_tiny_decode)
+                       make_prefill, make_spec_verify, make_tiny_decode, make_tiny_prefill)
 
 from gpu_util import assert_close, decode_workspace, log, to_dev, to_f64, torch
 
@@ -215,3 +215,82 @@ def test_decode_zero_length_context_gives_zeros():
     got = gpu_decode_fp8(wl, pool, 16)
     assert (got[0] == 0).all()
     assert_close(got[1:], oracle_decode_fp8(wl, pool)[1:], "bf16", "ctx 0 neighbour")
+
+
+# ----------------------------------------------------------------------------
+# chunked prefill over fp8 pools
+
+
+def gpu_prefill_fp8(wl, pool, max_q_len=None):
+    t = torch()
+    q = to_dev(wl.q, "bf16")
+    out = t.empty_like(q)
+    bt = t.from_numpy(np.ascontiguousarray(wl.block_tables)).cuda()
+    qsl = t.from_numpy(np.ascontiguousarray(wl.query_start_loc, dtype=np.int32)).cuda()
+    cl = t.from_numpy(np.ascontiguousarray(wl.context_lens, dtype=np.int32)).cuda()
+    mq = int(np.diff(wl.query_start_loc).max()) if max_q_len is None else max_q_len
+    pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, mq, float(wl.scale), pool.desc)
+    t.cuda.synchronize()
+    return to_f64(out)
+
+
+def oracle_prefill_fp8(wl, pool, rows=None):
+    return f8.prefill_attention(wl.q, pool.ok, pool.ov, wl.block_tables, wl.query_start_loc,
+                                wl.context_lens, wl.scale, pool.k_scale, pool.v_scale, rows=rows)
+
+
+PREFILL_SHAPES = [
+    # Hq, Hkv, prior, chunk: narrow (few rows) and wide (many rows) workgroups,
+    # ragged tails, empty priors
+    (32, 8, (0, 5, 40), (7, 16, 33)),
+    (32, 8, (0,), (1,)),
+    (32, 8, (16, 100, 0, 63), (1, 15, 130, 64)),
+    (64, 8, (3, 200), (17, 70)),
+    (8, 4, (31, 0), (40, 129)),
+    (4, 4, (10,), (200,)),
+    (16, 2, (0, 77), (300, 5)),
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,prior,chunk", PREFILL_SHAPES)
+def test_prefill_tiny_shapes(Hq, Hkv, prior, chunk):
+    log(f"fp8 prefill Hq={Hq} Hkv={Hkv} prior={prior} chunk={chunk}")
+    wl = make_tiny_prefill(seed=71 + Hq + sum(chunk), prior=prior, chunk=chunk, Hq=Hq, Hkv=Hkv, D=128)
+    pool = fp8_pool_for(wl)
+    pool.assert_codes_equal("prior + chunk")
+    got = gpu_prefill_fp8(wl, pool)
+    err = assert_close(got, oracle_prefill_fp8(wl, pool), "bf16", f"fp8 prefill {Hq}/{Hkv}")
+    log(f"  max abs err {err:.3g}")
+
+
+def test_prefill_long_mixed_chunks_sampled():
+    """The long-context prefill batch (4 x 512-token chunks over 4096 prior
+    tokens) over fp8 pools; 24 sampled rows per request checked."""
+    log("fp8 prefill long mixed (sampled)")
+    wl = make_prefill(5)
+    pool = fp8_pool_for(wl)
+    got = gpu_prefill_fp8(wl, pool)
+    assert np.isfinite(got).all()
+    rows = [int(wl.query_start_loc[r]) + i for r in range(wl.num_reqs) for i in range(0, 512, 22)]
+    ref = oracle_prefill_fp8(wl, pool, rows=rows)
+    err = assert_close(got[rows], ref[rows], "bf16", "long mixed fp8")
+    log(f"  max abs err {err:.3g}")
+
+
+def test_spec_verification_attention_over_fp8_pools():
+    log("fp8 verification attention k=4")
+    wl = make_spec_verify(batch=24, k=4, vocab=8).attn
+    pool = fp8_pool_for(wl)
+    got = gpu_prefill_fp8(wl, pool)
+    assert_close(got, oracle_prefill_fp8(wl, pool), "bf16", "fp8 verification")
+
+
+def test_prefill_last_row_matches_decode_over_the_same_codes():
+    log("fp8 prefill last row vs decode")
+    wl = make_tiny_prefill(seed=5, prior=(40, 300), chunk=(9, 33), Hq=32, Hkv=8, D=128)
+    pool = fp8_pool_for(wl)
+    got = gpu_prefill_fp8(wl, pool)
+    last = wl.query_start_loc[1:] - 1
+    dec = f8.decode_attention(wl.q[last], pool.ok, pool.ov, wl.block_tables, wl.context_lens,
+                              wl.scale, pool.k_scale, pool.v_scale)
+    assert_close(got[last], dec, "bf16", "last rows")
