@@ -196,7 +196,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *                  at most max_context_len; sizes the grid)
  *   workspace      device scratch of pa_decode_shared_prefix_workspace_bytes
  *                  bytes; same rules as pa_decode's.
- * The other arguments are pa_decode's.  Supported: bf16 pools, D in {64, 128},
+ * The other arguments are pa_decode's.  Supported: bf16 pools with D in
+ * {64, 128} and PA_FP8_E4M3 pools with D = 128,
  * num_q_heads / Hkv in {1, 2, 4, 8}, group_size * (num_q_heads / Hkv) <= 256.
  * The prefix part runs on bf16 MFMA (P rounded to bf16, as in
  * pa_prefill_chunk); each sequence's own blocks run through the decode

@@ -793,7 +793,8 @@ hipError_t launch_decode_own_and_merge(const SharedPrefixArgs& a, const CacheGeo
   p.num_blocks = g.num_blocks;
   p.num_partitions = a.d.num_partitions;
   p.partition_blocks = a.d.partition_blocks;
-  p.scale_log2 = a.d.scale * kLog2e;
+  p.scale_log2 = a.d.scale * g.k_scale * kLog2e;
+  p.v_scale = g.v_scale;
   p.prefix_lens = a.prefix_lens;
   p.group_size = a.group_size;
   p.prefix_partition = a.prefix_partition;
@@ -804,6 +805,7 @@ hipError_t launch_decode_own_and_merge(const SharedPrefixArgs& a, const CacheGeo
   if (g.elem_bytes == EB_ && g.head_dim == D_ && G == G_) return launch_own_and_merge_t<EB_, D_, G_>(p, stream);
   PA_OWN_CASE(2, 128, 1) PA_OWN_CASE(2, 128, 2) PA_OWN_CASE(2, 128, 4) PA_OWN_CASE(2, 128, 8)
   PA_OWN_CASE(2, 64, 1) PA_OWN_CASE(2, 64, 2) PA_OWN_CASE(2, 64, 4) PA_OWN_CASE(2, 64, 8)
+  PA_OWN_CASE(1, 128, 1) PA_OWN_CASE(1, 128, 2) PA_OWN_CASE(1, 128, 4) PA_OWN_CASE(1, 128, 8)
 #undef PA_OWN_CASE
   return hipErrorInvalidValue;
 }

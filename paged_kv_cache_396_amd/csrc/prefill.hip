@@ -190,7 +190,6 @@ template <int D, int G, int NCB, bool PFX = false, int W = kPfWaves, int S = kPf
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kernel(PrefillParams p) {
   using C = PrefillCfg<D, W, KB>;
-  static_assert(KB == 2 || (KB == 1 && !PFX), "fp8 pools: chunk mode only");
   constexpr int COLS = W * 32 * NCB;  // columns per workgroup
   constexpr int QT = COLS / G;        // queries per workgroup
   static_assert(S == 2 || S == 4, "stage count: even, and a power of two");
@@ -734,16 +733,16 @@ static hipError_t launch_prefill_t(PrefillParams prm, int max_q_len, hipStream_t
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, int KB>
 static hipError_t launch_prefix_t(const PrefillParams& prm, int num_groups, hipStream_t stream) {
   constexpr int NCB = PA_PF_NCB;
   const int64_t grid = (int64_t)prm.prefix_parts * num_groups * prm.num_kv_heads;
   if (pf_narrow(prm.group_size, G)) {
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true, kPfNarrowWaves, kPfNarrowStages>),
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true, kPfNarrowWaves, kPfNarrowStages, KB>),
                        dim3((unsigned)grid), dim3(kPfNarrowWaves * kWave), 0, stream, prm);
   } else {
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true>), dim3((unsigned)grid),
-                       dim3(kPfWaves * kWave), 0, stream, prm);
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true, kPfWaves, kPfStages, KB>),
+                       dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, prm);
   }
   return hipGetLastError();
 }
@@ -763,7 +762,9 @@ hipError_t launch_prefix_partials(const SharedPrefixArgs& a, const CacheGeom& g,
   p.num_q_heads = a.d.num_q_heads;
   p.num_kv_heads = g.num_kv_heads;
   p.num_blocks = g.num_blocks;
-  p.scale_log2 = a.d.scale * kLog2e;
+  // fp8 pools: the K scale multiplies every score; partial outputs stay in
+  // code units and the merge applies the V scale
+  p.scale_log2 = a.d.scale * g.k_scale * kLog2e;
   p.prefix_lens = a.prefix_lens;
   p.group_size = a.group_size;
   p.prefix_partition = a.prefix_partition;
@@ -775,10 +776,12 @@ hipError_t launch_prefix_partials(const SharedPrefixArgs& a, const CacheGeom& g,
   p.ws_o = a.d.ws + (2 * rows * a.ws_stride + 3) / 4 * 4;
   const int G = a.d.num_q_heads / g.num_kv_heads;
   const int groups = a.d.num_seqs / a.group_size;
-#define PA_PREFIX_CASE(D_, G_) \
-  if (g.head_dim == D_ && G == G_) return launch_prefix_t<D_, G_>(p, groups, stream);
-  PA_PREFIX_CASE(128, 1) PA_PREFIX_CASE(128, 2) PA_PREFIX_CASE(128, 4) PA_PREFIX_CASE(128, 8)
-  PA_PREFIX_CASE(64, 1) PA_PREFIX_CASE(64, 2) PA_PREFIX_CASE(64, 4) PA_PREFIX_CASE(64, 8)
+#define PA_PREFIX_CASE(KB_, D_, G_)                           \
+  if (g.elem_bytes == KB_ && g.head_dim == D_ && G == G_) \
+    return launch_prefix_t<D_, G_, KB_>(p, groups, stream);
+  PA_PREFIX_CASE(2, 128, 1) PA_PREFIX_CASE(2, 128, 2) PA_PREFIX_CASE(2, 128, 4) PA_PREFIX_CASE(2, 128, 8)
+  PA_PREFIX_CASE(2, 64, 1) PA_PREFIX_CASE(2, 64, 2) PA_PREFIX_CASE(2, 64, 4) PA_PREFIX_CASE(2, 64, 8)
+  PA_PREFIX_CASE(1, 128, 1) PA_PREFIX_CASE(1, 128, 2) PA_PREFIX_CASE(1, 128, 4) PA_PREFIX_CASE(1, 128, 8)
 #undef PA_PREFIX_CASE
   return hipErrorInvalidValue;
 }
@@ -790,7 +793,7 @@ bool prefill_supported(int elem_bytes, int head_dim, int group) {
 }
 
 bool shared_prefix_supported(int elem_bytes, int head_dim, int group, int group_size) {
-  return elem_bytes == 2 && prefill_supported(elem_bytes, head_dim, group) && group_size >= 1 &&
+  return prefill_supported(elem_bytes, head_dim, group) && group_size >= 1 &&
          group_size <= prefill_queries_per_tile(group);
 }
 
