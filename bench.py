@@ -357,9 +357,10 @@ def bench_shared_prefix(wl, pool, q, bt, cl, max_ctx, steps, warmup):
 
 
 def bench_fp8_decode(wl, steps, warmup, partition=0):
-    """The decode step (cache write + pa_decode) of the same workload with
-    fp8 (E4M3) pools: the same bf16 K/V rows are quantized into the pools
-    with per-pool scales, and attention reads half the bytes."""
+    """The decode step (pa_decode_append: cache write fused with decode) of
+    the same workload with fp8 (E4M3) pools: the same bf16 K/V rows are
+    quantized into the pools with per-pool scales, and attention reads half
+    the bytes.  The two-call step and pa_decode alone are timed beside it."""
     import torch
 
     import paged_kv_cache_396_amd as pa
@@ -391,19 +392,28 @@ def bench_fp8_decode(wl, steps, warmup, partition=0):
                      partition_size=partition, workspace=ws)
 
     def step():
+        pa.pa_decode_append(out, q, new_k, new_v, new_slots, pk, pv, bt, cl, max_ctx,
+                            float(wl.scale), desc, partition_size=partition, workspace=ws)
+
+    def two_call_step():
         pa.pa_reshape_and_cache(new_k, new_v, new_slots, pk, pv, desc)
         decode()
 
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
     for _ in range(warmup):
         step()
+        two_call_step()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        step()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms_step = a.elapsed_time(b) / steps
+    ms_step = timed(step)
+    ms_two = timed(two_call_step)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for e0, e1 in evs:
@@ -418,6 +428,7 @@ def bench_fp8_decode(wl, steps, warmup, partition=0):
         "kv_dtype": "fp8_e4m3", "k_scale": float(FP8_K_SCALE), "v_scale": float(FP8_V_SCALE),
         "ms_per_step": round(ms_step, 5), "tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": kv, "step_gbs": round(kv / (ms_step * 1e-3) / 1e9, 1),
+        "two_call_ms_per_step": round(ms_two, 5),
         "decode_call_median_ms": round(dec, 5),
         "decode_call_gbs": round(kv / (dec * 1e-3) / 1e9, 1),
         "decode_call_hbm_frac": round(kv / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -751,7 +762,15 @@ def main():
     ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
+    # one step of the layer: every sequence's newest K/V row goes into its
+    # slot and the sequences attend over their whole context, in one launch
+    # (pa_decode_append); the two-call form is timed beside it
     def step():
+        pa.pa_decode_append(out, q, new_k, new_v, new_slots, pool.k, pool.v, bt, cl, max_ctx,
+                            float(wl.scale), pool.desc, partition_size=args.partition,
+                            workspace=ws)
+
+    def two_call_step():
         pa.pa_reshape_and_cache(new_k, new_v, new_slots, pool.k, pool.v, pool.desc)
         decode()
 
@@ -761,6 +780,7 @@ def main():
 
     for _ in range(args.warmup):
         step()
+        two_call_step()
     torch.cuda.synchronize()
 
     # timed steps: nothing but the hot path between the two events
@@ -777,33 +797,43 @@ def main():
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
 
-    # roofline of the decode call: each call bracketed by its own events on
-    # the launch stream (a separate pass, so the events do not pad the steps)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:
-        pa.pa_reshape_and_cache(new_k, new_v, new_slots, pool.k, pool.v, pool.desc)
-        a.record(stream)
-        decode()
-        b.record(stream)
+    # the same steps as two calls (cache write, then decode)
+    start2 = torch.cuda.Event(enable_timing=True)
+    stop2 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    start2.record(stream)
+    for _ in range(args.steps):
+        two_call_step()
+    stop2.record(stream)
+    torch.cuda.synchronize()
+    ms_two = start2.elapsed_time(stop2) / args.steps
+
+    def per_call(fn, before=None):
+        """Each call bracketed by its own events on the launch stream (a
+        separate pass, so the events do not pad the timed steps)."""
+        evs = []
+        for _ in range(args.steps):
+            if before is not None:
+                before()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    # roofline of the step's launch (pa_decode_append) and of pa_decode alone
+    step_ms = per_call(step)
+    step_avg_ms = float(np.mean(step_ms))
+    dec_ms = per_call(decode, before=lambda: pa.pa_reshape_and_cache(
+        new_k, new_v, new_slots, pool.k, pool.v, pool.desc))
     dec_avg_ms = float(np.mean(dec_ms))
 
     # the same call with the caches cold: an untimed 512 MiB write (larger
     # than the L2s and the 256 MB last-level cache together) before each one
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold = []
-    for _ in range(args.steps):
-        pa.pa_reshape_and_cache(new_k, new_v, new_slots, pool.k, pool.v, pool.desc)
-        scrub.fill_(7)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        decode()
-        b.record(stream)
-        cold.append((a, b))
-    torch.cuda.synchronize()
-    cold_ms = [a.elapsed_time(b) for a, b in cold]
+    cold_ms = per_call(step, before=lambda: scrub.fill_(7))
     del scrub
 
     def dist(ms):
@@ -814,7 +844,7 @@ def main():
 
     kv = wl.kv_bytes
     value = kv / (ms_step * 1e-3) / 1e9
-    achieved = kv / (dec_avg_ms * 1e-3) / 1e9
+    achieved = kv / (step_avg_ms * 1e-3) / 1e9
     traffic = _traffic(args.workload, kv)
     line = {
         "metric": METRIC,
@@ -834,19 +864,26 @@ def main():
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": wl.num_kv_heads, "head_dim": D,
             "block_size": 16, "context_lens": "U[128,4096]" if cfg == 2 else "per config",
             "ctx_sum": int(wl.context_lens.sum()), "num_blocks": wl.num_blocks,
-            "partition_tokens": part, "new_tokens_per_step": int(len(wl.new_slots)),
+            "decode_schedule": ("work-balanced: equal block ranges, one per resident workgroup"
+                                if part == 0 else f"partitions of {part} tokens"),
+            "new_tokens_per_step": int(len(wl.new_slots)),
             "parallelism": "single GPU",
         },
         "tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": kv,
+        "step_call": "pa_decode_append (cache write of the 64 new tokens fused with decode)",
+        "step_call_hot": dist(step_ms),
+        "step_call_cold": dist(cold_ms),
+        "two_call_step": {"calls": "pa_reshape_and_cache + pa_decode", "ms_per_step": round(ms_two, 5),
+                          "gbs": round(kv / (ms_two * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(kv / (ms_two * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "decode_call_ms": round(dec_avg_ms, 5),
         "decode_call_hot": dist(dec_ms),
-        "decode_call_cold": dist(cold_ms),
         "wall_s": round(wall, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "kernel": "pa_decode_append (decode_balanced_kernel + decode_balanced_reduce_kernel)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

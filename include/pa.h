@@ -126,9 +126,13 @@ int pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mappi
 /*
  * Partition size pa_decode uses for `partition_size_request`
  * (0 = automatic, < 0 = one partition per sequence, > 0 = that many tokens,
- * a multiple of 16).  Returns the resolved size in tokens, or a negative
- * pa_status.  The automatic choice depends on the current device's compute
- * unit count and on the shape.
+ * a multiple of 16).  Returns the resolved size in tokens, 0 when the call
+ * runs the work-balanced schedule instead (an automatic call with fewer
+ * than 4 (sequence, kv head) pairs per compute unit, at most 1024 sequences
+ * and a context that would be split: the blocks of all sequences are cut
+ * into equal ranges, one per resident workgroup, and the pieces of a
+ * sequence are merged), or a negative pa_status.  The automatic choice
+ * depends on the current device's compute unit count and on the shape.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size_request);
@@ -160,7 +164,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   partition_size 0 = automatic split-K, < 0 = no split, > 0 = tokens per
  *                  partition (multiple of 16).  Long contexts are split into
  *                  partitions whose partial softmax states are merged by a
- *                  second kernel with the same rescaling identity.
+ *                  second kernel with the same rescaling identity.  The
+ *                  automatic choice may be the work-balanced schedule (see
+ *                  pa_decode_partition_size), whose pieces are merged the
+ *                  same way.
  *   workspace      device scratch of pa_decode_workspace_bytes(...) bytes
  *                  (may be NULL when that is 0).  Contents need no
  *                  initialisation and are overwritten; two calls in flight at
@@ -176,6 +183,37 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
               int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
               size_t workspace_bytes, const pa_cache_desc* desc, void* stream);
+
+/*
+ * pa_decode_append — one decode step of a layer in one launch: the cache
+ * write of every sequence's newest token (pa_reshape_and_cache of k, v,
+ * slot_mapping with num_tokens = num_seqs) fused with pa_decode over the
+ * updated pools (zihan-zhang.net vLLM study, 3.2: each step appends the new
+ * token's K/V to its sequence's last block, then attends over all blocks).
+ *
+ *   k, v           device [num_seqs][Hkv][D], the q dtype (bf16 for
+ *                  PA_FP8_E4M3 pools, encoded as pa_reshape_and_cache does):
+ *                  row s is sequence s's newest token
+ *   slot_mapping   device int64 [num_seqs]; slot of row s, negative = none
+ *   context_lens   count the newest token (position context_lens[s] - 1)
+ * The other arguments, the workspace rules and the supported variants are
+ * pa_decode's.  Contract: for every s with slot_mapping[s] >= 0,
+ * context_lens[s] >= 1 and slot_mapping[s] is position context_lens[s] - 1
+ * of the sequence, i.e. block_tables[s][(ctx-1)/16] * 16 + (ctx-1) % 16, and
+ * no other row's context holds that slot.  Then the pools end bit-identical
+ * to pa_reshape_and_cache's and out equals pa_decode's over them up to the
+ * order of fp32 sums (the newest token's K/V are taken from k, v instead of
+ * being read back; its softmax term is added after the other tokens').
+ * Rows with context 0 are not written.  Outside the contract the pools are
+ * written as pa_reshape_and_cache writes them (slots in range) but out is
+ * unspecified.
+ */
+int pa_decode_append(void* out, const void* q, const void* k, const void* v,
+                     const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                     int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
+                     size_t workspace_bytes, const pa_cache_desc* desc, void* stream);
 
 /*
  * pa_decode_shared_prefix — pa_decode for sequences that share a prompt

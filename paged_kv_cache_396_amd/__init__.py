@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     pa_cache_bytes,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_append,
     pa_decode_partition_size,
     pa_decode_shared_prefix,
     pa_decode_shared_prefix_workspace_bytes,

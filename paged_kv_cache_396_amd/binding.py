@@ -77,6 +77,9 @@ def lib():
         L.pa_decode_workspace_bytes.restype = sz
         L.pa_decode.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, f32, i32, P, sz, D, P]
         L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_append.argtypes = [P, P, P, P, P, P, P, P, i32, P, i32, i32, i32, f32, i32, P,
+                                       sz, D, P]
+        L.pa_decode_append.restype = ctypes.c_int
         L.pa_decode_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.pa_decode_shared_prefix_workspace_bytes.restype = sz
         L.pa_decode_shared_prefix.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, f32, P, i32, i32,
@@ -214,6 +217,35 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
                            block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq,
                            float(scale), int(partition_size), _ptr(workspace), ws_bytes,
                            ctypes.byref(desc), _stream(stream)))
+
+
+def pa_decode_append(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                     max_context_len: int, scale: float, desc: CacheDesc, partition_size: int = 0,
+                     workspace=None, stream=None):
+    """One decode step in one launch: ``k``/``v`` [S, Hkv, D] are the sequences'
+    newest tokens, written to ``slot_mapping`` (int64 [S]) and attended to
+    together with the rest of each context."""
+    torch = _torch()
+    for t, n in ((out, "out"), (q, "q"), (k, "k"), (v, "v"), (slot_mapping, "slot_mapping"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens")):
+        _dev(t, n)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    S, Hq, _ = q.shape
+    if k.shape[0] != S or v.shape[0] != S or slot_mapping.shape[0] != S:
+        raise ValueError("k, v and slot_mapping need one row per sequence")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_append(
+        _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq,
+        float(scale), int(partition_size), _ptr(workspace), ws_bytes, ctypes.byref(desc),
+        _stream(stream)))
 
 
 def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -141,28 +141,7 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
 // the rounding below are the readings taken for it.  An incoming bf16 value
 // x becomes the E4M3 code nearest to x / scale (one correctly rounded fp32
 // division), ties to the even code, magnitudes beyond 448 saturating; a NaN
-// becomes 0x7F with x's sign bit.
-
-// Four bf16 values (two words, element order lo, hi, lo, hi) -> one word of
-// four codes, element i in byte i.
-__device__ inline uint32_t quantize4(uint32_t w0, uint32_t w1, float scale) {
-  const float x[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
-  float c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(x[i] / scale, -448.f), 448.f);
-  // the conversion rounds to nearest even; the clamp keeps it in range
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], r, true);
-  uint32_t keep = 0xffffffffu, nan = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (x[i] != x[i]) {
-      keep &= ~(0xffu << (8 * i));
-      nan |= (0x7fu | ((__float_as_uint(x[i]) >> 31) << 7)) << (8 * i);
-    }
-  }
-  return ((uint32_t)r & keep) | nan;
-}
+// becomes 0x7F with x's sign bit (quantize4).
 
 // One workgroup takes 16 consecutive input tokens of one kv head, as the
 // bf16/fp32 kernel does.  Input chunk c (8 bf16 of one token) becomes 8 codes.

@@ -129,6 +129,17 @@ struct DecodeParams {
   int prefix_partition;        // tokens per prefix partition
   int max_prefix;              // prefix tokens the prefix kernel covers at most
   int ws_stride;               // partial slots per row
+  // balanced schedule only
+  int num_ranges;              // ranges per kv head the grid offers
+  int max_ctx;                 // host bound on every context length
+  // fused append (pa_decode_append) only: row s of new_k / new_v (q dtype,
+  // [num_seqs][num_kv_heads][D]) is sequence s's newest token, written to
+  // pool slot new_slots[s]; null when the call appends nothing
+  const char* new_k;
+  const char* new_v;
+  const int64_t* new_slots;
+  float k_quant_scale;         // fp8 pools: the pools' scales for encoding
+  float v_quant_scale;
 };
 
 // Shared tokens of sequence s's group, clamped to its context and rounded
@@ -474,6 +485,86 @@ struct WaveDecoder {
 
   static __device__ constexpr int head_lane(int h) { return (h * C::HEAD_SPAN) << C::AR; }
   __device__ int dim_of(int x) const { return vdim0 + (kWave / C::VCPR) * x; }
+
+  // ---- fused append: one new token's K and V rows in the register layout
+  // of a tile (knew[u]: K chunk u of the lane; vnew[i]: the element of the
+  // dim of V chunk i), encoded as the pool stores them.
+  __device__ void load_new_row(const char* krow, const char* vrow, float ksc, float vsc,
+                               uint4 (&knew)[C::U], uint32_t (&vnew)[C::NV]) const {
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      const int ch = u * C::LPR + c;  // 16-byte chunk of the pool row
+      if constexpr (EB == 1) {
+        // 16 codes from 16 bf16 inputs
+        const uint4 a = *(const uint4*)(krow + ch * 32);
+        const uint4 b = *(const uint4*)(krow + ch * 32 + 16);
+        knew[u] = make_uint4(quantize4(a.x, a.y, ksc), quantize4(a.z, a.w, ksc),
+                             quantize4(b.x, b.y, ksc), quantize4(b.z, b.w, ksc));
+      } else {
+        knew[u] = *(const uint4*)(krow + ch * 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::NV; ++i) {
+      const int dim = (lane + kWave * i) / C::VCPR;
+      if constexpr (EB == 1)
+        vnew[i] = quantize4(*(const uint16_t*)(vrow + dim * 2), 0u, vsc) & 0xffu;
+      else if constexpr (EB == 2)
+        vnew[i] = *(const uint16_t*)(vrow + dim * 2);
+      else
+        vnew[i] = *(const uint32_t*)(vrow + dim * 4);
+    }
+  }
+
+  // Keeps the new row in this wave's LDS stash: K chunks in pool order, one
+  // V element (low bits of a word) per dim.
+  __device__ void stash_new_row(uint4* sk, uint32_t* sv, const uint4 (&knew)[C::U],
+                                const uint32_t (&vnew)[C::NV]) const {
+    if (r == 0) {
+#pragma unroll
+      for (int u = 0; u < C::U; ++u) sk[u * C::LPR + c] = knew[u];
+    }
+    if (vpart == 0) {
+#pragma unroll
+      for (int i = 0; i < C::NV; ++i) sv[(lane + kWave * i) / C::VCPR] = vnew[i];
+    }
+  }
+
+  // A tile whose token 0 is the stashed row (the other tokens are zeros and
+  // are masked by the caller's nvalid = 1).
+  __device__ void stashed_tile(const uint4* sk, const uint32_t* sv, uint4 (&kt)[C::NR][C::U],
+                               uint4 (&vt)[C::NV]) const {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::NR; ++i)
+#pragma unroll
+      for (int u = 0; u < C::U; ++u) kt[i][u] = (r == 0 && i == 0) ? sk[u * C::LPR + c] : z;
+#pragma unroll
+    for (int i = 0; i < C::NV; ++i)
+      vt[i] = vpart == 0 ? make_uint4(sv[(lane + kWave * i) / C::VCPR], 0, 0, 0) : z;
+  }
+
+  // Stores the new row to offset o of the (block, kv head) tiles at kt / vt.
+  __device__ void store_new_row(char* kt, char* vt, int o, const uint4 (&knew)[C::U],
+                                const uint32_t (&vnew)[C::NV]) const {
+    if (r == 0) {
+#pragma unroll
+      for (int u = 0; u < C::U; ++u) *(uint4*)(kt + o * C::RB + (u * C::LPR + c) * 16) = knew[u];
+    }
+    if (vpart == 0) {
+#pragma unroll
+      for (int i = 0; i < C::NV; ++i) {
+        const int dim = (lane + kWave * i) / C::VCPR;
+        char* dst = vt + ((int64_t)dim * kBlock + o) * EB;
+        if constexpr (EB == 1)
+          *(uint8_t*)dst = (uint8_t)vnew[i];
+        else if constexpr (EB == 2)
+          *(uint16_t*)dst = (uint16_t)vnew[i];
+        else
+          *(uint32_t*)dst = vnew[i];
+      }
+    }
+  }
 };
 
 // Occupancy target (waves per SIMD) the register allocator must meet.
@@ -500,71 +591,57 @@ constexpr int decode_slots() {
   return EB == 1 ? PA_DECODE_SLOTS_FP8 : 2;
 }
 
-// CASC: shared-prefix decode.  The workgroup covers a partition of the
-// sequence's own blocks only (those after its group's shared prefix) and
-// always leaves a partial state for the merge.
-template <int EB, int D, int G, bool CASC = false>
-__global__ __launch_bounds__(kDecodeWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<EB, D, G>())))
-void decode_partition_kernel(DecodeParams p) {
+// LDS of one decode workgroup: the waves' probability exchange buffers and
+// their (m, l, O) for the final merge.
+template <int EB, int D, int G>
+struct DecodeLds {
+  using C = DecodeCfg<EB, D, G>;
+  __attribute__((aligned(16))) uint32_t pbuf[kDecodeWaves][8 * G * C::PWORDS];
+  float sm[kDecodeWaves][G];
+  float sl[kDecodeWaves][G];
+  __attribute__((aligned(16))) float so[kDecodeWaves][G][D];
+  // fused append: each wave's copy of the newest token's K row (pool
+  // encoding) and V elements
+  uint4 newk[kDecodeWaves][C::RB / 16];
+  uint32_t newv[kDecodeWaves][D];
+};
+
+// Streams blocks [b0, b1) of one sequence (ctx tokens, block table row bt)
+// for kv head g through wave w's register tile ring: the wave takes blocks
+// b0 + w, b0 + w + NW, ...  On entry my_ids holds, one per lane, the ids of
+// blocks b0 + w + NW * lane (or anything for blocks at or past b1), fetched
+// by the caller so that the fetch overlaps its other loads.
+// Fused append: when `s` is not negative, b1 is the sequence's last block
+// and row s of the new rows is its newest token, at position ctx - 1.  The
+// wave that takes that block loads the token's rows with its first block
+// ids, stores them to the token's slot (unless write_row is false: then a
+// later kernel of the call writes them) and keeps a copy in LDS.  If the slot
+// is row tn = (ctx - 1) % 16 of that block (the case the contract asks
+// for), the block is scored without its pool row tn, and after the last
+// block the token is scored from the LDS copy as a one-token tile: the same
+// set of tokens as a decode over the written pool, with no read of the
+// written row in this launch.
+template <int EB, int D, int G>
+__device__ inline void stream_blocks(WaveDecoder<EB, D, G>& wd, DecodeLds<EB, D, G>& lds,
+                                     const DecodeParams& p, const int32_t* bt, int g, int w,
+                                     int b0, int b1, int ctx, int my_ids, int s = -1,
+                                     bool write_row = true) {
   using C = DecodeCfg<EB, D, G>;
   constexpr int NW = kDecodeWaves;
-
-  __shared__ __attribute__((aligned(16))) uint32_t pbuf[NW][8 * G * C::PWORDS];
-  __shared__ float sm[NW][G];
-  __shared__ float sl[NW][G];
-  __shared__ __attribute__((aligned(16))) float so[NW][G][D];
-
-  const int bid = blockIdx.x;
-  const int g = bid % p.num_kv_heads;
-  const int s = (bid / p.num_kv_heads) % p.num_seqs;
-  // partitions past the first exist only for the longer sequences: they are
-  // dispatched first, so the last workgroups to start are first partitions,
-  // which every (sequence, kv head) has and which even out the tail
-  const int part = p.num_partitions - 1 - bid / (p.num_kv_heads * p.num_seqs);
-
-  // wave index, provably uniform so that loop control stays scalar
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  WaveDecoder<EB, D, G> wd;
-  wd.init(pbuf[w], p.scale_log2);
   const int lane = wd.lane;
-  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-
-  int b0, ctx, nblk, nparts, pre = 0;
-  int my_ids;  // id of block b0 + w + NW*(c0 + lane) for the current chunk c0
-  if constexpr (!CASC) {
-    b0 = part * p.partition_blocks;
-    // The first block ids of this wave and q do not depend on the context
-    // length: issue them together with its load, so the first KV tile waits
-    // on one memory round trip instead of two.
-    {
-      const int jb = b0 + w + NW * lane;
-      my_ids = jb < min(p.max_blocks_per_seq, b0 + p.partition_blocks) ? bt[jb] : 0;
-    }
-    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::QRB, wd.qv);
-    ctx = clamp_ctx(p.context_lens[s], p);
-    nblk = (ctx + kBlock - 1) / kBlock;
-    nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
-  } else {
-    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::QRB, wd.qv);
-    ctx = max(0, min(p.context_lens[s], p.max_blocks_per_seq * kBlock));
-    const int pl = prefix_of(p, s, ctx);
-    pre = prefix_parts(p, pl);
-    // own blocks [pl / 16, nblk), cut into at most num_partitions partitions
-    nblk = min((ctx + kBlock - 1) / kBlock, pl / kBlock + p.num_partitions * p.partition_blocks);
-    ctx = min(ctx, nblk * kBlock);
-    const int own = nblk - pl / kBlock;
-    nparts = own == 0 ? 1 : (own + p.partition_blocks - 1) / p.partition_blocks;
-    b0 = pl / kBlock + part * p.partition_blocks;
-    const int jb = b0 + w + NW * lane;
-    my_ids = jb < min(nblk, b0 + p.partition_blocks) ? bt[jb] : 0;
-  }
-  if (part >= nparts) return;  // uniform over the workgroup
-  const int b1 = min(nblk, b0 + p.partition_blocks);
-  wd.reset();
-
   const int64_t tile_bytes = (int64_t)kBlock * C::RB;
 
+  const bool app = s >= 0 && w == (b1 - 1 - b0) % NW;  // uniform
+  const int tn = (ctx - 1) & (kBlock - 1);
+  int64_t slot = -1, slot_in = -1;
+  bool hit = false;  // the last block was scored without its row tn
+  uint4 knew[C::U];
+  uint32_t vnew[C::NV];
+  if (app) {
+    const int64_t row = ((int64_t)s * p.num_kv_heads + g) * C::QRB;
+    slot_in = p.new_slots[s];
+    wd.load_new_row(p.new_k + row, p.new_v + row, p.k_quant_scale, p.v_quant_scale, knew, vnew);
+  }
   // block ids of this wave's blocks, one per lane, refreshed every 64 blocks
   auto fetch_ids = [&](int n0) {
     const int jb = b0 + w + NW * (n0 + lane);
@@ -582,20 +659,41 @@ void decode_partition_kernel(DecodeParams p) {
 
   auto process = [&](uint4 (&kc)[C::NR][C::U], uint4 (&vc)[C::NV], int id_cur, int n) {
     const int jblk = b0 + w + NW * n;
-    const int nvalid = id_ok(id_cur) ? min(kBlock, ctx - jblk * kBlock) : 0;
+    int nvalid = id_ok(id_cur) ? min(kBlock, ctx - jblk * kBlock) : 0;
+    if (app && jblk == b1 - 1 && nvalid == tn + 1 && (int64_t)id_cur * kBlock + tn == slot) {
+      nvalid = tn;  // the token itself comes from the LDS copy
+      hit = true;
+    }
     wd.process(kc, vc, nvalid);
   };
 
   // Blocks are taken in chunks of 64 (one block id per lane).  NS register
   // slots rotate: while one tile is computed the next NS - 1 are in flight.
   // The loads are unconditional (a tile past the chunk's end is an empty
-  // descriptor), so the wait before each tile is a static count.
-  for (int c0 = 0; c0 < nmine; c0 += 64) {
-    const int cnt = min(64, nmine - c0);
-    if (c0 > 0) fetch_ids(c0);
-    auto id_at = [&](int i) { return __builtin_amdgcn_readlane(my_ids, min(i, cnt - 1)); };
+  // descriptor), so the wait before each tile is a static count.  The first
+  // chunk's first loads are issued before the loop, and the appended row's
+  // registers die before it.
+  int cnt = min(64, nmine);
+  auto id_at = [&](int i) { return __builtin_amdgcn_readlane(my_ids, min(i, cnt - 1)); };
+  auto prologue = [&]() {
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t) load_tile(id_at(t), t < cnt && id_ok(id_at(t)), kb[t], vb[t]);
+  };
+  if (app) {
+    // the new row was loaded right after the block ids, which the first
+    // tile loads wait for anyway: write it out and keep a copy before them
+    // (after them, the wait for the row would also cover the first tile)
+    slot = ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot_in >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)slot_in);
+    if (write_row && slot >= 0 && slot < (int64_t)p.num_blocks * kBlock) {
+      const int64_t base = (slot / kBlock * p.num_kv_heads + g) * tile_bytes;
+      wd.store_new_row((char*)p.k_cache + base, (char*)p.v_cache + base, (int)(slot % kBlock),
+                       knew, vnew);
+    }
+    wd.stash_new_row(lds.newk[w], lds.newv[w], knew, vnew);
+  }
+  if (nmine > 0) prologue();
+  for (int c0 = 0; c0 < nmine;) {
     for (int n = 0; n < cnt; n += NS) {
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl) {
@@ -604,40 +702,58 @@ void decode_partition_kernel(DecodeParams p) {
         if (n + sl < cnt) process(kb[sl], vb[sl], id_at(n + sl), c0 + n + sl);
       }
     }
+    c0 += 64;
+    if (c0 >= nmine) break;
+    cnt = min(64, nmine - c0);
+    fetch_ids(c0);
+    prologue();
   }
+  if (hit) {
+    wd.stashed_tile(lds.newk[w], lds.newv[w], kb[0], vb[0]);
+    wd.process(kb[0], vb[0], 1);
+  }
+}
 
-  // ---- wave totals
+// Wave totals, then the merge of the NW waves' (m, l, O) in LDS with the
+// online-softmax rescale.  With `single` the workgroup writes the normalised
+// output rows of (sequence s, kv head g); otherwise query head h of the group
+// leaves its partial state in workspace slot base + h * stride.  Ends with the
+// LDS still in use: the caller syncs before the next tile of work.
+template <int EB, int D, int G>
+__device__ inline void finish_waves(WaveDecoder<EB, D, G>& wd, DecodeLds<EB, D, G>& lds,
+                                    const DecodeParams& p, int w, int s, int g, bool single,
+                                    int64_t base, int64_t stride) {
+  using C = DecodeCfg<EB, D, G>;
+  constexpr int NW = kDecodeWaves;
+  const int lane = wd.lane;
   const float l_head = wd.totals();
   if ((lane & (C::ROW_BITS | C::HEAD_BITS | C::DUP_BITS)) == 0) {
-    sm[w][wd.hh] = wd.m_mine;
-    sl[w][wd.hh] = l_head;
+    lds.sm[w][wd.hh] = wd.m_mine;
+    lds.sl[w][wd.hh] = l_head;
   }
   if (wd.vpart == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int x = 0; x < C::NV; ++x) so[w][h][wd.dim_of(x)] = wd.o[h][x];
+      for (int x = 0; x < C::NV; ++x) lds.so[w][h][wd.dim_of(x)] = wd.o[h][x];
   }
   __syncthreads();
 
-  // ---- merge the waves
-  const bool single = !CASC && nparts == 1;
   for (int e = threadIdx.x; e < G * D; e += NW * kWave) {
     const int h = e / D;
     const int x = e - h * D;
-    float M = sm[0][h];
+    float M = lds.sm[0][h];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm[ww][h]);
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, lds.sm[ww][h]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      const float f = exp2f(sm[ww][h] - M);
-      L = fmaf(sl[ww][h], f, L);
-      O = fmaf(so[ww][h][x], f, O);
+      const float f = exp2f(lds.sm[ww][h] - M);
+      L = fmaf(lds.sl[ww][h], f, L);
+      O = fmaf(lds.so[ww][h][x], f, O);
     }
-    const int hq = g * G + h;
-    const int64_t row = (int64_t)s * p.num_q_heads + hq;
     if (single) {
+      const int64_t row = (int64_t)s * p.num_q_heads + g * G + h;
       float val = L > 0.f ? O / L : 0.f;
       if constexpr (EB == 1) val *= p.v_scale;
       if constexpr (EB <= 2)
@@ -645,13 +761,357 @@ void decode_partition_kernel(DecodeParams p) {
       else
         ((float*)p.out)[row * D + x] = val;
     } else {
-      const int64_t slot = CASC ? row * p.ws_stride + pre + part : row * p.num_partitions + part;
+      const int64_t slot = base + h * stride;
       p.ws_o[slot * D + x] = O;
       if (x == 0) {
         p.ws_m[slot] = M;
         p.ws_l[slot] = L;
       }
     }
+  }
+}
+
+// CASC: shared-prefix decode.  The workgroup covers a partition of the
+// sequence's own blocks only (those after its group's shared prefix) and
+// always leaves a partial state for the merge.
+template <int EB, int D, int G, bool CASC = false>
+__global__ __launch_bounds__(kDecodeWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<EB, D, G>())))
+void decode_partition_kernel(DecodeParams p) {
+  constexpr int NW = kDecodeWaves;
+  __shared__ DecodeLds<EB, D, G> lds;
+
+  const int bid = blockIdx.x;
+  const int g = bid % p.num_kv_heads;
+  const int s = (bid / p.num_kv_heads) % p.num_seqs;
+  // partitions past the first exist only for the longer sequences: they are
+  // dispatched first, so the last workgroups to start are first partitions,
+  // which every (sequence, kv head) has and which even out the tail
+  const int part = p.num_partitions - 1 - bid / (p.num_kv_heads * p.num_seqs);
+
+  // wave index, provably uniform so that loop control stays scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  WaveDecoder<EB, D, G> wd;
+  wd.init(lds.pbuf[w], p.scale_log2);
+  const int lane = wd.lane;
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+
+  int b0, ctx, nblk, nparts, pre = 0;
+  int my_ids;  // id of block b0 + w + NW * lane
+  if constexpr (!CASC) {
+    b0 = part * p.partition_blocks;
+    // The first block ids of this wave and q do not depend on the context
+    // length: issue them together with its load, so the first KV tile waits
+    // on one memory round trip instead of two.
+    {
+      const int jb = b0 + w + NW * lane;
+      my_ids = jb < min(p.max_blocks_per_seq, b0 + p.partition_blocks) ? bt[jb] : 0;
+    }
+    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * DecodeCfg<EB, D, G>::QRB, wd.qv);
+    ctx = clamp_ctx(p.context_lens[s], p);
+    nblk = (ctx + kBlock - 1) / kBlock;
+    nparts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  } else {
+    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * DecodeCfg<EB, D, G>::QRB, wd.qv);
+    ctx = max(0, min(p.context_lens[s], p.max_blocks_per_seq * kBlock));
+    const int pl = prefix_of(p, s, ctx);
+    pre = prefix_parts(p, pl);
+    // own blocks [pl / 16, nblk), cut into at most num_partitions partitions
+    nblk = min((ctx + kBlock - 1) / kBlock, pl / kBlock + p.num_partitions * p.partition_blocks);
+    ctx = min(ctx, nblk * kBlock);
+    const int own = nblk - pl / kBlock;
+    nparts = own == 0 ? 1 : (own + p.partition_blocks - 1) / p.partition_blocks;
+    b0 = pl / kBlock + part * p.partition_blocks;
+    const int jb = b0 + w + NW * lane;
+    my_ids = jb < min(nblk, b0 + p.partition_blocks) ? bt[jb] : 0;
+  }
+  if (part >= nparts) return;  // uniform over the workgroup
+  const int b1 = min(nblk, b0 + p.partition_blocks);
+  wd.reset();
+  const bool append = !CASC && p.new_k != nullptr && b1 == nblk && ctx > 0;
+  stream_blocks(wd, lds, p, bt, g, w, b0, b1, ctx, my_ids, append ? s : -1);
+
+  const int64_t row0 = (int64_t)s * p.num_q_heads + g * G;
+  const int64_t stride = CASC ? p.ws_stride : p.num_partitions;
+  finish_waves(wd, lds, p, w, s, g, !CASC && nparts == 1, row0 * stride + pre + part, stride);
+}
+
+// ---------------------------------------------------------------------------
+// Work-balanced schedule.  For one kv head, the blocks of all sequences in
+// sequence order form one list of T = sum_s ceil(ctx_s / 16) entries.  The
+// list is cut into R ranges of equal length (entry j belongs to range
+// floor(j R / T)) and workgroup (range, kv head) reads exactly its range, so
+// every workgroup streams the same number of tiles whatever the mix of
+// context lengths and no long sequence leaves a tail of late workgroups.
+// A range holds pieces ("segments") of one or more sequences.  A sequence
+// that lies wholly inside a range is finished there; otherwise the range's
+// first segment (slot 0) or last segment (slot 1) leaves a partial state and
+// the merge kernel combines the pieces of the sequence, range by range.
+constexpr int kBalancedMinBlocks = 8;   // blocks a range holds at least
+
+// Ranges actually used for a list of T blocks when the grid offers R.
+__device__ inline int balanced_ranges(int R, int T) {
+  return max(1, min(R, (T + kBalancedMinBlocks - 1) / kBalancedMinBlocks));
+}
+__device__ inline int range_of(int j, int T, int R) { return (int)((int64_t)j * R / T); }
+__device__ inline int range_start(int w, int T, int R) {
+  return (int)(((int64_t)w * T + R - 1) / R);
+}
+// Tokens of a context that the balanced schedule reads: bounded by the table
+// row and by the host's bound on every context length.
+__device__ inline int balanced_ctx(int ctx, const DecodeParams& p) {
+  const int cap = min(p.max_blocks_per_seq * kBlock, p.max_ctx);
+  return max(0, min(ctx, cap));
+}
+
+template <int EB, int D, int G>
+__global__ __launch_bounds__(kDecodeWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<EB, D, G>())))
+void decode_balanced_kernel(DecodeParams p) {
+  using C = DecodeCfg<EB, D, G>;
+  constexpr int NW = kDecodeWaves;
+  constexpr int PER_THREAD = kBalancedMaxSeqs / (NW * kWave);
+  static_assert(PER_THREAD * NW * kWave == kBalancedMaxSeqs, "scan layout");
+  __shared__ DecodeLds<EB, D, G> lds;
+  __shared__ int cum[kBalancedMaxSeqs + 1];  // blocks before sequence s
+  __shared__ int sctx[kBalancedMaxSeqs];     // context of sequence s
+  __shared__ int wtot[NW];
+
+  const int g = blockIdx.x % p.num_kv_heads;
+  const int range = blockIdx.x / p.num_kv_heads;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int S = p.num_seqs;
+
+  // ---- block counts of every sequence and their exclusive prefix sums
+  const int sfirst = threadIdx.x * PER_THREAD;
+  int cl[PER_THREAD];
+  int run = 0;
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    cl[i] = sfirst + i < S ? balanced_ctx(p.context_lens[sfirst + i], p) : 0;
+    run += (cl[i] + kBlock - 1) / kBlock;
+  }
+  int inc = run;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  if (lane == kWave - 1) wtot[w] = inc;
+  __syncthreads();
+  int excl = inc - run, T = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    excl += ww < w ? wtot[ww] : 0;
+    T += wtot[ww];
+  }
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    if (sfirst + i < S) {
+      cum[sfirst + i] = excl;
+      sctx[sfirst + i] = cl[i];
+    }
+    excl += (cl[i] + kBlock - 1) / kBlock;
+  }
+  if (threadIdx.x == 0) cum[S] = T;
+  __syncthreads();
+
+  T = __builtin_amdgcn_readfirstlane(T);
+  if (T == 0) return;
+  const int R = balanced_ranges(p.num_ranges, T);
+  if (range >= R) return;
+  const int B0 = range_start(range, T, R);
+  const int B1 = range_start(range + 1, T, R);
+  if (B0 >= B1) return;
+  // first sequence of the range: the last s with cum[s] <= B0
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(cum[mid]) <= B0)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+
+  WaveDecoder<EB, D, G> wd;
+  wd.init(lds.pbuf[w], p.scale_log2);
+  for (int s = lo; s < S; ++s) {
+    const int cs = __builtin_amdgcn_readfirstlane(cum[s]);
+    const int ce = __builtin_amdgcn_readfirstlane(cum[s + 1]);
+    if (cs >= B1) break;
+    const int sb = max(B0, cs), se = min(B1, ce);
+    if (sb >= se) continue;  // a sequence with no blocks
+    const int ctx = __builtin_amdgcn_readfirstlane(sctx[s]);
+    const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+    const int b0 = sb - cs, b1 = se - cs;
+    const int jb = b0 + w + NW * lane;
+    const int my_ids = jb < b1 ? bt[jb] : 0;
+    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::QRB, wd.qv);
+    wd.reset();
+    // the new rows reach the pools in the merge kernel: a store here would
+    // hold up this wave's later tile waits until the store is acknowledged
+    const bool append = p.new_k != nullptr && se == ce && ctx > 0;
+    stream_blocks(wd, lds, p, bt, g, w, b0, b1, ctx, my_ids, append ? s : -1, false);
+    const bool whole = cs >= B0 && ce <= B1;
+    const int slot = sb == B0 ? 0 : 1;
+    finish_waves(wd, lds, p, w, s, g, whole,
+                 ((int64_t)(g * p.num_ranges + range) * 2 + slot) * G, 1);
+    __syncthreads();
+  }
+}
+
+// Fused append in the balanced schedule: one wave writes sequence s's
+// newest token for kv head g to its slot, encoded as the cache write encodes
+// it (a bit copy; E4M3 codes for fp8 pools).  Rows whose context is empty
+// or whose slot is negative or outside the pool are not written.
+template <int EB, int D>
+__device__ inline void write_new_row(const DecodeParams& p, int s, int g) {
+  constexpr int RB = D * EB;                   // pool bytes of one row
+  constexpr int QB = EB == 4 ? 4 : 2;          // bytes of an input element
+  const int lane = threadIdx.x;
+  const int64_t slot = p.new_slots[s];
+  const int ctx = balanced_ctx(p.context_lens[s], p);
+  const char* krow = p.new_k + ((int64_t)s * p.num_kv_heads + g) * D * QB;
+  const char* vrow = p.new_v + ((int64_t)s * p.num_kv_heads + g) * D * QB;
+  uint4 kc = make_uint4(0, 0, 0, 0);
+  if (lane < RB / 16) {
+    if constexpr (EB == 1) {
+      const uint4 a = *(const uint4*)(krow + lane * 32);
+      const uint4 b = *(const uint4*)(krow + lane * 32 + 16);
+      kc = make_uint4(quantize4(a.x, a.y, p.k_quant_scale), quantize4(a.z, a.w, p.k_quant_scale),
+                      quantize4(b.x, b.y, p.k_quant_scale), quantize4(b.z, b.w, p.k_quant_scale));
+    } else {
+      kc = *(const uint4*)(krow + lane * 16);
+    }
+  }
+  constexpr int XL = D / kWave;
+  uint32_t ve[XL];
+#pragma unroll
+  for (int e = 0; e < XL; ++e) {
+    const int dim = lane + e * kWave;
+    if constexpr (EB == 1)
+      ve[e] = quantize4(*(const uint16_t*)(vrow + dim * 2), 0u, p.v_quant_scale) & 0xffu;
+    else if constexpr (EB == 2)
+      ve[e] = *(const uint16_t*)(vrow + dim * 2);
+    else
+      ve[e] = *(const uint32_t*)(vrow + dim * 4);
+  }
+  if (ctx <= 0 || slot < 0 || slot >= (int64_t)p.num_blocks * kBlock) return;
+  const int64_t base = (slot / kBlock * p.num_kv_heads + g) * (int64_t)kBlock * RB;
+  const int o = (int)(slot % kBlock);
+  if (lane < RB / 16) *(uint4*)(p.k_cache + base + o * RB + lane * 16) = kc;
+#pragma unroll
+  for (int e = 0; e < XL; ++e) {
+    char* dst = (char*)p.v_cache + base + ((int64_t)(lane + e * kWave) * kBlock + o) * EB;
+    if constexpr (EB == 1)
+      *(uint8_t*)dst = (uint8_t)ve[e];
+    else if constexpr (EB == 2)
+      *(uint16_t*)dst = (uint16_t)ve[e];
+    else
+      *(uint32_t*)dst = ve[e];
+  }
+}
+
+// Merge of the balanced schedule: one wave per (sequence, query head).  The
+// wave recomputes the list position of the sequence's blocks, finds the
+// ranges that hold them and merges their partial states in range order with
+// the online-softmax rescale.  Sequences finished inside one range are left
+// alone; sequences without blocks get a zero row.
+// Workgroups past num_seqs * num_q_heads (launched for a fused append) each
+// write one (sequence, kv head)'s new row; the merge waves do not wait on
+// those stores.
+template <int EB, int D>
+__global__ __launch_bounds__(kWave) void decode_balanced_reduce_kernel(DecodeParams p) {
+  if (blockIdx.x >= p.num_seqs * p.num_q_heads) {
+    const int r = blockIdx.x - p.num_seqs * p.num_q_heads;
+    write_new_row<EB, D>(p, r / p.num_kv_heads, r % p.num_kv_heads);
+    return;
+  }
+  const int s = blockIdx.x / p.num_q_heads;
+  const int hq = blockIdx.x - s * p.num_q_heads;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int g = hq / G;
+  const int h = hq - g * G;
+  const int lane = threadIdx.x;
+  const int64_t row = (int64_t)s * p.num_q_heads + hq;
+  constexpr int XL = D / kWave;  // dims per lane
+
+  int tot = 0, before = 0;
+  for (int i = lane; i < p.num_seqs; i += kWave) {
+    const int n = (balanced_ctx(p.context_lens[i], p) + kBlock - 1) / kBlock;
+    tot += n;
+    before += i < s ? n : 0;
+  }
+#pragma unroll
+  for (int m = kWave / 2; m > 0; m >>= 1) {
+    tot += __shfl_xor(tot, m);
+    before += __shfl_xor(before, m);
+  }
+  const int nb = (balanced_ctx(p.context_lens[s], p) + kBlock - 1) / kBlock;
+  if (nb == 0) {
+#pragma unroll
+    for (int e = 0; e < XL; ++e) {
+      const int x = lane + e * kWave;
+      if constexpr (EB <= 2)
+        ((uint16_t*)p.out)[row * D + x] = 0;
+      else
+        ((float*)p.out)[row * D + x] = 0.f;
+    }
+    return;
+  }
+  const int R = balanced_ranges(p.num_ranges, tot);
+  const int wf = range_of(before, tot, R);
+  const int wl = range_of(before + nb - 1, tot, R);
+  if (wf == wl) return;  // finished by the decode kernel
+  const int first_slot = before > range_start(wf, tot, R) ? 1 : 0;
+  const int nparts = wl - wf + 1;
+  auto slot_of = [&](int q) {
+    return ((int64_t)(g * p.num_ranges + wf + q) * 2 + (q == 0 ? first_slot : 0)) * G + h;
+  };
+
+  float acc[XL];
+#pragma unroll
+  for (int e = 0; e < XL; ++e) acc[e] = 0.f;
+  float L = 0.f, M = kNegBig;
+  constexpr int PG = 8;  // partial states loaded together
+  for (int q0 = 0; q0 < nparts; q0 += PG) {
+    float mq[PG], lq[PG], oq[PG][XL];
+#pragma unroll
+    for (int j = 0; j < PG; ++j) {
+      const int64_t sl = slot_of(min(q0 + j, nparts - 1));
+      mq[j] = p.ws_m[sl];
+      lq[j] = p.ws_l[sl];
+#pragma unroll
+      for (int e = 0; e < XL; ++e) oq[j][e] = p.ws_o[sl * D + lane + e * kWave];
+    }
+    float Mg = M;
+#pragma unroll
+    for (int j = 0; j < PG; ++j)
+      if (q0 + j < nparts) Mg = fmaxf(Mg, mq[j]);
+    const float r = exp2f(M - Mg);  // rescale of what was merged so far
+    L *= r;
+#pragma unroll
+    for (int e = 0; e < XL; ++e) acc[e] *= r;
+#pragma unroll
+    for (int j = 0; j < PG; ++j) {
+      const float f = q0 + j < nparts ? exp2f(mq[j] - Mg) : 0.f;
+      L = fmaf(lq[j], f, L);
+#pragma unroll
+      for (int e = 0; e < XL; ++e) acc[e] = fmaf(oq[j][e], f, acc[e]);
+    }
+    M = Mg;
+  }
+  float inv = L > 0.f ? 1.f / L : 0.f;
+  if constexpr (EB == 1) inv *= p.v_scale;
+#pragma unroll
+  for (int e = 0; e < XL; ++e) {
+    const float val = acc[e] * inv;
+    const int x = lane + e * kWave;
+    if constexpr (EB <= 2)
+      ((uint16_t*)p.out)[row * D + x] = to_bf16(val);
+    else
+      ((float*)p.out)[row * D + x] = val;
   }
 }
 
@@ -745,6 +1205,25 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
 
 template <int EB, int D, int G>
 static hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream) {
+  if (prm.num_ranges > 0) {
+    // one range per resident workgroup slot of this variant
+    static_assert(decode_waves_per_eu<EB, D, G>() <= kBalancedMaxWgPerCu, "workspace bound");
+    DecodeParams bp = prm;
+    bp.num_ranges = max(1, prm.num_ranges * decode_waves_per_eu<EB, D, G>() / kBalancedMaxWgPerCu);
+    const int64_t rows = (int64_t)bp.num_ranges * 2 * bp.num_q_heads;
+    bp.ws_l = bp.ws_m + rows;
+    bp.ws_o = bp.ws_m + 2 * rows;
+    hipLaunchKernelGGL((decode_balanced_kernel<EB, D, G>),
+                       dim3((unsigned)(bp.num_ranges * bp.num_kv_heads)),
+                       dim3(kDecodeWaves * kWave), 0, stream, bp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t writers = bp.new_k ? (int64_t)bp.num_seqs * bp.num_kv_heads : 0;
+    hipLaunchKernelGGL((decode_balanced_reduce_kernel<EB, D>),
+                       dim3((unsigned)(bp.num_seqs * bp.num_q_heads + writers)), dim3(kWave), 0,
+                       stream, bp);
+    return hipGetLastError();
+  }
   const int64_t grid = (int64_t)prm.num_partitions * prm.num_seqs * prm.num_kv_heads;
   hipLaunchKernelGGL((decode_partition_kernel<EB, D, G>), dim3((unsigned)grid),
                      dim3(kDecodeWaves * kWave), 0, stream, prm);
@@ -818,10 +1297,19 @@ hipError_t launch_decode(const DecodeArgs& a, const CacheGeom& g, hipStream_t st
   p.v_cache = (const char*)a.v_cache;
   p.block_tables = a.block_tables;
   p.context_lens = a.context_lens;
+  // partial slots (seq, q head, partition): m, l, then o (the balanced
+  // schedule lays out its own (kv head, range, 2, group head) slots)
   const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads * a.num_partitions;
   p.ws_m = a.ws;
   p.ws_l = a.ws ? a.ws + rows : nullptr;
   p.ws_o = a.ws ? a.ws + 2 * rows : nullptr;
+  p.num_ranges = a.num_ranges;
+  p.max_ctx = a.max_ctx;
+  p.new_k = (const char*)a.new_k;
+  p.new_v = (const char*)a.new_v;
+  p.new_slots = a.new_slots;
+  p.k_quant_scale = g.k_scale;
+  p.v_quant_scale = g.v_scale;
   p.max_blocks_per_seq = a.max_blocks_per_seq;
   p.num_seqs = a.num_seqs;
   p.num_q_heads = a.num_q_heads;

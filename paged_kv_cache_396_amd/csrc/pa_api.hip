@@ -118,6 +118,39 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ct
   return part >= whole ? whole : part;
 }
 
+// Upper bound on the ranges per kv head of the balanced schedule (it sizes
+// the workspace), or 0 for per-partition workgroups.  The balanced schedule
+// serves automatic calls that the rule above would split (few (sequence, kv
+// head) units for the chip): it gives every workgroup the same number of
+// blocks however unequal the contexts.  The launch takes one range per
+// resident workgroup slot of the kernel variant (at most
+// kBalancedMaxWgPerCu per compute unit) times kBalancedRounds.
+int32_t balanced_ranges(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx, int32_t req) {
+  if (req != 0 || num_seqs < 1 || num_seqs > pa::kBalancedMaxSeqs || num_kv_heads < 1 ||
+      pa::kBalancedRounds < 1)
+    return 0;
+  const int32_t whole = max_ctx < 16 ? 16 : round_up16(max_ctx);
+  if (resolve_partition(num_seqs, num_kv_heads, max_ctx, 0) >= whole) return 0;
+  // block-list positions are int32 on the device
+  if ((int64_t)num_seqs * (((int64_t)max_ctx + 15) / 16) >= ((int64_t)1 << 31)) return 0;
+  const int64_t r =
+      (int64_t)device_cu_count() * pa::kBalancedMaxWgPerCu * pa::kBalancedRounds / num_kv_heads;
+  return (int32_t)(r < 1 ? 1 : r);
+}
+
+// Workspace bytes of a decode call: partial states of (kv head, range, 2,
+// group head) for the balanced schedule, of (seq, q head, partition)
+// otherwise; 0 when nothing is split.
+size_t decode_ws_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_ctx, int32_t req) {
+  const int32_t ranges = balanced_ranges(num_seqs, num_kv_heads, max_ctx, req);
+  if (ranges > 0) return (size_t)ranges * 2 * num_q_heads * (head_dim + 2) * sizeof(float);
+  const int32_t part = resolve_partition(num_seqs, num_kv_heads, max_ctx, req);
+  const int64_t nparts = ((int64_t)max_ctx + part - 1) / part;
+  if (nparts <= 1) return 0;
+  return (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
+}
+
 }  // namespace
 
 PA_API int pa_abi_version(void) { return PA_ABI_VERSION; }
@@ -154,6 +187,8 @@ PA_API int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
   if (partition_size_request > 0 && partition_size_request % PA_BLOCK_SIZE != 0)
     return fail(PA_ERR_SHAPE, "partition_size %d is not a multiple of 16",
                 (int)partition_size_request);
+  if (balanced_ranges(num_seqs, num_kv_heads, max_context_len, partition_size_request) > 0)
+    return 0;
   return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size_request);
 }
 
@@ -164,18 +199,19 @@ PA_API size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, i
       max_context_len < 0)
     return 0;
   if (partition_size_request > 0 && partition_size_request % PA_BLOCK_SIZE != 0) return 0;
-  const int32_t part = resolve_partition(num_seqs, num_kv_heads, max_context_len,
-                                         partition_size_request);
-  const int64_t nparts = ((int64_t)max_context_len + part - 1) / part;
-  if (nparts <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
+  return decode_ws_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                         partition_size_request);
 }
 
-PA_API int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                     const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
-                     int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
-                     size_t workspace_bytes, const pa_cache_desc* desc, void* stream) {
+namespace {
+
+// pa_decode, and pa_decode_append when new_k is not null.
+int decode_call(void* out, const void* q, const void* new_k, const void* new_v,
+                const int64_t* new_slots, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
+                size_t workspace_bytes, const pa_cache_desc* desc, void* stream) {
   pa::CacheGeom g;
   int st = check_desc(desc, &g);
   if (st != PA_OK) return st;
@@ -194,15 +230,19 @@ PA_API int pa_decode(void* out, const void* q, const void* k_cache, const void* 
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_NULL, "out, q, k_cache, v_cache, block_tables and context_lens must be non-NULL");
+  if (new_k && (!new_v || !new_slots))
+    return fail(PA_ERR_NULL, "k, v and slot_mapping must be non-NULL");
   const int32_t part = resolve_partition(num_seqs, g.num_kv_heads, max_context_len, partition_size);
   int64_t nparts = ((int64_t)max_context_len + part - 1) / part;
   if (nparts < 1) nparts = 1;
   if (nparts * num_seqs * g.num_kv_heads >= ((int64_t)1 << 31) ||
       (int64_t)num_seqs * num_q_heads >= ((int64_t)1 << 31))
     return fail(PA_ERR_OVERFLOW, "decode grid too large");
+  const int32_t ranges = balanced_ranges(num_seqs, g.num_kv_heads, max_context_len, partition_size);
   float* ws = nullptr;
-  if (nparts > 1) {
-    const size_t need = (size_t)num_seqs * num_q_heads * nparts * (g.head_dim + 2) * sizeof(float);
+  if (nparts > 1 || ranges > 0) {
+    const size_t need = decode_ws_bytes(num_seqs, num_q_heads, g.num_kv_heads, g.head_dim,
+                                        max_context_len, partition_size);
     if (!workspace || workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given (ptr %p)", need,
                   workspace_bytes, workspace);
@@ -222,9 +262,40 @@ PA_API int pa_decode(void* out, const void* q, const void* k_cache, const void* 
   a.num_partitions = (int)nparts;
   a.partition_blocks = part / PA_BLOCK_SIZE;
   a.scale = scale;
+  a.num_ranges = ranges;
+  a.max_ctx = max_context_len;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.new_slots = new_slots;
   hipError_t e = pa::launch_decode(a, g, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+}  // namespace
+
+PA_API int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                     int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
+                     size_t workspace_bytes, const pa_cache_desc* desc, void* stream) {
+  return decode_call(out, q, nullptr, nullptr, nullptr, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                     scale, partition_size, workspace, workspace_bytes, desc, stream);
+}
+
+PA_API int pa_decode_append(void* out, const void* q, const void* k, const void* v,
+                            const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len,
+                            int32_t num_seqs, int32_t num_q_heads, float scale,
+                            int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            const pa_cache_desc* desc, void* stream) {
+  if (num_seqs > 0 && (!k || !v || !slot_mapping))
+    return fail(PA_ERR_NULL, "k, v and slot_mapping must be non-NULL");
+  return decode_call(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                     scale, partition_size, workspace, workspace_bytes, desc, stream);
 }
 
 namespace {

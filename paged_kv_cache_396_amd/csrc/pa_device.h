@@ -46,6 +46,31 @@ __device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
+// E4M3 encoding of bf16 values for fp8 pools (code c stands for value(c) *
+// scale): the code nearest to x / scale (one correctly rounded fp32
+// division), ties to the even code, magnitudes beyond 448 saturating; a NaN
+// becomes 0x7F with x's sign bit.
+// Four bf16 values (two words, element order lo, hi, lo, hi) -> one word of
+// four codes, element i in byte i.
+__device__ inline uint32_t quantize4(uint32_t w0, uint32_t w1, float scale) {
+  const float x[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(x[i] / scale, -448.f), 448.f);
+  // the conversion rounds to nearest even; the clamp keeps it in range
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], r, true);
+  uint32_t keep = 0xffffffffu, nan = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (x[i] != x[i]) {
+      keep &= ~(0xffu << (8 * i));
+      nan |= (0x7fu | ((__float_as_uint(x[i]) >> 31) << 7)) << (8 * i);
+    }
+  }
+  return ((uint32_t)r & keep) | nan;
+}
+
 // a.lo*b.lo + a.hi*b.hi + c with bf16 inputs and fp32 accumulation.
 __device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),

@@ -37,7 +37,29 @@ struct DecodeArgs {
   int num_partitions;   // per sequence, grid extent
   int partition_blocks; // blocks per partition
   float scale;
+  // > 0: balanced schedule (num_partitions and partition_blocks unused) whose
+  // workspace holds 2 * num_ranges * num_q_heads partial slots; the launch
+  // uses num_ranges * (resident workgroups per CU) / kBalancedMaxWgPerCu
+  // ranges per kv head
+  int num_ranges = 0;
+  int max_ctx = 0;      // host bound on every context length
+  // fused append: row s of new_k / new_v ([num_seqs][Hkv][D], q dtype) is
+  // sequence s's newest token, written to slot new_slots[s]; null: none
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
+  const int64_t* new_slots = nullptr;
 };
+
+// Sequences the balanced schedule supports in one call (one workgroup scans
+// all their block counts in LDS).
+constexpr int kBalancedMaxSeqs = 1024;
+// Resident decode workgroups per compute unit of any kernel variant (at
+// most), and workgroups per resident slot of the balanced schedule.
+constexpr int kBalancedMaxWgPerCu = 4;
+#ifndef PA_BALANCED_ROUNDS
+#define PA_BALANCED_ROUNDS 1
+#endif
+constexpr int kBalancedRounds = PA_BALANCED_ROUNDS;
 
 // True if (dtype, head_dim, group) has a compiled decode kernel.
 bool decode_supported(int elem_bytes, int head_dim, int group);

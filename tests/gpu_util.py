@@ -127,6 +127,29 @@ def gpu_decode(wl, pool, partition_size=0, context_lens=None, max_ctx=None, work
     return out
 
 
+def gpu_decode_append(wl, pool, partition_size=0, slots=None, workspace=None, qdtype=None):
+    """pa_decode_append of the workload's newest tokens (wl.new_k / new_v at
+    wl.new_slots, or ``slots``) on a pool that holds the history only."""
+    t = torch()
+    qd = wl.dtype if qdtype is None else qdtype
+    q = to_dev(wl.q, qd)
+    out = t.empty_like(q)
+    k = to_dev(wl.new_k, qd)
+    v = to_dev(wl.new_v, qd)
+    sl = t.from_numpy(np.ascontiguousarray(wl.new_slots if slots is None else slots,
+                                           dtype=np.int64)).cuda()
+    bt = t.from_numpy(np.ascontiguousarray(wl.block_tables)).cuda()
+    cl = t.from_numpy(np.ascontiguousarray(wl.context_lens, dtype=np.int32)).cuda()
+    maxctx = int(wl.context_lens.max())
+    S, Hq, D = wl.q.shape
+    ws = workspace if workspace is not None else decode_workspace(S, Hq, wl.num_kv_heads, D, maxctx,
+                                                                   partition_size)
+    pa.pa_decode_append(out, q, k, v, sl, pool.k, pool.v, bt, cl, maxctx, float(wl.scale),
+                        pool.desc, partition_size=partition_size, workspace=ws)
+    t.cuda.synchronize()
+    return out
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"

@@ -225,3 +225,37 @@ def test_split_k_workspace_reused_across_calls():
         out = to_f64(gpu_decode(wl, pool, partition_size=256, context_lens=shorter, max_ctx=3000,
                                 workspace=ws))
         assert_close(out, ref_short, "bf16", f"shorter call {it}")
+
+
+# ---- the work-balanced schedule (automatic calls with few (sequence, kv
+# head) units): equal block ranges per workgroup, pieces merged by range
+
+def test_balanced_nan_workspace():
+    """The balanced merge reads only the slots this call wrote."""
+    log("decode balanced NaN workspace")
+    wl = make_tiny_decode(seed=88, ctx=(3000, 1, 700, 16, 4096, 33, 2), Hq=32, Hkv=8, D=128,
+                          dtype="bf16")
+    cl = wl.context_lens.copy()
+    cl[5] = 0
+    ws = decode_workspace(7, 32, 8, 128, 4096)
+    ws.fill_(float("nan"))
+    out = to_f64(gpu_decode(wl, gpu_pool_for(wl), context_lens=cl, workspace=ws))
+    assert (out[5] == 0).all()
+    ref = oracle.decode(wl.q, *oracle_pools(wl, oracle), wl.block_tables, cl, wl.scale, wl.dtype)
+    keep = [s for s in range(7) if s != 5]
+    assert_close(out[keep], ref[keep], "bf16", "balanced NaN workspace")
+
+
+@pytest.mark.parametrize("S", [1024, 1025])
+def test_balanced_sequence_limit(S):
+    """1024 sequences are scanned by every workgroup; 1025 fall back to
+    per-partition workgroups.  One long context makes the call split."""
+    log(f"decode {S} sequences with one long context")
+    rng = np.random.default_rng(S)
+    ctx = [int(x) for x in rng.integers(1, 40, S)]
+    ctx[S // 3] = 3000
+    wl = make_tiny_decode(seed=S, ctx=tuple(ctx), Hq=4, Hkv=1, D=64, dtype="bf16")
+    out = to_f64(gpu_decode(wl, gpu_pool_for(wl), partition_size=0))
+    seqs = sorted(set(list(range(0, S, 37)) + [S // 3, S - 1]))
+    ref = _oracle_decode(wl, seqs=seqs)
+    assert_close(out[seqs], ref[seqs], "bf16", f"{S} sequences")

@@ -1,0 +1,115 @@
+"""pa_decode_append (cache write of each sequence's newest token fused with
+decode) on the GPU.
+
+The pools it leaves must equal, byte for byte, those of pa_reshape_and_cache
+of the same rows (every untouched slot keeps its NaN poison); its output is
+compared with the fp64 oracle over the written pools at the decode
+tolerances (fp32 max-abs 1e-5; bf16 |gpu - ref| <= 2e-2 + 2e-2 |ref|).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_decode, make_tiny_decode
+
+from gpu_util import (assert_close, decode_workspace, gpu_decode, gpu_decode_append, gpu_pool_for,
+                      log, oracle_pools, raw_bits, to_f64, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_decode(wl, seqs=None):
+    pk, pv = oracle_pools(wl, oracle)
+    return oracle.decode(wl.q, pk, pv, wl.block_tables, wl.context_lens, wl.scale, wl.dtype,
+                         seqs=seqs)
+
+
+def _assert_pools_equal(a, b, what):
+    torch().cuda.synchronize()
+    for x, y, n in ((a.k_bits(), b.k_bits(), "K"), (a.v_bits(), b.v_bits(), "V")):
+        bad = np.flatnonzero(x != y)
+        assert bad.size == 0, f"{what} {n}: {bad.size} elements differ, first at {bad[0]}"
+
+
+SHAPES = [
+    # dtype, D, Hq, Hkv, ctx (ctx % 16 == 1 puts the new token first in a
+    # fresh block, ctx % 16 == 0 last in a full one)
+    ("bf16", 128, 32, 8, (1, 7, 16, 17, 100, 513, 1000)),
+    ("bf16", 128, 64, 8, (3, 48, 255, 700)),
+    ("bf16", 128, 4, 2, (5, 31, 300, 32)),
+    ("bf16", 64, 8, 4, (1, 33, 77, 32)),
+    ("bf16", 64, 16, 2, (9, 160, 401)),
+    ("f32", 64, 4, 2, (5, 17, 33, 64, 130)),
+    ("f32", 128, 16, 4, (12, 150, 16)),
+    ("f32", 128, 8, 1, (70, 1)),
+]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,ctx", SHAPES)
+@pytest.mark.parametrize("partition", [0, -1, 64])
+def test_append_equals_write_then_decode(dtype, D, Hq, Hkv, ctx, partition):
+    log(f"decode append {dtype} D={D} Hq={Hq} Hkv={Hkv} ctx={ctx} partition={partition}")
+    wl = make_tiny_decode(seed=141 + D + Hq, ctx=ctx, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype)
+    pool = gpu_pool_for(wl, with_new=False)
+    out = to_f64(gpu_decode_append(wl, pool, partition_size=partition))
+    _assert_pools_equal(pool, gpu_pool_for(wl), "append")
+    assert_close(out, _oracle_decode(wl), dtype, f"append {dtype} {D} {Hq}/{Hkv}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_append_single_token_is_the_v_row(dtype):
+    """ctx = 1: the only token is the appended one; its weight is exactly 1."""
+    log(f"decode append single token {dtype}")
+    wl = make_tiny_decode(seed=15, ctx=(1, 1, 1, 1), Hq=8, Hkv=2, D=128, dtype=dtype)
+    pool = gpu_pool_for(wl, with_new=False)
+    got = to_f64(gpu_decode_append(wl, pool))
+    for s in range(4):
+        for h in range(8):
+            assert np.array_equal(got[s, h], oracle.widen(wl.new_v[s, h // 4], dtype))
+
+
+def test_append_negative_slot_writes_nothing():
+    """A row with slot -1 is not written; its sequence reads the pool as is
+    (its newest token was written beforehand)."""
+    log("decode append negative slot")
+    wl = make_tiny_decode(seed=16, ctx=(40, 17, 300), Hq=8, Hkv=2, D=128, dtype="bf16")
+    pool = gpu_pool_for(wl, with_new=False)
+    pool.write(wl.new_k[:1], wl.new_v[:1], wl.new_slots[:1])
+    slots = wl.new_slots.copy()
+    slots[0] = -1
+    out = to_f64(gpu_decode_append(wl, pool, slots=slots))
+    _assert_pools_equal(pool, gpu_pool_for(wl), "negative slot")
+    assert_close(out, _oracle_decode(wl), "bf16", "negative slot")
+
+
+def test_append_nan_workspace_and_repeat():
+    """The workspace needs no initial contents; a second step over the same
+    pool (rows rewritten with the same values) gives the same output."""
+    log("decode append NaN workspace")
+    wl = make_tiny_decode(seed=17, ctx=(3000, 1, 700, 16, 4096, 33), Hq=32, Hkv=8, D=128,
+                          dtype="bf16")
+    ws = decode_workspace(6, 32, 8, 128, 4096)
+    ws.fill_(float("nan"))
+    pool = gpu_pool_for(wl, with_new=False)
+    a = gpu_decode_append(wl, pool, workspace=ws)
+    b = gpu_decode_append(wl, pool, workspace=ws)
+    assert np.array_equal(raw_bits(a), raw_bits(b))
+    _assert_pools_equal(pool, gpu_pool_for(wl), "repeat")
+    assert_close(to_f64(a), _oracle_decode(wl), "bf16", "NaN workspace")
+
+
+def test_append_llama3_8b_layer():
+    """The Llama-3.1-8B-shaped step (64 sequences, contexts U[128, 4096]) in
+    the launch configuration the benchmark times."""
+    log("decode append llama-3.1-8b layer")
+    wl = make_decode(2)
+    pool = gpu_pool_for(wl, with_new=False)
+    out = to_f64(gpu_decode_append(wl, pool))
+    _assert_pools_equal(pool, gpu_pool_for(wl), "llama-3.1-8b append")
+    ref = _oracle_decode(wl)
+    err = assert_close(out, ref, "bf16", "llama-3.1-8b append")
+    log(f"  max abs err {err:.3g}")
+    # and within rounding of the two-call path
+    two = to_f64(gpu_decode(wl, gpu_pool_for(wl)))
+    assert_close(out, two, "bf16", "append vs write + decode")

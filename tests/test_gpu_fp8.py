@@ -18,7 +18,8 @@ from workloads import (FP8_K_SCALE, FP8_POISON, FP8_V_SCALE, bf16_bits_from_f32,
                        make_prefill, make_spec_verify, make_tiny_decode, make_tiny_prefill,
                        make_tiny_shared)
 
-from gpu_util import assert_close, decode_workspace, gpu_shared_prefix, log, to_dev, to_f64, torch
+from gpu_util import (assert_close, decode_workspace, gpu_decode_append, gpu_shared_prefix, log,
+                      to_dev, to_f64, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -205,6 +206,24 @@ def test_decode_llama3_8b_batch64_sampled():
         assert np.isfinite(got).all()
         err = assert_close(got[seqs], ref[seqs], "bf16", f"partition {part}")
         log(f"  partition {part}: max abs err {err:.3g}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,ctx", SHAPES[:3])
+@pytest.mark.parametrize("partition", [0, -1, 64])
+def test_decode_append(Hq, Hkv, ctx, partition):
+    """pa_decode_append over fp8 pools: the appended rows are encoded as
+    pa_reshape_and_cache encodes them (codes compared with the oracle's), and
+    the output matches the oracle over the resulting codes."""
+    log(f"fp8 decode append Hq={Hq} Hkv={Hkv} ctx={ctx} partition={partition}")
+    wl = make_tiny_decode(seed=161 + Hq, ctx=ctx, Hq=Hq, Hkv=Hkv, D=128, dtype="bf16")
+    pool = Fp8Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, FP8_K_SCALE, FP8_V_SCALE)
+    pool.write(wl.hist_k, wl.hist_v, wl.hist_slots)
+    got = to_f64(gpu_decode_append(wl, pool, partition_size=partition, qdtype="bf16"))
+    f8.reshape_and_cache(pool.ok, pool.ov, wl.new_k, wl.new_v, wl.new_slots, pool.k_scale,
+                         pool.v_scale)
+    pool.assert_codes_equal("appended rows")
+    err = assert_close(got, oracle_decode_fp8(wl, pool), "bf16", f"fp8 append {Hq}/{Hkv}")
+    log(f"  max abs err {err:.3g}")
 
 
 def test_decode_zero_length_context_gives_zeros():
