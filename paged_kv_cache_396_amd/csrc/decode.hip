@@ -543,28 +543,6 @@ struct WaveDecoder {
     for (int i = 0; i < C::NV; ++i)
       vt[i] = vpart == 0 ? make_uint4(sv[(lane + kWave * i) / C::VCPR], 0, 0, 0) : z;
   }
-
-  // Stores the new row to offset o of the (block, kv head) tiles at kt / vt.
-  __device__ void store_new_row(char* kt, char* vt, int o, const uint4 (&knew)[C::U],
-                                const uint32_t (&vnew)[C::NV]) const {
-    if (r == 0) {
-#pragma unroll
-      for (int u = 0; u < C::U; ++u) *(uint4*)(kt + o * C::RB + (u * C::LPR + c) * 16) = knew[u];
-    }
-    if (vpart == 0) {
-#pragma unroll
-      for (int i = 0; i < C::NV; ++i) {
-        const int dim = (lane + kWave * i) / C::VCPR;
-        char* dst = vt + ((int64_t)dim * kBlock + o) * EB;
-        if constexpr (EB == 1)
-          *(uint8_t*)dst = (uint8_t)vnew[i];
-        else if constexpr (EB == 2)
-          *(uint16_t*)dst = (uint16_t)vnew[i];
-        else
-          *(uint32_t*)dst = vnew[i];
-      }
-    }
-  }
 };
 
 // Occupancy target (waves per SIMD) the register allocator must meet.
@@ -614,8 +592,9 @@ struct DecodeLds {
 // Fused append: when `s` is not negative, b1 is the sequence's last block
 // and row s of the new rows is its newest token, at position ctx - 1.  The
 // wave that takes that block loads the token's rows with its first block
-// ids, stores them to the token's slot (unless write_row is false: then a
-// later kernel of the call writes them) and keeps a copy in LDS.  If the slot
+// ids and keeps a copy in LDS (a later kernel of the call writes them to
+// the pool: a store here would hold up this wave's later tile waits until
+// it is acknowledged, behind the whole read stream).  If the slot
 // is row tn = (ctx - 1) % 16 of that block (the case the contract asks
 // for), the block is scored without its pool row tn, and after the last
 // block the token is scored from the LDS copy as a one-token tile: the same
@@ -624,8 +603,7 @@ struct DecodeLds {
 template <int EB, int D, int G>
 __device__ inline void stream_blocks(WaveDecoder<EB, D, G>& wd, DecodeLds<EB, D, G>& lds,
                                      const DecodeParams& p, const int32_t* bt, int g, int w,
-                                     int b0, int b1, int ctx, int my_ids, int s = -1,
-                                     bool write_row = true) {
+                                     int b0, int b1, int ctx, int my_ids, int s = -1) {
   using C = DecodeCfg<EB, D, G>;
   constexpr int NW = kDecodeWaves;
   const int lane = wd.lane;
@@ -681,15 +659,10 @@ __device__ inline void stream_blocks(WaveDecoder<EB, D, G>& wd, DecodeLds<EB, D,
   };
   if (app) {
     // the new row was loaded right after the block ids, which the first
-    // tile loads wait for anyway: write it out and keep a copy before them
-    // (after them, the wait for the row would also cover the first tile)
+    // tile loads wait for anyway: keep its copy before them (after them,
+    // the wait for the row would also cover the first tile)
     slot = ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot_in >> 32)) << 32) |
            (uint32_t)__builtin_amdgcn_readfirstlane((int)slot_in);
-    if (write_row && slot >= 0 && slot < (int64_t)p.num_blocks * kBlock) {
-      const int64_t base = (slot / kBlock * p.num_kv_heads + g) * tile_bytes;
-      wd.store_new_row((char*)p.k_cache + base, (char*)p.v_cache + base, (int)(slot % kBlock),
-                       knew, vnew);
-    }
     wd.stash_new_row(lds.newk[w], lds.newv[w], knew, vnew);
   }
   if (nmine > 0) prologue();
@@ -949,10 +922,8 @@ void decode_balanced_kernel(DecodeParams p) {
     const int my_ids = jb < b1 ? bt[jb] : 0;
     wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::QRB, wd.qv);
     wd.reset();
-    // the new rows reach the pools in the merge kernel: a store here would
-    // hold up this wave's later tile waits until the store is acknowledged
     const bool append = p.new_k != nullptr && se == ce && ctx > 0;
-    stream_blocks(wd, lds, p, bt, g, w, b0, b1, ctx, my_ids, append ? s : -1, false);
+    stream_blocks(wd, lds, p, bt, g, w, b0, b1, ctx, my_ids, append ? s : -1);
     const bool whole = cs >= B0 && ce <= B1;
     const int slot = sb == B0 ? 0 : 1;
     finish_waves(wd, lds, p, w, s, g, whole,
@@ -961,17 +932,17 @@ void decode_balanced_kernel(DecodeParams p) {
   }
 }
 
-// Fused append in the balanced schedule: one wave writes sequence s's
-// newest token for kv head g to its slot, encoded as the cache write encodes
-// it (a bit copy; E4M3 codes for fp8 pools).  Rows whose context is empty
-// or whose slot is negative or outside the pool are not written.
+// Fused append: one wave writes sequence s's newest token for kv head g to
+// its slot, encoded as the cache write encodes it (a bit copy; E4M3 codes
+// for fp8 pools).  Rows whose context length is not positive, or whose slot
+// is negative or outside the pool, are not written.
 template <int EB, int D>
 __device__ inline void write_new_row(const DecodeParams& p, int s, int g) {
   constexpr int RB = D * EB;                   // pool bytes of one row
   constexpr int QB = EB == 4 ? 4 : 2;          // bytes of an input element
   const int lane = threadIdx.x;
   const int64_t slot = p.new_slots[s];
-  const int ctx = balanced_ctx(p.context_lens[s], p);
+  const int ctx = p.context_lens[s];
   const char* krow = p.new_k + ((int64_t)s * p.num_kv_heads + g) * D * QB;
   const char* vrow = p.new_v + ((int64_t)s * p.num_kv_heads + g) * D * QB;
   uint4 kc = make_uint4(0, 0, 0, 0);
@@ -1203,6 +1174,13 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
   }
 }
 
+// Fused append with per-partition workgroups: the new rows of every
+// (sequence, kv head), one wave each, after the decode of the call.
+template <int EB, int D>
+__global__ __launch_bounds__(kWave) void append_rows_kernel(DecodeParams p) {
+  write_new_row<EB, D>(p, blockIdx.x / p.num_kv_heads, blockIdx.x % p.num_kv_heads);
+}
+
 template <int EB, int D, int G>
 static hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream) {
   if (prm.num_ranges > 0) {
@@ -1228,10 +1206,19 @@ static hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream) {
   hipLaunchKernelGGL((decode_partition_kernel<EB, D, G>), dim3((unsigned)grid),
                      dim3(kDecodeWaves * kWave), 0, stream, prm);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || prm.num_partitions <= 1) return e;
-  hipLaunchKernelGGL((decode_reduce_kernel<EB, D>), dim3((unsigned)(prm.num_seqs * prm.num_q_heads)),
-                     dim3(kWave), 0, stream, prm);
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (prm.num_partitions > 1) {
+    hipLaunchKernelGGL((decode_reduce_kernel<EB, D>),
+                       dim3((unsigned)(prm.num_seqs * prm.num_q_heads)), dim3(kWave), 0, stream, prm);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (prm.new_k) {
+    hipLaunchKernelGGL((append_rows_kernel<EB, D>),
+                       dim3((unsigned)(prm.num_seqs * prm.num_kv_heads)), dim3(kWave), 0, stream, prm);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 bool decode_supported(int elem_bytes, int head_dim, int group) {
