@@ -564,9 +564,12 @@ constexpr int decode_waves_per_eu() {
 #ifndef PA_DECODE_SLOTS_FP8
 #define PA_DECODE_SLOTS_FP8 2
 #endif
+#ifndef PA_DECODE_SLOTS_BF16
+#define PA_DECODE_SLOTS_BF16 2
+#endif
 template <int EB>
 constexpr int decode_slots() {
-  return EB == 1 ? PA_DECODE_SLOTS_FP8 : 2;
+  return EB == 1 ? PA_DECODE_SLOTS_FP8 : EB == 2 ? PA_DECODE_SLOTS_BF16 : 2;
 }
 
 // LDS of one decode workgroup: the waves' probability exchange buffers and

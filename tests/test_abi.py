@@ -105,6 +105,50 @@ def test_workspace_size_formula():
     assert pa.pa_decode_workspace_bytes(2, 8, 2, 64, 100, 24) == 0   # invalid request
 
 
+def test_balanced_schedule_choice_and_workspace():
+    """Automatic calls that the partition rule would split run the balanced
+    schedule (partition size reported as 0) for up to 1024 sequences; its
+    workspace holds 2 partial slots per (kv head, range, group head), with
+    ranges = CUs * 4 / Hkv for the workspace bound (no GPU here: 256 CUs)."""
+    cus = 256
+    # 64 seqs x 8 kv heads = 512 units < 4 per CU, contexts up to 4096: split
+    assert pa.pa_decode_partition_size(64, 8, 4096, 0) == 0
+    ranges = cus * 4 // 8
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) == ranges * 2 * 32 * (128 + 2) * 4
+    # explicit partitions and "no split" keep the per-partition schedule
+    assert pa.pa_decode_partition_size(64, 8, 4096, 512) == 512
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 512) == 64 * 32 * 8 * (128 + 2) * 4
+    assert pa.pa_decode_partition_size(64, 8, 4096, -1) == 4096
+    # enough units for the chip: no split, no workspace
+    assert pa.pa_decode_partition_size(256, 8, 2048, 0) == 2048
+    assert pa.pa_decode_workspace_bytes(256, 64, 8, 128, 2048, 0) == 0
+    # short contexts that the rule would not split
+    assert pa.pa_decode_partition_size(4, 2, 64, 0) == 64
+    # up to 1023 (sequence, kv head) units on 256 CUs: balanced; 1024 units
+    # are 4 per CU, which the partition rule does not split
+    assert pa.pa_decode_partition_size(1023, 1, 3000, 0) == 0
+    assert pa.pa_decode_partition_size(1024, 1, 3000, 0) == 3008
+
+
+def test_decode_append_argument_errors():
+    L = pa.lib()
+    d = pa.cache_desc(16, 2, 64, pa.PA_BF16)
+    one, z = ctypes.c_void_p(1), ctypes.c_void_p(0)
+
+    def call(k=one, v=one, slots=one, desc=d, num_seqs=2, num_q_heads=8):
+        return L.pa_decode_append(one, one, k, v, slots, one, one, one, 8, one, 100, num_seqs,
+                                  num_q_heads, 0.125, -1, z, 0,
+                                  ctypes.byref(desc) if desc is not None else None, z)
+
+    assert call(k=z) == -1
+    assert b"slot_mapping" in L.pa_last_error()
+    assert call(v=z) == -1
+    assert call(slots=z) == -1
+    assert call(desc=None) == -1
+    assert call(num_q_heads=7) == -2
+    assert call(num_seqs=0, k=z, v=z, slots=z) == 0    # nothing to do
+
+
 def test_reshape_and_cache_argument_errors():
     L = pa.lib()
     d = pa.cache_desc(16, 2, 64, pa.PA_BF16)

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
+import paged_kv_cache_396_amd as pa
 from workloads import make_decode, make_tiny_decode, make_tiny_shared
 
 from gpu_util import (assert_close, decode_workspace, gpu_decode, gpu_pool_for, log, oracle_pools,
@@ -246,15 +247,17 @@ def test_balanced_nan_workspace():
     assert_close(out[keep], ref[keep], "bf16", "balanced NaN workspace")
 
 
-@pytest.mark.parametrize("S", [1024, 1025])
-def test_balanced_sequence_limit(S):
-    """1024 sequences are scanned by every workgroup; 1025 fall back to
-    per-partition workgroups.  One long context makes the call split."""
+@pytest.mark.parametrize("S", [1000, 1023])
+def test_balanced_many_sequences(S):
+    """Every workgroup scans all S block counts in LDS (up to four per
+    thread); one long context makes the call split, and the 1023 units stay
+    under 4 per compute unit, so the balanced schedule runs."""
     log(f"decode {S} sequences with one long context")
     rng = np.random.default_rng(S)
     ctx = [int(x) for x in rng.integers(1, 40, S)]
     ctx[S // 3] = 3000
     wl = make_tiny_decode(seed=S, ctx=tuple(ctx), Hq=4, Hkv=1, D=64, dtype="bf16")
+    assert pa.pa_decode_partition_size(S, 1, 3000, 0) == 0, "expected the balanced schedule"
     out = to_f64(gpu_decode(wl, gpu_pool_for(wl), partition_size=0))
     seqs = sorted(set(list(range(0, S, 37)) + [S // 3, S - 1]))
     ref = _oracle_decode(wl, seqs=seqs)
