@@ -872,7 +872,7 @@ def main():
         "tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": kv,
-        "step_call": "pa_decode_append (cache write of the 64 new tokens fused with decode)",
+        "step_call": f"pa_decode_append (cache write of the {len(wl.new_slots)} new tokens fused with decode)",
         "step_call_hot": dist(step_ms),
         "step_call_cold": dist(cold_ms),
         "two_call_step": {"calls": "pa_reshape_and_cache + pa_decode", "ms_per_step": round(ms_two, 5),
