@@ -682,8 +682,8 @@ def read_ceiling(steps=10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_b64", choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=0, help="0 auto, <0 no split, >0 tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
