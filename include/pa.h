@@ -204,9 +204,9 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * to pa_reshape_and_cache's and out equals pa_decode's over them up to the
  * order of fp32 sums (the newest token's K/V are taken from k, v instead of
  * being read back; its softmax term is added after the other tokens').
- * Rows with context 0 are not written.  Outside the contract the pools are
- * written as pa_reshape_and_cache writes them (slots in range) but out is
- * unspecified.
+ * Rows whose context length is 0 (or negative) are not written.  Outside the
+ * contract the pools are written as pa_reshape_and_cache writes them (slots
+ * in range) but out is unspecified.
  */
 int pa_decode_append(void* out, const void* q, const void* k, const void* v,
                      const int64_t* slot_mapping, void* k_cache, void* v_cache,
