@@ -138,9 +138,14 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t
                                  int32_t partition_size_request);
 
 /*
- * Workspace bytes pa_decode needs for these sizes and this partition request
- * (the same request later passed to pa_decode).  0 means no workspace is
- * needed (every sequence fits one partition).
+ * Workspace bytes pa_decode (and pa_decode_append) needs for these sizes and
+ * this partition request (the same request later passed to pa_decode), on
+ * the current device: the work-balanced schedule's workspace grows with the
+ * device's compute unit count (2 partial states per (kv head, range, q head
+ * of the group), ranges = 4 * CUs / num_kv_heads at most), independent of
+ * the context lengths.  0 means no workspace is needed (every sequence fits
+ * one partition).  pa_decode rechecks the size on the device it launches on
+ * and returns PA_ERR_WORKSPACE when it is too small.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
