@@ -77,7 +77,7 @@ typedef enum {
  * with bias 7, 3 mantissa bits, no infinities, largest magnitude 448) and
  * one fp32 scale per pool; the activations that meet such a pool (k and v
  * rows written, q, out) are bf16.  The pages name an fp8 KV cache for its
- * doubled capacity and halved attention bytes (plumephp.com vLLM deep dive,
+ * doubled capacity and halved attention bytes (zihan-zhang.net vLLM study,
  * 4.2.1) without fixing a format or scaling; these are the readings taken. */
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
@@ -348,7 +348,7 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
 
 /*
  * pa_rejection_sample — the verification step of speculative decoding
- * (plumephp.com vLLM deep dive, 4.1.1; vLLM: from PagedAttention to
+ * (zihan-zhang.net vLLM study, 4.1.1; vLLM: from PagedAttention to
  * Speculative Decoding, 5.3-5.4).  A drafter proposed num_draft = k tokens per
  * request; the target model scored the k + 1 positions in one pass (its
  * attention: pa_prefill_chunk with k + 1 query rows per request).  Candidate

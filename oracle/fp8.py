@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's CPU
 baseline may import this module.  It shares no code with the HIP library.
 
 The pages name an fp8 KV cache as a serving option that doubles the cache's
-capacity and halves the bytes attention reads (plumephp.com vLLM deep dive,
+capacity and halves the bytes attention reads (zihan-zhang.net vLLM study,
 4.2.1: KV cache quantization; the same page's 4.2.3 lists it for long
 contexts at high concurrency).  They fix neither the 8-bit format nor how
 values are scaled into it.  Readings taken here:
@@ -33,7 +33,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .paged_attention import BLOCK_SIZE, attend, gather, widen
+from . import paged_attention
+from .paged_attention import BLOCK_SIZE, widen
 
 FP8_MAX = 448.0
 NAN_CODE = 0x7F
@@ -123,54 +124,25 @@ def reshape_and_cache(pool_k, pool_v, k, v, slot_mapping, k_scale, v_scale, dtyp
 
 
 # ----------------------------------------------------------------------------
-# attention over dequantized pools
+# attention over dequantized pools: the same attention as over a bf16 pool
+# (the generic decode / prefill of paged_attention, pinned on their own), with
+# every gathered K and V code replaced by the value it stands for
 
 
 def decode_attention(q, pool_k, pool_v, block_tables, context_lens, scale, k_scale, v_scale,
                      q_dtype="bf16", seqs=None):
     """Decode attention (one query per sequence, whole context visible) over
     fp8 pools; float64 [S, Hq, D], zeros for empty contexts."""
-    S, Hq, D = q.shape
-    Hkv = pool_k.shape[2]
-    G = Hq // Hkv
-    sc = float(np.float32(scale))
-    out = np.zeros((S, Hq, D), dtype=np.float64)
-    for s in (range(S) if seqs is None else seqs):
-        n = int(context_lens[s])
-        if n == 0:
-            continue
-        K = dequantize(gather(pool_k, block_tables[s], n), k_scale)
-        V = dequantize(gather(pool_v, block_tables[s], n), v_scale)
-        qs = widen(q[s], q_dtype)
-        for h in range(Hq):
-            out[s, h], _ = attend(qs[h], K[:, h // G, :], V[:, h // G, :], sc)
-    return out
+    return paged_attention.decode(q, pool_k, pool_v, block_tables, context_lens, scale, q_dtype,
+                                  seqs=seqs, k_value=lambda c: dequantize(c, k_scale),
+                                  v_value=lambda c: dequantize(c, v_scale))
 
 
 def prefill_attention(q, pool_k, pool_v, block_tables, query_start_loc, context_lens, scale,
                       k_scale, v_scale, q_dtype="bf16", rows=None):
     """Causal attention of each request's query chunk (its last n_r tokens)
     against its paged fp8 context; float64 [total_q, Hq, D]."""
-    Tq, Hq, D = q.shape
-    Hkv = pool_k.shape[2]
-    G = Hq // Hkv
-    sc = float(np.float32(scale))
-    out = np.zeros((Tq, Hq, D), dtype=np.float64)
-    want = None if rows is None else set(int(r) for r in rows)
-    for r in range(len(context_lens)):
-        lo, hi = int(query_start_loc[r]), int(query_start_loc[r + 1])
-        n_r, ctx = hi - lo, int(context_lens[r])
-        if n_r == 0:
-            continue
-        K = dequantize(gather(pool_k, block_tables[r], ctx), k_scale)
-        V = dequantize(gather(pool_v, block_tables[r], ctx), v_scale)
-        for i in range(n_r):
-            row = lo + i
-            if want is not None and row not in want:
-                continue
-            pos = ctx - n_r + i
-            qrow = widen(q[row], q_dtype)
-            for h in range(Hq):
-                g = h // G
-                out[row, h], _ = attend(qrow[h], K[: pos + 1, g, :], V[: pos + 1, g, :], sc)
-    return out
+    return paged_attention.prefill_chunk(q, pool_k, pool_v, block_tables, query_start_loc,
+                                         context_lens, scale, q_dtype, rows=rows,
+                                         k_value=lambda c: dequantize(c, k_scale),
+                                         v_value=lambda c: dequantize(c, v_scale))

@@ -154,27 +154,37 @@ def attend(qvec: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
     return (w @ V) / l, w / l
 
 
+def _value_fns(dtype, k_value, v_value):
+    """How raw pool elements become float64 values: widened as ``dtype`` unless
+    the caller gives its own mapping (an 8-bit pool's dequantization)."""
+    kf = k_value if k_value is not None else (lambda raw: widen(raw, dtype))
+    vf = v_value if v_value is not None else (lambda raw: widen(raw, dtype))
+    return kf, vf
+
+
 def decode(q, pool_k, pool_v, block_tables, context_lens, scale, dtype, num_kv_heads=None,
-           return_weights=False, seqs=None):
+           return_weights=False, seqs=None, k_value=None, v_value=None):
     """Decode attention for every (sequence, q head): one query per sequence,
     the whole context visible (the newest token included).
 
     ``q`` is raw [S, Hq, D]; the result is float64 [S, Hq, D].  A sequence of
     length 0 yields zeros.  ``seqs`` restricts the work to some sequences
-    (others stay zero) for sampled checks at large sizes.
+    (others stay zero).  ``k_value`` / ``v_value`` map gathered raw pool
+    elements to float64 (default: widen them as ``dtype``, the q dtype too).
     """
     S, Hq, D = q.shape
     Hkv = pool_k.shape[2] if num_kv_heads is None else num_kv_heads
     G = Hq // Hkv
     sc = float(np.float32(scale))
+    kf, vf = _value_fns(dtype, k_value, v_value)
     out = np.zeros((S, Hq, D), dtype=np.float64)
     weights = {}
     for s in (range(S) if seqs is None else seqs):
         n = int(context_lens[s])
         if n == 0:
             continue
-        K = widen(gather(pool_k, block_tables[s], n), dtype)
-        V = widen(gather(pool_v, block_tables[s], n), dtype)
+        K = kf(gather(pool_k, block_tables[s], n))
+        V = vf(gather(pool_v, block_tables[s], n))
         qs = widen(q[s], dtype)
         for h in range(Hq):
             g = h // G
@@ -186,19 +196,21 @@ def decode(q, pool_k, pool_v, block_tables, context_lens, scale, dtype, num_kv_h
 
 
 def prefill_chunk(q, pool_k, pool_v, block_tables, query_start_loc, context_lens, scale, dtype,
-                  rows=None):
+                  rows=None, k_value=None, v_value=None):
     """Causal attention of each request's query chunk against its paged context.
 
     Request r owns query rows query_start_loc[r] .. query_start_loc[r+1]-1 (n_r of
     them); they are the last n_r tokens of its ctx_r-token context, so query i
     sits at position ctx_r - n_r + i and sees keys 0 .. that position.
     ``rows`` optionally restricts the work to some query rows (others stay zero).
+    ``k_value`` / ``v_value`` as for ``decode``.
     Returns float64 [total_q, Hq, D].
     """
     Tq, Hq, D = q.shape
     Hkv = pool_k.shape[2]
     G = Hq // Hkv
     sc = float(np.float32(scale))
+    kf, vf = _value_fns(dtype, k_value, v_value)
     out = np.zeros((Tq, Hq, D), dtype=np.float64)
     want = None if rows is None else set(int(r) for r in rows)
     R = len(context_lens)
@@ -208,8 +220,8 @@ def prefill_chunk(q, pool_k, pool_v, block_tables, query_start_loc, context_lens
         ctx = int(context_lens[r])
         if n_r == 0:
             continue
-        K = widen(gather(pool_k, block_tables[r], ctx), dtype)
-        V = widen(gather(pool_v, block_tables[r], ctx), dtype)
+        K = kf(gather(pool_k, block_tables[r], ctx))
+        V = vf(gather(pool_v, block_tables[r], ctx))
         for i in range(n_r):
             row = lo + i
             if want is not None and row not in want:

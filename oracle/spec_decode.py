@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's CPU
 baseline may import this module.  It shares no code with the HIP library.
 
-What the pages fix (plumephp.com vLLM deep dive, 4.1.1; vLLM: from
+What the pages fix (zihan-zhang.net vLLM study, 4.1.1; vLLM: from
 PagedAttention to Speculative Decoding, 5.3-5.4):
 
 * a cheap drafter proposes k tokens x_0..x_{k-1}, drawn from its

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
 // bias 7, 3 mantissa bits; no infinities, largest magnitude 448) and one fp32
 // scale per pool: code c stands for value(c) * scale.  The pages only say
 // that an fp8 KV cache doubles capacity and halves attention's bytes
-// (plumephp.com vLLM deep dive, 4.2.1); the format, the per-pool scale and
+// (zihan-zhang.net vLLM study, 4.2.1); the format, the per-pool scale and
 // the rounding below are the readings taken for it.  An incoming bf16 value
 // x becomes the E4M3 code nearest to x / scale (one correctly rounded fp32
 // division), ties to the even code, magnitudes beyond 448 saturating; a NaN

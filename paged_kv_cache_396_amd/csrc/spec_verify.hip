@@ -1,6 +1,6 @@
 // Verification of drafted tokens by rejection sampling (speculative decoding).
 //
-// plumephp.com vLLM deep dive, 4.1.1: a drafter proposes k tokens from its
+// zihan-zhang.net vLLM study, 4.1.1: a drafter proposes k tokens from its
 // distributions q_i; the target model's distributions p_0..p_k come from one
 // forward pass over all k + 1 positions (its attention is pa_prefill_chunk
 // with k + 1 query rows per request).  Candidate x_i is kept with

@@ -8,7 +8,12 @@ Sources of truth used here, none of them the oracle itself:
   codes, the count of finite codes);
 * the rounding error bound (half the spacing of neighbouring codes);
 * hand-computed attention results for two-token contexts, where each scale
-  enters the closed form.
+  enters the closed form;
+* textbook attention written out with dense matrices over values that torch
+  dequantizes (torch quantizes, torch gives each code's value): causal
+  prefill masked with np.triu, and decode by scalar loops, both with several
+  q heads per kv head, every query row and a prior context;
+* GQA equal to MHA with the kv heads replicated.
 The last tests plant mistakes in the oracle and check that a pin fails.
 """
 
@@ -20,7 +25,7 @@ import torch
 
 import oracle.fp8 as f8
 from oracle.paged_attention import BLOCK_SIZE
-from workloads import bf16_bits_from_f32
+from workloads import bf16_bits_from_f32, make_tiny_decode, make_tiny_prefill
 
 
 def torch_values():
@@ -212,6 +217,143 @@ def test_prefill_last_row_equals_decode():
 
 
 # ----------------------------------------------------------------------------
+# attention over fp8 pools against textbook attention over torch's values
+
+# scales that keep N(0, 1) draws far inside +-448 (no saturation, which
+# torch's cast does not do), neither a power of two
+PIN_K_SCALE = np.float32(0.05)
+PIN_V_SCALE = np.float32(0.04)
+
+
+def _bf16_f32(raw):
+    return (np.asarray(raw).astype(np.uint32) << 16).view(np.float32)
+
+
+def torch_dequant(raw, scale):
+    """Value each bf16 input stands for once stored in an fp8 pool: x / scale
+    in fp32, cast to E4M3 by torch, the code's value (torch) times scale."""
+    codes = torch_codes(_bf16_f32(raw) / np.float32(scale))
+    return torch_values()[codes] * float(np.float32(scale))
+
+
+def _fp8_pools(wl):
+    pk = f8.new_pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, 0x7F)
+    pv = f8.new_pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, 0x7F)
+    for k, v, sl in ((wl.hist_k, wl.hist_v, wl.hist_slots), (wl.new_k, wl.new_v, wl.new_slots)):
+        f8.reshape_and_cache(pk, pv, k, v, sl, PIN_K_SCALE, PIN_V_SCALE)
+    return pk, pv
+
+
+def _pin_prefill():
+    return make_tiny_prefill(seed=31, prior=(0, 21, 40), chunk=(7, 16, 9), Hq=8, Hkv=2, D=16,
+                             dtype="bf16")
+
+
+def textbook_causal_fp8(wl):
+    """softmax(scale Q K^T + causal mask) V per request and head, dense, the
+    mask from np.triu over the request's full context, K and V from torch's
+    dequantization of the request's logical-order rows."""
+    Tq, Hq, D = wl.q.shape
+    Hkv = wl.num_kv_heads
+    G = Hq // Hkv
+    sc = float(np.float32(wl.scale))
+    out = np.zeros((Tq, Hq, D))
+    koff = 0
+    for r in range(wl.num_reqs):
+        lo, hi = int(wl.query_start_loc[r]), int(wl.query_start_loc[r + 1])
+        n_r, ctx = hi - lo, int(wl.context_lens[r])
+        prior = ctx - n_r
+        K = torch_dequant(np.concatenate([wl.hist_k[koff: koff + prior], wl.new_k[lo:hi]]), PIN_K_SCALE)
+        V = torch_dequant(np.concatenate([wl.hist_v[koff: koff + prior], wl.new_v[lo:hi]]), PIN_V_SCALE)
+        koff += prior
+        Q = _bf16_f32(wl.q[lo:hi]).astype(np.float64)
+        hidden = np.triu(np.ones((n_r, ctx), dtype=bool), k=prior + 1)
+        for h in range(Hq):
+            Z = sc * (Q[:, h, :] @ K[:, h // G, :].T)
+            Z[hidden] = -np.inf
+            P = np.exp(Z - Z.max(axis=1, keepdims=True))
+            out[lo:hi, h] = (P / P.sum(axis=1, keepdims=True)) @ V[:, h // G, :]
+    return out
+
+
+def check_fp8_prefill_textbook(wl):
+    pk, pv = _fp8_pools(wl)
+    got = f8.prefill_attention(wl.q, pk, pv, wl.block_tables, wl.query_start_loc, wl.context_lens,
+                               wl.scale, PIN_K_SCALE, PIN_V_SCALE)
+    err = np.max(np.abs(got - textbook_causal_fp8(wl)))
+    assert err <= 1e-12, f"fp8 prefill vs textbook: {err}"
+
+
+def test_fp8_prefill_equals_textbook_causal_attention():
+    check_fp8_prefill_textbook(_pin_prefill())
+
+
+def _pin_decode():
+    return make_tiny_decode(seed=33, ctx=(1, 16, 23, 50), Hq=8, Hkv=2, D=16, dtype="bf16")
+
+
+def scalar_decode_fp8(wl):
+    """Decode attention by scalar loops (math.fsum) over torch-dequantized
+    logical-order K/V; q head h reads kv head h // G."""
+    S, Hq, D = wl.q.shape
+    Hkv = wl.num_kv_heads
+    G = Hq // Hkv
+    sc = float(np.float32(wl.scale))
+    res = np.zeros((S, Hq, D))
+    off = 0
+    for s, n in enumerate(int(c) for c in wl.context_lens):
+        K = torch_dequant(np.concatenate([wl.hist_k[off: off + n - 1], wl.new_k[s: s + 1]]), PIN_K_SCALE)
+        V = torch_dequant(np.concatenate([wl.hist_v[off: off + n - 1], wl.new_v[s: s + 1]]), PIN_V_SCALE)
+        off += n - 1
+        qf = _bf16_f32(wl.q[s]).astype(np.float64)
+        for h in range(Hq):
+            g = h // G
+            z = [sc * math.fsum(qf[h, x] * K[t, g, x] for x in range(D)) for t in range(n)]
+            m = max(z)
+            e = [math.exp(zz - m) for zz in z]
+            l = math.fsum(e)
+            for x in range(D):
+                res[s, h, x] = math.fsum(e[t] * V[t, g, x] for t in range(n)) / l
+    return res
+
+
+def check_fp8_decode_scalar(wl):
+    pk, pv = _fp8_pools(wl)
+    got = f8.decode_attention(wl.q, pk, pv, wl.block_tables, wl.context_lens, wl.scale,
+                              PIN_K_SCALE, PIN_V_SCALE)
+    err = np.max(np.abs(got - scalar_decode_fp8(wl)))
+    assert err <= 1e-12, f"fp8 decode vs scalar loops: {err}"
+
+
+def test_fp8_decode_equals_scalar_attention_with_gqa():
+    check_fp8_decode_scalar(_pin_decode())
+
+
+def check_fp8_gqa_equals_mha(wl):
+    pk, pv = _fp8_pools(wl)
+    G = wl.num_q_heads // wl.num_kv_heads
+    gqa = f8.decode_attention(wl.q, pk, pv, wl.block_tables, wl.context_lens, wl.scale,
+                              PIN_K_SCALE, PIN_V_SCALE)
+    mha = f8.decode_attention(wl.q, np.repeat(pk, G, axis=2), np.repeat(pv, G, axis=2),
+                              wl.block_tables, wl.context_lens, wl.scale, PIN_K_SCALE, PIN_V_SCALE)
+    assert np.array_equal(gqa, mha)
+    # and the same for every row of a prefill chunk
+    wp = _pin_prefill()
+    pk, pv = _fp8_pools(wp)
+    Gp = wp.num_q_heads // wp.num_kv_heads
+    a = f8.prefill_attention(wp.q, pk, pv, wp.block_tables, wp.query_start_loc, wp.context_lens,
+                             wp.scale, PIN_K_SCALE, PIN_V_SCALE)
+    b = f8.prefill_attention(wp.q, np.repeat(pk, Gp, axis=2), np.repeat(pv, Gp, axis=2),
+                             wp.block_tables, wp.query_start_loc, wp.context_lens, wp.scale,
+                             PIN_K_SCALE, PIN_V_SCALE)
+    assert np.array_equal(a, b)
+
+
+def test_fp8_gqa_equals_mha_with_replicated_kv_heads():
+    check_fp8_gqa_equals_mha(_pin_decode())
+
+
+# ----------------------------------------------------------------------------
 # planted mistakes
 
 
@@ -242,3 +384,63 @@ def test_planted_wrong_exponent_bias_is_caught(monkeypatch):
     monkeypatch.setattr(f8, "E4M3_TABLE", bad)
     with pytest.raises(AssertionError):
         test_table_matches_torch_e4m3fn()
+
+
+def _plain_fp8_prefill(future=0, modmap=False):
+    """A prefill over fp8 pools written out with its own loops, with one of
+    two planted mistakes: each row sees ``future`` keys past its position,
+    or q head h reads kv head h % Hkv."""
+    def run(q, pool_k, pool_v, block_tables, query_start_loc, context_lens, scale, k_scale, v_scale,
+            q_dtype="bf16", rows=None):
+        Tq, Hq, D = q.shape
+        Hkv = pool_k.shape[2]
+        G = Hq // Hkv
+        out = np.zeros((Tq, Hq, D))
+        for r in range(len(context_lens)):
+            lo, hi = int(query_start_loc[r]), int(query_start_loc[r + 1])
+            ctx = int(context_lens[r])
+            nb = (ctx + BLOCK_SIZE - 1) // BLOCK_SIZE
+            ids = np.asarray(block_tables[r][:nb], dtype=np.int64)
+            K = f8.dequantize(pool_k[ids].reshape(nb * BLOCK_SIZE, Hkv, D)[:ctx], k_scale)
+            V = f8.dequantize(pool_v[ids].reshape(nb * BLOCK_SIZE, Hkv, D)[:ctx], v_scale)
+            for i in range(hi - lo):
+                pos = ctx - (hi - lo) + i
+                qrow = _bf16_f32(q[lo + i]).astype(np.float64)
+                for h in range(Hq):
+                    g = h % Hkv if modmap else h // G
+                    z = float(np.float32(scale)) * (K[: pos + 1 + future, g] @ qrow[h])
+                    w = np.exp(z - z.max())
+                    out[lo + i, h] = (w @ V[: pos + 1 + future, g]) / w.sum()
+        return out
+    return run
+
+
+def test_planted_fp8_prefill_future_key_is_caught(monkeypatch):
+    # the unplanted loops pass the pin: the mistake, not the rewrite, fails it
+    monkeypatch.setattr(f8, "prefill_attention", _plain_fp8_prefill())
+    check_fp8_prefill_textbook(_pin_prefill())
+    monkeypatch.setattr(f8, "prefill_attention", _plain_fp8_prefill(future=1))
+    with pytest.raises(AssertionError):
+        check_fp8_prefill_textbook(_pin_prefill())
+
+
+def test_planted_fp8_prefill_wrong_gqa_map_is_caught(monkeypatch):
+    monkeypatch.setattr(f8, "prefill_attention", _plain_fp8_prefill(modmap=True))
+    with pytest.raises(AssertionError):
+        check_fp8_prefill_textbook(_pin_prefill())
+
+
+def test_planted_fp8_decode_wrong_gqa_map_is_caught(monkeypatch):
+    plain = _plain_fp8_prefill(modmap=True)
+
+    def decode_modmap(q, pool_k, pool_v, block_tables, context_lens, scale, k_scale, v_scale,
+                      q_dtype="bf16", seqs=None):
+        # decode is a one-row chunk per sequence
+        qsl = np.arange(q.shape[0] + 1, dtype=np.int32)
+        return plain(q, pool_k, pool_v, block_tables, qsl, context_lens, scale, k_scale, v_scale)
+
+    monkeypatch.setattr(f8, "decode_attention", decode_modmap)
+    with pytest.raises(AssertionError):
+        check_fp8_decode_scalar(_pin_decode())
+    with pytest.raises(AssertionError):
+        check_fp8_gqa_equals_mha(_pin_decode())

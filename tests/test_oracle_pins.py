@@ -487,3 +487,28 @@ def test_planted_wrong_v_layout_is_caught(monkeypatch):
 
     _expect_pin_failure(monkeypatch, "v_pool_bytes", v_bytes_untransposed,
                         test_physical_layout_matches_written_formula)
+
+
+def test_planted_causal_future_key_is_caught(monkeypatch):
+    # each query row also sees the key just past its own position
+    def prefill_future(q, pool_k, pool_v, block_tables, query_start_loc, context_lens, scale, dtype,
+                       rows=None, **kw):
+        Tq, Hq, D = q.shape
+        Hkv = pool_k.shape[2]
+        out = np.zeros((Tq, Hq, D))
+        for r in range(len(context_lens)):
+            lo, hi = int(query_start_loc[r]), int(query_start_loc[r + 1])
+            ctx = int(context_lens[r])
+            K = oracle.widen(oracle.gather(pool_k, block_tables[r], ctx), dtype)
+            V = oracle.widen(oracle.gather(pool_v, block_tables[r], ctx), dtype)
+            for i in range(hi - lo):
+                pos = ctx - (hi - lo) + i
+                qrow = oracle.widen(q[lo + i], dtype)
+                for h in range(Hq):
+                    g = h // (Hq // Hkv)
+                    out[lo + i, h], _ = oracle.attend(qrow[h], K[: pos + 2, g], V[: pos + 2, g],
+                                                      float(np.float32(scale)))
+        return out
+
+    wl = make_tiny_prefill(seed=15, prior=(3, 20), chunk=(6, 13), Hq=4, Hkv=2, D=16, dtype="bf16")
+    _expect_pin_failure(monkeypatch, "prefill_chunk", prefill_future, lambda: check_prefill_textbook(wl))
