@@ -381,20 +381,25 @@ struct WaveDecoder {
     }
     float pr[C::NF];
 #pragma unroll
-    for (int k = 0; k < C::NF; ++k) {
-      pr[k] = exp2f(z[k] - m_mine);
-      l_mine += pr[k];
-    }
+    for (int k = 0; k < C::NF; ++k) pr[k] = exp2f(z[k] - m_mine);
 
-    // ---- probabilities -> LDS as [pair][head] (bf16 pairs or fp32 pairs)
+    // ---- probabilities -> LDS as [pair][head] (bf16 pairs or fp32 pairs).
+    // With bf16 P the running sum adds the rounded weights, the same ones
+    // P.V applies, so the output is a convex combination of V rows.
     if constexpr (EB <= 2) {
       if constexpr (C::NF == 2) {
-        pb[(tk0 >> 1) * G + hh] = pack_bf16(pr[0], pr[1]);
+        const uint32_t pw = pack_bf16(pr[0], pr[1]);
+        l_mine += bf16_lo(pw) + bf16_hi(pw);
+        pb[(tk0 >> 1) * G + hh] = pw;
       } else {
+        const uint16_t pw = to_bf16(pr[0]);
+        l_mine += bf16_lo(pw);
         if ((c & C::DUP_BITS) == 0)
-          ((uint16_t*)pb)[((tk0 >> 1) * G + hh) * 2 + (tk0 & 1)] = to_bf16(pr[0]);
+          ((uint16_t*)pb)[((tk0 >> 1) * G + hh) * 2 + (tk0 & 1)] = pw;
       }
     } else {
+#pragma unroll
+      for (int k = 0; k < C::NF; ++k) l_mine += pr[k];
       if ((c & C::DUP_BITS) == 0) {
 #pragma unroll
         for (int k = 0; k < C::NF; ++k) {

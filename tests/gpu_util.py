@@ -208,3 +208,76 @@ def gpu_shared_prefix(wl, pool, group_size, prefix_lens, max_prefix=None, worksp
                                group_size, mp, pool.desc, ws)
     t.cuda.synchronize()
     return out
+
+
+
+# ----------------------------------------------------------------------------
+# the long-context mixed batch as one step over one pool
+
+
+class MixedStep:
+    """One step of the long-context mixed batch (decode 8 x 32768 and 4
+    chunked-prefill requests of 512 tokens over 4096 prior tokens) on one
+    shared pool that holds both halves' history.  The decode half appends
+    each sequence's newest token and attends (pa_decode_append); the prefill
+    half writes its chunk's K/V (pa_reshape_and_cache) and attends causally
+    (pa_prefill_chunk).  ``run(concurrent)`` issues the halves back to back
+    on one stream, or on two streams of default priority that start and end
+    on the caller's stream."""
+
+    def __init__(self, dec, pre):
+        t = torch()
+        self.dec, self.pre = dec, pre
+        self.pool = GpuPool(dec.num_blocks, dec.num_kv_heads, dec.head_dim, dec.dtype)
+        self.pool.write(dec.hist_k, dec.hist_v, dec.hist_slots)
+        self.pool.write(pre.hist_k, pre.hist_v, pre.hist_slots)
+        self.dq = to_dev(dec.q, dec.dtype)
+        self.dout = t.empty_like(self.dq)
+        self.dk, self.dv = to_dev(dec.new_k, dec.dtype), to_dev(dec.new_v, dec.dtype)
+        self.dslots = t.from_numpy(dec.new_slots).cuda()
+        self.dbt = t.from_numpy(dec.block_tables).cuda()
+        self.dcl = t.from_numpy(dec.context_lens).cuda()
+        S, Hq, D = dec.q.shape
+        self.max_ctx = int(dec.context_lens.max())
+        ws_bytes = pa.pa_decode_workspace_bytes(S, Hq, dec.num_kv_heads, D, self.max_ctx, 0)
+        self.ws = t.empty(max(1, (ws_bytes + 3) // 4), dtype=t.float32, device="cuda")
+        self.pq = to_dev(pre.q, pre.dtype)
+        self.pout = t.empty_like(self.pq)
+        self.pk, self.pv = to_dev(pre.new_k, pre.dtype), to_dev(pre.new_v, pre.dtype)
+        self.pslots = t.from_numpy(pre.new_slots).cuda()
+        self.pbt = t.from_numpy(pre.block_tables).cuda()
+        self.pqsl = t.from_numpy(pre.query_start_loc).cuda()
+        self.pcl = t.from_numpy(pre.context_lens).cuda()
+        self.s1, self.s2 = t.cuda.Stream(), t.cuda.Stream()
+
+    def decode_half(self, stream=None):
+        d = self.dec
+        pa.pa_decode_append(self.dout, self.dq, self.dk, self.dv, self.dslots, self.pool.k,
+                            self.pool.v, self.dbt, self.dcl, self.max_ctx, float(d.scale),
+                            self.pool.desc, workspace=self.ws, stream=stream)
+
+    def prefill_half(self, stream=None):
+        p = self.pre
+        pa.pa_reshape_and_cache(self.pk, self.pv, self.pslots, self.pool.k, self.pool.v,
+                                self.pool.desc, stream=stream)
+        pa.pa_prefill_chunk(self.pout, self.pq, self.pool.k, self.pool.v, self.pbt, self.pqsl,
+                            self.pcl, p.max_q_len, float(p.scale), self.pool.desc, stream=stream)
+
+    def run(self, concurrent):
+        t = torch()
+        main = t.cuda.current_stream()
+        if not concurrent:
+            self.decode_half(main)
+            self.prefill_half(main)
+            return
+        ev = t.cuda.Event()
+        ev.record(main)
+        self.s1.wait_event(ev)
+        self.s2.wait_event(ev)
+        self.decode_half(self.s1)
+        self.prefill_half(self.s2)
+        e1, e2 = t.cuda.Event(), t.cuda.Event()
+        e1.record(self.s1)
+        e2.record(self.s2)
+        main.wait_event(e1)
+        main.wait_event(e2)

@@ -138,25 +138,27 @@ def test_config2_permuted_layout_bitwise_equal():
     assert np.array_equal(raw_bits(oa), raw_bits(ob))
 
 
-def test_config3_llama2_70b_sampled():
-    """Full-size launch; the oracle checks 16 sampled sequences (all heads)."""
-    log("decode config 3 (full launch, sampled check)")
+def test_config3_llama2_70b_full():
+    """The 70B layer at full size: all 256 sequences and 64 heads against the
+    oracle."""
+    log("decode config 3 (full)")
     wl = make_decode(3)
     pool = gpu_pool_for(wl)
     out = to_f64(gpu_decode(wl, pool))
-    seqs = list(range(0, 256, 16))
-    ref = _oracle_decode(wl, seqs=seqs)
-    assert np.isfinite(out).all()
-    assert_close(out[seqs], ref[seqs], "bf16", "config 3 sampled")
+    log("  oracle ...")
+    err = assert_close(out, _oracle_decode(wl), "bf16", "config 3")
+    log(f"  max abs err {err:.3g}")
 
 
 def test_config4_shared_prefix():
-    log("decode config 4 shared prefix")
+    """The shared-prefix batch through pa_decode: all 128 sequences against
+    the oracle, and bitwise equal to the same batch with private prompt
+    copies."""
+    log("decode config 4 shared prefix (full)")
     a = make_decode(4)
     out = to_f64(gpu_decode(a, gpu_pool_for(a)))
-    seqs = list(range(0, 128, 5))
-    ref = _oracle_decode(a, seqs=seqs)
-    assert_close(out[seqs], ref[seqs], "bf16", "config 4 sampled")
+    err = assert_close(out, _oracle_decode(a), "bf16", "config 4")
+    log(f"  max abs err {err:.3g}")
     b = make_decode(4, private_copies=True)
     ob = to_f64(gpu_decode(b, gpu_pool_for(b)))
     assert np.array_equal(out, ob), "shared and private tables differ"
@@ -205,9 +207,7 @@ def test_many_sequences():
     ctx = tuple(int(x) for x in np.random.default_rng(7).integers(1, 40, 4100))
     wl = make_tiny_decode(seed=77, ctx=ctx, Hq=4, Hkv=1, D=64, dtype="bf16")
     out = to_f64(gpu_decode(wl, gpu_pool_for(wl), partition_size=0))
-    seqs = list(range(0, 4100, 41))
-    ref = _oracle_decode(wl, seqs=seqs)
-    assert_close(out[seqs], ref[seqs], "bf16", "4100 sequences")
+    assert_close(out, _oracle_decode(wl), "bf16", "4100 sequences")
 
 
 def test_split_k_workspace_reused_across_calls():
@@ -259,6 +259,4 @@ def test_balanced_many_sequences(S):
     wl = make_tiny_decode(seed=S, ctx=tuple(ctx), Hq=4, Hkv=1, D=64, dtype="bf16")
     assert pa.pa_decode_partition_size(S, 1, 3000, 0) == 0, "expected the balanced schedule"
     out = to_f64(gpu_decode(wl, gpu_pool_for(wl), partition_size=0))
-    seqs = sorted(set(list(range(0, S, 37)) + [S // 3, S - 1]))
-    ref = _oracle_decode(wl, seqs=seqs)
-    assert_close(out[seqs], ref[seqs], "bf16", f"{S} sequences")
+    assert_close(out, _oracle_decode(wl), "bf16", f"{S} sequences")

@@ -192,19 +192,18 @@ def test_decode_scales_enter_as_stated():
     assert np.allclose(out2 * 2, base, rtol=1e-2, atol=1e-3)
 
 
-def test_decode_llama3_8b_batch64_sampled():
-    """Full-size launch (64 sequences of ~2k tokens, 32 q / 8 kv heads, D 128);
-    the oracle checks 12 sampled sequences, all heads."""
-    log("fp8 decode llama3-8B batch 64 (sampled)")
+def test_decode_llama3_8b_batch64_full():
+    """The 8B batch at full size (64 sequences of ~2k tokens, 32 q / 8 kv
+    heads, D 128) over fp8 pools: every sequence and head against the
+    oracle."""
+    log("fp8 decode llama3-8B batch 64 (full)")
     wl = make_decode(2)
     pool = fp8_pool_for(wl)
     pool.assert_codes_equal("config pools")
-    seqs = list(range(0, 64, 6))
-    ref = oracle_decode_fp8(wl, pool, seqs=seqs)
+    ref = oracle_decode_fp8(wl, pool)
     for part in (0, -1, 256):
         got = gpu_decode_fp8(wl, pool, part)
-        assert np.isfinite(got).all()
-        err = assert_close(got[seqs], ref[seqs], "bf16", f"partition {part}")
+        err = assert_close(got, ref, "bf16", f"partition {part}")
         log(f"  partition {part}: max abs err {err:.3g}")
 
 
@@ -283,17 +282,15 @@ def test_prefill_tiny_shapes(Hq, Hkv, prior, chunk):
     log(f"  max abs err {err:.3g}")
 
 
-def test_prefill_long_mixed_chunks_sampled():
+def test_prefill_long_mixed_chunks_full():
     """The long-context prefill batch (4 x 512-token chunks over 4096 prior
-    tokens) over fp8 pools; 24 sampled rows per request checked."""
-    log("fp8 prefill long mixed (sampled)")
+    tokens) over fp8 pools: every row and head against the oracle."""
+    log("fp8 prefill long mixed (full)")
     wl = make_prefill(5)
     pool = fp8_pool_for(wl)
     got = gpu_prefill_fp8(wl, pool)
-    assert np.isfinite(got).all()
-    rows = [int(wl.query_start_loc[r]) + i for r in range(wl.num_reqs) for i in range(0, 512, 22)]
-    ref = oracle_prefill_fp8(wl, pool, rows=rows)
-    err = assert_close(got[rows], ref[rows], "bf16", "long mixed fp8")
+    log("  oracle ...")
+    err = assert_close(got, oracle_prefill_fp8(wl, pool), "bf16", "long mixed fp8")
     log(f"  max abs err {err:.3g}")
 
 

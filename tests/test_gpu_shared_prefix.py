@@ -86,15 +86,13 @@ def test_workspace_reused_and_larger_bound():
     assert_close(c, _oracle_decode(wl), "bf16", "larger bound")
 
 
-def test_config4_shared_prefix_sampled():
+def test_config4_shared_prefix_full():
     """The shared-prefix batch at full size: 32 prompts x 4 samples, 2048-token
-    prompts, tails U[1, 256]; sampled sequences checked against the oracle."""
-    log("shared prefix config 4 (full launch, sampled check)")
+    prompts, tails U[1, 256]; every sequence against the oracle."""
+    log("shared prefix config 4 (full)")
     wl = make_decode(4)
     prefix = [wl.extra["prompt_len"]] * 32
     _check_shared_tables(wl, 4, prefix)
     out = to_f64(gpu_shared_prefix(wl, gpu_pool_for(wl), 4, prefix))
-    assert np.isfinite(out).all()
-    seqs = [0, 1, 3, 4, 37, 64, 99, 126, 127]
-    ref = _oracle_decode(wl, seqs=seqs)
-    assert_close(out[seqs], ref[seqs], "bf16", "config 4 shared prefix")
+    err = assert_close(out, _oracle_decode(wl), "bf16", "config 4 shared prefix")
+    log(f"  max abs err {err:.3g}")

@@ -174,17 +174,14 @@ def test_workspace_needs_no_initialisation_and_is_reusable():
 def test_verification_attention_batch64(k):
     """The target model's attention over the k + 1 appended positions of the
     64-sequence 8B batch (contexts U[128, 4096)), through pa_prefill_chunk;
-    12 sampled requests checked against the oracle, all rows finite."""
+    every request, row and head against the oracle."""
     log(f"verification attention k={k}")
     wl = make_spec_verify(k=k, vocab=8).attn
     out = to_f64(gpu_prefill(wl, gpu_pool_for(wl)))
-    assert np.isfinite(out).all()
-    reqs = list(range(0, 64, 6))
-    rows = [r for q in reqs for r in range(int(wl.query_start_loc[q]), int(wl.query_start_loc[q + 1]))]
     pk, pv = oracle_pools(wl, oracle)
     ref = oracle.prefill_chunk(wl.q, pk, pv, wl.block_tables, wl.query_start_loc, wl.context_lens,
-                               wl.scale, wl.dtype, rows=rows)
-    err = assert_close(out[rows], ref[rows], "bf16", f"k={k}")
+                               wl.scale, wl.dtype)
+    err = assert_close(out, ref, "bf16", f"k={k}")
     log(f"  max abs err {err:.3g}")
 
 
