@@ -221,6 +221,29 @@ int pa_decode_append(void* out, const void* q, const void* k, const void* v,
                      size_t workspace_bytes, const pa_cache_desc* desc, void* stream);
 
 /*
+ * pa_decode_append_noalloc — pa_decode_append for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and the same result (bitwise equal to
+ * pa_decode_append's for the same inputs).  The split-K partial states go to
+ * a scratch array inside the library, PA_NOALLOC_SCRATCH_BYTES bytes per GPU,
+ * held by every GPU the library runs on until the process ends; the call
+ * itself allocates nothing.  A call whose workspace
+ * (pa_decode_workspace_bytes) exceeds that size returns PA_ERR_WORKSPACE and
+ * launches nothing.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap on one GPU (two streams, or two threads) race and must be
+ * ordered by the caller.  The scratch needs no initial contents; each call
+ * overwrites what it reads.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int pa_decode_append_noalloc(void* out, const void* q, const void* k, const void* v,
+                             const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len,
+                             int32_t num_seqs, int32_t num_q_heads, float scale,
+                             int32_t partition_size, const pa_cache_desc* desc, void* stream);
+
+/*
  * pa_decode_shared_prefix — pa_decode for sequences that share a prompt
  * prefix (parallel sampling: several samples of one prompt point their block
  * tables at the same prompt blocks; zihan-zhang.net vLLM study, 3.2.2, and

@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     pa_copy_blocks,
     pa_decode,
     pa_decode_append,
+    pa_decode_append_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     pa_decode_partition_size,
     pa_decode_shared_prefix,
     pa_decode_shared_prefix_workspace_bytes,

@@ -80,6 +80,9 @@ def lib():
         L.pa_decode_append.argtypes = [P, P, P, P, P, P, P, P, i32, P, i32, i32, i32, f32, i32, P,
                                        sz, D, P]
         L.pa_decode_append.restype = ctypes.c_int
+        L.pa_decode_append_noalloc.argtypes = [P, P, P, P, P, P, P, P, i32, P, i32, i32, i32, f32,
+                                               i32, D, P]
+        L.pa_decode_append_noalloc.restype = ctypes.c_int
         L.pa_decode_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.pa_decode_shared_prefix_workspace_bytes.restype = sz
         L.pa_decode_shared_prefix.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, f32, P, i32, i32,
@@ -246,6 +249,33 @@ def pa_decode_append(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables,
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq,
         float(scale), int(partition_size), _ptr(workspace), ws_bytes, ctypes.byref(desc),
         _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # PA_NOALLOC_SCRATCH_BYTES in include/pa.h
+
+
+def pa_decode_append_noalloc(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables,
+                             context_lens, max_context_len: int, scale: float, desc: CacheDesc,
+                             partition_size: int = 0, stream=None):
+    """pa_decode_append without a workspace argument: the library's own static
+    scratch holds the split-K partial states (calls on one GPU must not
+    overlap)."""
+    torch = _torch()
+    for t, n in ((out, "out"), (q, "q"), (k, "k"), (v, "v"), (slot_mapping, "slot_mapping"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens")):
+        _dev(t, n)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    S, Hq, _ = q.shape
+    if k.shape[0] != S or v.shape[0] != S or slot_mapping.shape[0] != S:
+        raise ValueError("k, v and slot_mapping need one row per sequence")
+    _check(lib().pa_decode_append_noalloc(
+        _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, Hq,
+        float(scale), int(partition_size), ctypes.byref(desc), _stream(stream)))
 
 
 def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -272,6 +272,34 @@ int decode_call(void* out, const void* q, const void* new_k, const void* new_v,
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// The library's own decode scratch for pa_decode_append_noalloc: a file-scope
+// device array, one copy per GPU, held until the process ends.  Host code
+// never passes its name to a kernel (on the host that name is only a
+// stand-in); it uses the device address hipGetSymbolAddress returns, looked
+// up once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+int scratch_ptr(float** out) {
+  static std::mutex mu;
+  static float* ptrs[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(PA_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    ptrs[dev] = (float*)p;
+  }
+  *out = ptrs[dev];
+  return PA_OK;
+}
+
 }  // namespace
 
 PA_API int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -296,6 +324,39 @@ PA_API int pa_decode_append(void* out, const void* q, const void* k, const void*
   return decode_call(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
                      scale, partition_size, workspace, workspace_bytes, desc, stream);
+}
+
+PA_API int pa_decode_append_noalloc(void* out, const void* q, const void* k, const void* v,
+                                    const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    int32_t num_seqs, int32_t num_q_heads, float scale,
+                                    int32_t partition_size, const pa_cache_desc* desc,
+                                    void* stream) {
+  if (num_seqs > 0 && (!k || !v || !slot_mapping))
+    return fail(PA_ERR_NULL, "k, v and slot_mapping must be non-NULL");
+  pa::CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != PA_OK) return st;
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len < 0)
+    return decode_call(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables,
+                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                       scale, partition_size, nullptr, 0, desc, stream);
+  if (partition_size > 0 && partition_size % PA_BLOCK_SIZE != 0)
+    return fail(PA_ERR_SHAPE, "partition_size %d is not a multiple of 16", (int)partition_size);
+  const size_t need = decode_ws_bytes(num_seqs, num_q_heads, g.num_kv_heads, g.head_dim,
+                                      max_context_len, partition_size);
+  if (need > kScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_decode_append_noalloc: this call needs %zu bytes of scratch, the library's "
+                "static scratch holds %zu (use pa_decode_append with a workspace)",
+                need, kScratchBytes);
+  float* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != PA_OK) return st;
+  return decode_call(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                     scale, partition_size, ws, kScratchBytes, desc, stream);
 }
 
 namespace {
