@@ -699,7 +699,17 @@ def bench_spec_verify(timer, steps, warmup):
     def write():
         pa.pa_reshape_and_cache(nk, nv, ns, pool.k, pool.v, pool.desc)
 
+    max_ctx = int(a.context_lens.max())
+    Tq, Hq, D = a.q.shape
+    pws_bytes = pa.pa_prefill_chunk_workspace_bytes(a.num_reqs, Tq, k1, max_ctx, Hq, a.num_kv_heads,
+                                                    D, 0)
+    pws = torch.empty(max(1, (pws_bytes + 3) // 4), dtype=torch.float32, device="cuda")
+
     def attend():
+        pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, k1, float(a.scale), pool.desc,
+                            max_context_len=max_ctx, workspace=pws)
+
+    def attend_unsplit():
         pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, k1, float(a.scale), pool.desc)
 
     def sample():
@@ -714,6 +724,7 @@ def bench_spec_verify(timer, steps, warmup):
         step()
     round_cold = timer.calls(step, steps, cold=True)
     attn_cold = timer.calls(attend, steps, cold=True)
+    attn_unsplit_cold = timer.calls(attend_unsplit, steps, cold=True)
     samp_cold = timer.calls(sample, steps, cold=True)
     n = on.cpu().numpy()
     V = int(w.target_probs.shape[2])
@@ -724,7 +735,9 @@ def bench_spec_verify(timer, steps, warmup):
         "tokens_per_round_mean": round(float(n.mean()), 4),
         "round_cold": dist(round_cold),
         "tokens_per_s": round(float(n.sum()) / (np.median(round_cold) * 1e-3), 1),
+        "verify_attention_call": "pa_prefill_chunk, k + 1 rows per request, automatic split-K over the keys",
         "verify_attention_cold": dist(attn_cold, kv),
+        "verify_attention_unsplit_cold": dist(attn_unsplit_cold, kv),
         "rejection_sample_cold": dist(samp_cold, samp_bytes),
     }
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 #define PA_BLOCK_SIZE 16
 
 typedef enum {
@@ -357,17 +357,41 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n
  *                    position.
  *   block_tables     device int32 [num_reqs][max_blocks_per_seq]
  *   max_q_len        host bound on every n_r (sizes the grid)
+ *   max_context_len  host bound on every ctx_r (sizes a split; a context
+ *                    beyond it is cut to the bound when the call is split)
+ *   partition_size   split-K over the keys: 0 = automatic (only with a
+ *                    workspace; NULL workspace = no split), < 0 = no split,
+ *                    > 0 = keys per part (a multiple of 64).  Parts of one
+ *                    query tile leave partial softmax states that a second
+ *                    kernel merges with the online-softmax rescale (zihan-
+ *                    zhang.net vLLM study, 4.3.1), as pa_decode's split-K.
+ *                    The automatic rule splits only calls of a few rows per
+ *                    request (speculative verification), whose long
+ *                    contexts would otherwise stream through one workgroup.
+ *   workspace        device scratch of pa_prefill_chunk_workspace_bytes(...)
+ *                    bytes for the same sizes and partition_size, or NULL;
+ *                    a split call with a smaller one returns
+ *                    PA_ERR_WORKSPACE.  Contents need no initialisation; two
+ *                    calls in flight at once must not share one.
  * Uses bf16 MFMA for Q K^T and P V with fp32 accumulation and an fp32
  * online-softmax state; P is rounded to bf16 before the P V product.  fp8
  * codes are widened exactly to bf16 after the LDS read; the K scale is folded
  * into `scale` and the V scale into the normalisation.  With k + 1 rows per
- * request this is the verification attention of speculative decoding.
+ * request this is the verification attention of speculative decoding
+ * (zihan-zhang.net vLLM study, 4.1.1: the target scores the k drafted
+ * positions in one pass).
  */
+size_t pa_prefill_chunk_workspace_bytes(int32_t num_reqs, int32_t total_q_tokens,
+                                        int32_t max_q_len, int32_t max_context_len,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t partition_size);
 int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* query_start_loc, const int32_t* context_lens,
                      int32_t num_reqs, int32_t total_q_tokens, int32_t max_q_len,
-                     int32_t num_q_heads, float scale, const pa_cache_desc* desc, void* stream);
+                     int32_t max_context_len, int32_t num_q_heads, float scale,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes,
+                     const pa_cache_desc* desc, void* stream);
 
 /*
  * pa_rejection_sample — the verification step of speculative decoding

@@ -28,6 +28,7 @@ from .binding import (  # noqa: F401
     pa_decode_shared_prefix_workspace_bytes,
     pa_decode_workspace_bytes,
     pa_prefill_chunk,
+    pa_prefill_chunk_workspace_bytes,
     pa_rejection_sample,
     pa_rejection_sample_workspace_bytes,
     pa_reshape_and_cache,

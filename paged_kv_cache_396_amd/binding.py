@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # PA_LIB may name another build of the same library (e.g. a tuning variant)
 LIB_PATH = os.environ.get("PA_LIB") or os.path.join(PKG, "libpa.so")
 
-ABI_VERSION = 2  # the pa_cache_desc layout below
+ABI_VERSION = 3  # the entry points and pa_cache_desc layout below
 PA_F32 = 0
 PA_BF16 = 1
 PA_FP8_E4M3 = 2
@@ -88,7 +88,10 @@ def lib():
         L.pa_decode_shared_prefix.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, f32, P, i32, i32,
                                               P, sz, D, P]
         L.pa_decode_shared_prefix.restype = ctypes.c_int
-        L.pa_prefill_chunk.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, i32, f32, D, P]
+        L.pa_prefill_chunk_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+        L.pa_prefill_chunk_workspace_bytes.restype = sz
+        L.pa_prefill_chunk.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, f32, i32,
+                                       P, sz, D, P]
         L.pa_prefill_chunk.restype = ctypes.c_int
         i64 = ctypes.c_int64
         L.pa_pool_create.argtypes = [i32]
@@ -307,9 +310,20 @@ def pa_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens
         ctypes.byref(desc), _stream(stream)))
 
 
+def pa_prefill_chunk_workspace_bytes(num_reqs, total_q_tokens, max_q_len, max_context_len,
+                                     num_q_heads, num_kv_heads, head_dim, partition_size=0) -> int:
+    return int(lib().pa_prefill_chunk_workspace_bytes(num_reqs, total_q_tokens, max_q_len,
+                                                      max_context_len, num_q_heads, num_kv_heads,
+                                                      head_dim, partition_size))
+
+
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
-                     max_q_len: int, scale: float, desc: CacheDesc, stream=None):
-    """Causal chunk attention; ``q``/``out`` are [total_q, Hq, D] (bf16)."""
+                     max_q_len: int, scale: float, desc: CacheDesc, stream=None,
+                     max_context_len=None, partition_size: int = 0, workspace=None):
+    """Causal chunk attention; ``q``/``out`` are [total_q, Hq, D] (bf16).  With a
+    ``workspace`` (and ``max_context_len``, the host bound on every context)
+    long contexts may be split over the keys (``partition_size`` 0 = automatic,
+    < 0 = never, > 0 = keys per part); without one the call is unsplit."""
     torch = _torch()
     for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (block_tables, "block_tables"), (query_start_loc, "query_start_loc"),
@@ -319,11 +333,20 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, co
                  (context_lens, "context_lens")):
         if t.dtype != torch.int32:
             raise ValueError(f"{n} must be int32")
+    if max_context_len is None:
+        if workspace is not None or partition_size > 0:
+            raise ValueError("a split prefill needs max_context_len")
+        max_context_len = 0
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
     Tq, Hq, _ = q.shape
     R = context_lens.shape[0]
     _check(lib().pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(block_tables), block_tables.shape[1], _ptr(query_start_loc),
-                                  _ptr(context_lens), R, Tq, int(max_q_len), Hq, float(scale),
+                                  _ptr(context_lens), R, Tq, int(max_q_len), int(max_context_len),
+                                  Hq, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
                                   ctypes.byref(desc), _stream(stream)))
 
 

@@ -476,21 +476,81 @@ PA_API int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache
   return ok();
 }
 
+namespace {
+
+#ifndef PA_PF_SPLIT_FACTOR
+#define PA_PF_SPLIT_FACTOR 1
+#endif
+#ifndef PA_PF_SPLIT_MIN_KEYS
+#define PA_PF_SPLIT_MIN_KEYS 512
+#endif
+
+// Keys per part of a split prefill call, or 0 for no split.  Automatic:
+// only the narrow variant (a few query rows per request: speculative
+// verification, short chunks) is split, and only when its (request, kv
+// head) workgroups do not fill the resident slots (two per compute unit):
+// then each context is cut into parts so that the slots fill.  A batch that
+// already fills them is not split: on the 64-request verification batch
+// (contexts U[128, 4096)) parts of 512 to 2048 keys measured equal or
+// slower than whole contexts.  The wide variant keeps its compute units
+// busy on the matrix cores and is not split.
+int32_t prefill_part_keys(int32_t num_reqs, int32_t num_kv_heads, int32_t max_q_len, int32_t group,
+                          int32_t max_ctx, int32_t req) {
+  if (req < 0 || max_ctx <= 0) return 0;
+  if (req > 0) return req;
+  if (!pa::prefill_narrow(max_q_len, group)) return 0;
+  const int64_t qt = pa::prefill_tile_queries(max_q_len, group);
+  const int64_t units = (int64_t)num_reqs * num_kv_heads * ((max_q_len + qt - 1) / qt);
+  const int64_t slots = 2 * (int64_t)device_cu_count();
+  const int64_t target = (PA_PF_SPLIT_FACTOR * slots + units - 1) / (units > 0 ? units : 1);
+  if (target <= 1) return 0;
+  int64_t part = ((max_ctx + target - 1) / target + 63) / 64 * 64;
+  if (part < PA_PF_SPLIT_MIN_KEYS) part = PA_PF_SPLIT_MIN_KEYS;
+  return part >= max_ctx ? 0 : (int32_t)part;
+}
+
+size_t prefill_ws_bytes(int32_t total_q_tokens, int32_t num_q_heads, int32_t head_dim,
+                        int32_t max_ctx, int32_t part) {
+  if (part <= 0) return 0;
+  const int64_t parts = ((int64_t)max_ctx + part - 1) / part;
+  if (parts <= 1) return 0;
+  return pa::prefill_ws_floats((int64_t)total_q_tokens * num_q_heads, (int)parts, head_dim) *
+         sizeof(float);
+}
+
+}  // namespace
+
+PA_API size_t pa_prefill_chunk_workspace_bytes(int32_t num_reqs, int32_t total_q_tokens,
+                                               int32_t max_q_len, int32_t max_context_len,
+                                               int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t partition_size) {
+  if (num_reqs <= 0 || total_q_tokens <= 0 || max_q_len <= 0 || max_context_len <= 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0)
+    return 0;
+  if (partition_size > 0 && partition_size % 64 != 0) return 0;
+  const int32_t part = prefill_part_keys(num_reqs, num_kv_heads, max_q_len,
+                                         num_q_heads / num_kv_heads, max_context_len,
+                                         partition_size);
+  return prefill_ws_bytes(total_q_tokens, num_q_heads, head_dim, max_context_len, part);
+}
+
 PA_API int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* query_start_loc, const int32_t* context_lens,
                             int32_t num_reqs, int32_t total_q_tokens, int32_t max_q_len,
-                            int32_t num_q_heads, float scale, const pa_cache_desc* desc,
-                            void* stream) {
+                            int32_t max_context_len, int32_t num_q_heads, float scale,
+                            int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            const pa_cache_desc* desc, void* stream) {
   pa::CacheGeom g;
   int st = check_desc(desc, &g);
   if (st != PA_OK) return st;
-  if (num_reqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_blocks_per_seq < 1 ||
-      num_q_heads < 1)
+  if (num_reqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_context_len < 0 ||
+      max_blocks_per_seq < 1 || num_q_heads < 1)
     return fail(PA_ERR_SHAPE,
-                "num_reqs %d, total_q_tokens %d, max_q_len %d, max_blocks_per_seq %d, num_q_heads %d",
-                (int)num_reqs, (int)total_q_tokens, (int)max_q_len, (int)max_blocks_per_seq,
-                (int)num_q_heads);
+                "num_reqs %d, total_q_tokens %d, max_q_len %d, max_context_len %d, "
+                "max_blocks_per_seq %d, num_q_heads %d",
+                (int)num_reqs, (int)total_q_tokens, (int)max_q_len, (int)max_context_len,
+                (int)max_blocks_per_seq, (int)num_q_heads);
   if (num_q_heads % g.num_kv_heads != 0)
     return fail(PA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 (int)num_q_heads, g.num_kv_heads);
@@ -498,12 +558,22 @@ PA_API int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const
   if (!pa::prefill_supported(g.elem_bytes, g.head_dim, group))
     return fail(PA_ERR_UNSUPPORTED, "prefill variant dtype=%d head_dim=%d group=%d is not built",
                 (int)desc->dtype, g.head_dim, group);
+  if (partition_size > 0 && partition_size % 64 != 0)
+    return fail(PA_ERR_SHAPE, "partition_size %d is not a multiple of 64", (int)partition_size);
   if (num_reqs == 0 || total_q_tokens == 0 || max_q_len == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
     return fail(PA_ERR_NULL, "prefill pointers must be non-NULL");
-  const int64_t qt = pa::prefill_queries_per_tile(group);
-  if ((max_q_len + qt - 1) / qt * (int64_t)num_reqs * g.num_kv_heads >= ((int64_t)1 << 31) ||
-      (int64_t)total_q_tokens * num_q_heads * g.head_dim >= ((int64_t)1 << 40))
+  // automatic with no workspace: unsplit
+  const int32_t part =
+      (partition_size == 0 && !workspace)
+          ? 0
+          : prefill_part_keys(num_reqs, g.num_kv_heads, max_q_len, group, max_context_len,
+                              partition_size);
+  const int64_t parts = part > 0 ? ((int64_t)max_context_len + part - 1) / part : 1;
+  const int64_t qt = pa::prefill_tile_queries(max_q_len, group);
+  if ((max_q_len + qt - 1) / qt * (int64_t)num_reqs * g.num_kv_heads * parts >= ((int64_t)1 << 31) ||
+      (int64_t)num_reqs * max_q_len * num_q_heads >= ((int64_t)1 << 31) ||
+      (int64_t)total_q_tokens * num_q_heads * g.head_dim * (parts > 1 ? parts : 1) >= ((int64_t)1 << 40))
     return fail(PA_ERR_OVERFLOW, "prefill grid too large");
   pa::PrefillArgs a;
   a.out = out;
@@ -519,6 +589,15 @@ PA_API int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const
   a.max_q_len = max_q_len;
   a.num_q_heads = num_q_heads;
   a.scale = scale;
+  if (parts > 1) {
+    const size_t need = prefill_ws_bytes(total_q_tokens, num_q_heads, g.head_dim, max_context_len, part);
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "prefill workspace of %zu bytes needed, %zu given (ptr %p)",
+                  need, workspace_bytes, workspace);
+    a.max_parts = (int)parts;
+    a.part_keys = part;
+    a.ws = (float*)workspace;
+  }
   hipError_t e = pa::launch_prefill(a, g, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();

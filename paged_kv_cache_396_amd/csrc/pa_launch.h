@@ -80,12 +80,29 @@ struct PrefillArgs {
   int max_q_len;
   int num_q_heads;
   float scale;
+  // split-K over the keys (max_parts > 1): parts of part_keys keys (a
+  // multiple of 64); ws holds prefill_ws_floats(total_q_tokens *
+  // num_q_heads, max_parts, head_dim) floats
+  int max_parts = 1;
+  int part_keys = 0;
+  float* ws = nullptr;
 };
+
+// Floats of a split prefill's workspace: m and l of every (row, q head,
+// part) slot, then o from a 16-byte boundary.
+inline size_t prefill_ws_floats(int64_t rows, int parts, int head_dim) {
+  const int64_t slots = rows * parts;
+  return (size_t)((2 * slots + 3) / 4 * 4 + slots * head_dim);
+}
 
 bool prefill_supported(int elem_bytes, int head_dim, int group);
 
 // Query rows one prefill workgroup covers for GQA group size `group`.
 int prefill_queries_per_tile(int group);
+// Query rows per tile of the variant a call with this max_q_len launches.
+int prefill_tile_queries(int max_q_len, int group);
+// True if a call with this max_q_len launches the narrow (4-wave) variant.
+bool prefill_narrow(int max_q_len, int group);
 
 hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t stream);
 

@@ -129,7 +129,21 @@ struct PrefillParams {
   int prefix_partition;
   int prefix_parts;  // grid extent (partitions of the longest prefix)
   int ws_stride;
+  // split chunk mode (max_parts > 1): workgroup (tile, request, kv head,
+  // part) covers keys [part * part_keys, +part_keys) of its tile's need;
+  // tiles needing more than one part leave partial states in slot
+  // row * ws_stride + part (ws_stride = max_parts) for prefill_merge_kernel
+  int part_keys;
+  int max_parts;
+  int qt;  // queries per tile of the launched variant
 };
+
+// Keys a query tile of request r needs (the chunk's rows up to q_end see
+// keys 0 .. prior + q_end - 1), clamped to the context and, when split, to
+// the grid's parts.
+__device__ inline int pf_tile_keys(int ctx, int prior, int q_end) {
+  return max(0, min(ctx, prior + q_end));
+}
 
 // Row order of a 16-key block in LDS: row m holds key pf_key16(m), i.e. the
 // rows of quads 1 and 2 are swapped.  With this order the accumulator
@@ -216,13 +230,16 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // prefix partition).
   const int L = blockIdx.x;
   int g, r, qs, n_r, q0, ctx, kbeg, nk, part = 0, prior;
+  bool partial = PFX;  // leaves a partial state instead of a normalised row
   if constexpr (!PFX) {
-    const int N = p.num_qtiles * p.num_reqs * p.num_kv_heads;
+    const int N = p.num_qtiles * p.num_reqs * p.num_kv_heads * p.max_parts;
     const int xcd = L & 7, slot = L >> 3;
     const int per = N >> 3, rem = N & 7;
     const int logical = xcd * per + min(xcd, rem) + slot;
     const int tile = logical % p.num_qtiles;
-    const int pair = logical / p.num_qtiles;
+    const int rest = logical / p.num_qtiles;
+    part = rest % p.max_parts;
+    const int pair = rest / p.max_parts;
     g = pair % p.num_kv_heads;
     r = pair / p.num_kv_heads;
     qs = p.query_start_loc[r];
@@ -232,12 +249,17 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     n_r = qe - qs;
     q0 = tile * QT;
     if (q0 >= n_r) return;  // uniform
-    const int ctx_cap = p.max_blocks_per_seq * kBlock;
+    const int ctx_cap = min(p.max_blocks_per_seq * kBlock, p.max_parts * p.part_keys);
     ctx = max(0, min(p.context_lens[r], ctx_cap));
     prior = ctx - n_r;  // < 0 only for out-of-contract input
     const int q_end = min(n_r, q0 + QT);
-    kbeg = 0;
-    nk = max(0, min(ctx, prior + q_end));  // keys this workgroup needs
+    nk = pf_tile_keys(ctx, prior, q_end);  // keys this tile needs
+    kbeg = part * p.part_keys;
+    if (p.max_parts > 1) {
+      if (kbeg >= nk && part > 0) return;  // uniform
+      partial = nk > p.part_keys;          // the tile needs more than one part
+      nk = min(nk, kbeg + p.part_keys);
+    }
   } else {
     part = L % p.prefix_parts;
     const int pair = L / p.prefix_parts;
@@ -675,7 +697,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     const int c = 32 * (w * NCB + cb) + cw;
     const int qi = q0 + c / G;
     if (qi >= n_r) continue;
-    if constexpr (PFX) {
+    if (partial) {  // uniform
       const int64_t slot = ((int64_t)(qs + qi) * p.num_q_heads + g * G + c % G) * p.ws_stride + part;
       if (half == 0) {
         p.ws_m[slot] = m_run[cb];
@@ -708,6 +730,77 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   }
 }
 
+// Merge of a split chunk: one wave per (request, query row, q head).  The
+// row's query tile needed nk keys, cut into ceil(nk / part_keys) parts whose
+// partial states (running max in log2 units, sum, unnormalised output) are
+// combined with the online-softmax rescale:
+//   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  out = sum_p O_p 2^(m_p - M) / L.
+// Rows whose tile needed one part were written by the chunk kernel.
+template <int D, int KB>
+__global__ __launch_bounds__(kWave) void prefill_merge_kernel(PrefillParams p, int max_q_len) {
+  const int h = blockIdx.x % p.num_q_heads;
+  const int ri = blockIdx.x / p.num_q_heads;
+  const int i = ri % max_q_len;
+  const int r = ri / max_q_len;
+  const int lane = threadIdx.x;
+  constexpr int XL = D / kWave;  // dims per lane
+  int qs = p.query_start_loc[r];
+  int qe = p.query_start_loc[r + 1];
+  const int ctx_raw = p.context_lens[r];
+  qs = max(0, min(qs, p.total_q_tokens));
+  qe = max(qs, min(qe, p.total_q_tokens));
+  const int n_r = qe - qs;
+  if (i >= n_r) return;
+  const int ctx_cap = min(p.max_blocks_per_seq * kBlock, p.max_parts * p.part_keys);
+  const int ctx = max(0, min(ctx_raw, ctx_cap));
+  const int prior = ctx - n_r;
+  const int q_end = min(n_r, (i / p.qt + 1) * p.qt);
+  const int nk = pf_tile_keys(ctx, prior, q_end);
+  if (nk <= p.part_keys) return;  // written by the chunk kernel
+  const int nparts = (nk + p.part_keys - 1) / p.part_keys;
+  const int64_t row = (int64_t)(qs + i) * p.num_q_heads + h;
+  const float* wm = p.ws_m + row * p.ws_stride;
+  const float* wl = p.ws_l + row * p.ws_stride;
+  const float* wo = p.ws_o + row * p.ws_stride * D;
+  float acc[XL];
+#pragma unroll
+  for (int e = 0; e < XL; ++e) acc[e] = 0.f;
+  float L = 0.f, M = kPfNegBig;
+  constexpr int PG = 8;  // partial states loaded together
+  for (int q0 = 0; q0 < nparts; q0 += PG) {
+    float mq[PG], lq[PG], oq[PG][XL];
+#pragma unroll
+    for (int j = 0; j < PG; ++j) {
+      const int q = min(q0 + j, nparts - 1);
+      mq[j] = wm[q];
+      lq[j] = wl[q];
+#pragma unroll
+      for (int e = 0; e < XL; ++e) oq[j][e] = wo[(int64_t)q * D + lane + e * kWave];
+    }
+    float Mg = M;
+#pragma unroll
+    for (int j = 0; j < PG; ++j)
+      if (q0 + j < nparts) Mg = fmaxf(Mg, mq[j]);
+    const float rs = exp2f(M - Mg);  // rescale of what was merged so far
+    L *= rs;
+#pragma unroll
+    for (int e = 0; e < XL; ++e) acc[e] *= rs;
+#pragma unroll
+    for (int j = 0; j < PG; ++j) {
+      const float f = q0 + j < nparts ? exp2f(mq[j] - Mg) : 0.f;
+      L = fmaf(lq[j], f, L);
+#pragma unroll
+      for (int e = 0; e < XL; ++e) acc[e] = fmaf(oq[j][e], f, acc[e]);
+    }
+    M = Mg;
+  }
+  float inv = L > 0.f ? 1.f / L : 0.f;
+  if constexpr (KB == 1) inv *= p.v_scale;
+  uint16_t* orow = (uint16_t*)p.out + row * D;
+#pragma unroll
+  for (int e = 0; e < XL; ++e) orow[lane + e * kWave] = to_bf16(acc[e] * inv);
+}
+
 // Query rows one workgroup of W waves covers for GQA group size G.
 constexpr int pf_queries(int W, int G) { return W * 32 * PA_PF_NCB / G; }
 
@@ -718,18 +811,22 @@ inline bool pf_narrow(int rows, int G) { return rows <= pf_queries(kPfNarrowWave
 template <int D, int G, int KB>
 static hipError_t launch_prefill_t(PrefillParams prm, int max_q_len, hipStream_t stream) {
   constexpr int NCB = PA_PF_NCB;
-  if (pf_narrow(max_q_len, G)) {
-    prm.num_qtiles = 1;
-    const int64_t grid = (int64_t)prm.num_reqs * prm.num_kv_heads;
+  const bool narrow = pf_narrow(max_q_len, G);
+  prm.qt = narrow ? pf_queries(kPfNarrowWaves, G) : pf_queries(kPfWaves, G);
+  prm.num_qtiles = (max_q_len + prm.qt - 1) / prm.qt;
+  const int64_t grid = (int64_t)prm.num_qtiles * prm.num_reqs * prm.num_kv_heads * prm.max_parts;
+  if (narrow) {
     hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, false, kPfNarrowWaves, kPfNarrowStages, KB>),
                        dim3((unsigned)grid), dim3(kPfNarrowWaves * kWave), 0, stream, prm);
-    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, false, kPfWaves, kPfStages, KB>),
+                       dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, prm);
   }
-  const int qt = pf_queries(kPfWaves, G);
-  prm.num_qtiles = (max_q_len + qt - 1) / qt;
-  const int64_t grid = (int64_t)prm.num_qtiles * prm.num_reqs * prm.num_kv_heads;
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, false, kPfWaves, kPfStages, KB>),
-                     dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || prm.max_parts <= 1) return e;
+  hipLaunchKernelGGL((prefill_merge_kernel<D, KB>),
+                     dim3((unsigned)((int64_t)prm.num_reqs * max_q_len * prm.num_q_heads)),
+                     dim3(kWave), 0, stream, prm, max_q_len);
   return hipGetLastError();
 }
 
@@ -748,6 +845,12 @@ static hipError_t launch_prefix_t(const PrefillParams& prm, int num_groups, hipS
 }
 
 int prefill_queries_per_tile(int group) { return pf_queries(kPfWaves, group); }
+
+bool prefill_narrow(int max_q_len, int group) { return pf_narrow(max_q_len, group); }
+
+int prefill_tile_queries(int max_q_len, int group) {
+  return pf_narrow(max_q_len, group) ? pf_queries(kPfNarrowWaves, group) : pf_queries(kPfWaves, group);
+}
 
 
 hipError_t launch_prefix_partials(const SharedPrefixArgs& a, const CacheGeom& g, hipStream_t stream) {
@@ -798,7 +901,7 @@ bool shared_prefix_supported(int elem_bytes, int head_dim, int group, int group_
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t stream) {
-  PrefillParams p;
+  PrefillParams p = {};
   p.out = a.out;
   p.q = (const char*)a.q;
   p.k_cache = (const char*)a.k_cache;
@@ -815,6 +918,17 @@ hipError_t launch_prefill(const PrefillArgs& a, const CacheGeom& g, hipStream_t 
   // fp8 pools: the K scale multiplies every score, the V scale the output
   p.scale_log2 = a.scale * g.k_scale * kLog2e;
   p.v_scale = g.v_scale;
+  // split: parts of part_keys keys, partial states in the workspace
+  // [rows][max_parts] m, then l, then o (from a 16-byte boundary)
+  p.max_parts = a.max_parts > 1 ? a.max_parts : 1;
+  p.part_keys = a.max_parts > 1 ? a.part_keys : (1 << 30);
+  if (p.max_parts > 1) {
+    const int64_t slots = (int64_t)a.total_q_tokens * a.num_q_heads * p.max_parts;
+    p.ws_stride = p.max_parts;
+    p.ws_m = a.ws;
+    p.ws_l = a.ws + slots;
+    p.ws_o = a.ws + (2 * slots + 3) / 4 * 4;
+  }
   const int G = a.num_q_heads / g.num_kv_heads;
 
 #define PA_PREFILL_CASE(KB_, D_, G_)                  \

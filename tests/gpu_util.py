@@ -165,9 +165,13 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
     return float(err.max()) if err.size else 0.0
 
 
-def gpu_prefill(wl, pool, max_q_len=None, query_start_loc=None, context_lens=None):
+def gpu_prefill(wl, pool, max_q_len=None, query_start_loc=None, context_lens=None,
+                partition_size=None, workspace_fill=None):
     """Run pa_prefill_chunk on a PrefillWorkload whose pool already holds the
-    prior and chunk K/V; returns the device output [total_q, Hq, D]."""
+    prior and chunk K/V; returns the device output [total_q, Hq, D].  With
+    ``partition_size`` (0 automatic, > 0 keys per part) the call gets a
+    workspace of the size the library asks for (filled with
+    ``workspace_fill`` if given) and may be split over the keys."""
     t = torch()
     q = to_dev(wl.q, wl.dtype)
     out = t.empty_like(q)
@@ -177,9 +181,36 @@ def gpu_prefill(wl, pool, max_q_len=None, query_start_loc=None, context_lens=Non
     qsl = t.from_numpy(np.ascontiguousarray(qsl_np, dtype=np.int32)).cuda()
     cl = t.from_numpy(np.ascontiguousarray(cl_np, dtype=np.int32)).cuda()
     mq = int(np.diff(qsl_np).max()) if max_q_len is None else int(max_q_len)
-    pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, mq, float(wl.scale), pool.desc)
+    if partition_size is None:
+        pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, mq, float(wl.scale), pool.desc)
+    else:
+        max_ctx = int(np.max(cl_np))
+        Tq, Hq, D = wl.q.shape
+        nb = pa.pa_prefill_chunk_workspace_bytes(len(cl_np), Tq, mq, max_ctx, Hq, wl.num_kv_heads, D,
+                                                 partition_size)
+        ws = t.empty(max(1, (nb + 3) // 4), dtype=t.float32, device="cuda")
+        if workspace_fill is not None:
+            ws.fill_(workspace_fill)
+        pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, mq, float(wl.scale), pool.desc,
+                            max_context_len=max_ctx, partition_size=partition_size, workspace=ws)
     t.cuda.synchronize()
     return out
+
+
+def prefill_splits(wl, max_q_len, partition_size):
+    """Parts per (row, head) a prefill call would use (1 = unsplit)."""
+    Tq, Hq, D = wl.q.shape
+    max_ctx = int(np.max(wl.context_lens))
+    nb = pa.pa_prefill_chunk_workspace_bytes(wl.num_reqs, Tq, max_q_len, max_ctx, Hq, wl.num_kv_heads,
+                                             D, partition_size)
+    if nb == 0:
+        return 1
+    # nb = 4 * ((2 S + 3) // 4 * 4 + S D) with S = rows * heads * parts
+    for parts in range(2, 4097):
+        S = Tq * Hq * parts
+        if 4 * ((2 * S + 3) // 4 * 4 + S * D) == nb:
+            return parts
+    raise AssertionError("workspace size matches no part count")
 
 
 def shared_prefix_workspace(S, Hq, Hkv, D, max_ctx, group_size, max_prefix):

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = pa.lib()
-    assert L.pa_abi_version() == 2
+    assert L.pa_abi_version() == 3
     assert L.pa_status_string(0) == b"ok"
     assert L.pa_status_string(-5) == b"workspace too small"
     assert L.pa_status_string(123) == b"unknown status"
@@ -164,10 +164,41 @@ def test_prefill_argument_errors():
     z = ctypes.c_void_p(0)
     d32 = pa.cache_desc(16, 2, 128, pa.PA_F32)
     d16 = pa.cache_desc(16, 2, 128, pa.PA_BF16)
+    one = ctypes.c_void_p(1)
+
+    def call(desc, num_reqs=1, max_ctx=100, heads=8, part=0, ws=z, ws_bytes=0, ptr=z, max_q=8):
+        return L.pa_prefill_chunk(ptr, ptr, ptr, ptr, ptr, 4, ptr, ptr, num_reqs, 8, max_q, max_ctx,
+                                  heads, 0.1, part, ws, ws_bytes, ctypes.byref(desc), z)
+
     # fp32 prefill is not built (MFMA path is bf16)
-    assert L.pa_prefill_chunk(z, z, z, z, z, 4, z, z, 1, 8, 8, 8, 0.1, ctypes.byref(d32), z) == -4
-    assert L.pa_prefill_chunk(z, z, z, z, z, 4, z, z, 1, 8, 8, 7, 0.1, ctypes.byref(d16), z) == -2
-    assert L.pa_prefill_chunk(z, z, z, z, z, 4, z, z, -1, 8, 8, 8, 0.1, ctypes.byref(d16), z) == -2
+    assert call(d32) == -4
+    assert call(d16, heads=7) == -2
+    assert call(d16, num_reqs=-1) == -2
+    assert call(d16, max_ctx=-1) == -2
+    assert call(d16, part=100) == -2           # not a multiple of 64
+    assert call(d16, num_reqs=0) == 0          # nothing to do
+    # a requested split needs its workspace: refused before any launch
+    need = L.pa_prefill_chunk_workspace_bytes(1, 8, 8, 4096, 8, 2, 128, 512)
+    assert need > 0
+    assert call(d16, max_ctx=4096, part=512, ptr=one) == -5
+    assert call(d16, max_ctx=4096, part=512, ptr=one, ws=one, ws_bytes=need - 4) == -5
+
+
+def test_prefill_workspace_sizes():
+    L = pa.lib()
+    # 8 rows, 8 q heads, D 128, parts of 512 keys over 4096: 8 parts per (row, head)
+    slots = 8 * 8 * 8
+    assert L.pa_prefill_chunk_workspace_bytes(1, 8, 8, 4096, 8, 2, 128, 512) == \
+        ((2 * slots + 3) // 4 * 4 + slots * 128) * 4
+    # no split: nothing needed
+    assert L.pa_prefill_chunk_workspace_bytes(1, 8, 8, 4096, 8, 2, 128, -1) == 0
+    assert L.pa_prefill_chunk_workspace_bytes(1, 8, 8, 400, 8, 2, 128, 512) == 0
+    # the wide variant (a 512-row chunk) is never split automatically
+    assert L.pa_prefill_chunk_workspace_bytes(4, 2048, 512, 4608, 32, 8, 128, 0) == 0
+    # a few rows per request, long contexts, too few requests to fill the
+    # chip: the automatic rule splits; enough requests: it does not
+    assert L.pa_prefill_chunk_workspace_bytes(16, 80, 5, 4096, 32, 8, 128, 0) > 0
+    assert L.pa_prefill_chunk_workspace_bytes(64, 320, 5, 4096, 32, 8, 128, 0) == 0
 
 
 def test_binding_raises_with_detail():

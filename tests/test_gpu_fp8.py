@@ -240,7 +240,7 @@ def test_decode_zero_length_context_gives_zeros():
 # chunked prefill over fp8 pools
 
 
-def gpu_prefill_fp8(wl, pool, max_q_len=None):
+def gpu_prefill_fp8(wl, pool, max_q_len=None, partition_size=None):
     t = torch()
     q = to_dev(wl.q, "bf16")
     out = t.empty_like(q)
@@ -248,7 +248,17 @@ def gpu_prefill_fp8(wl, pool, max_q_len=None):
     qsl = t.from_numpy(np.ascontiguousarray(wl.query_start_loc, dtype=np.int32)).cuda()
     cl = t.from_numpy(np.ascontiguousarray(wl.context_lens, dtype=np.int32)).cuda()
     mq = int(np.diff(wl.query_start_loc).max()) if max_q_len is None else max_q_len
-    pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, mq, float(wl.scale), pool.desc)
+    if partition_size is None:
+        pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, mq, float(wl.scale), pool.desc)
+    else:
+        Tq, Hq, D = wl.q.shape
+        max_ctx = int(wl.context_lens.max())
+        nb = pa.pa_prefill_chunk_workspace_bytes(wl.num_reqs, Tq, mq, max_ctx, Hq, wl.num_kv_heads,
+                                                 D, partition_size)
+        assert nb > 0, "expected a split call"
+        ws = t.full(((nb + 3) // 4,), float("nan"), dtype=t.float32, device="cuda")
+        pa.pa_prefill_chunk(out, q, pool.k, pool.v, bt, qsl, cl, mq, float(wl.scale), pool.desc,
+                            max_context_len=max_ctx, partition_size=partition_size, workspace=ws)
     t.cuda.synchronize()
     return to_f64(out)
 
@@ -300,6 +310,17 @@ def test_spec_verification_attention_over_fp8_pools():
     pool = fp8_pool_for(wl)
     got = gpu_prefill_fp8(wl, pool)
     assert_close(got, oracle_prefill_fp8(wl, pool), "bf16", "fp8 verification")
+
+
+@pytest.mark.parametrize("part", [0, 256])
+def test_spec_verification_attention_over_fp8_pools_split(part):
+    """Split over the keys (partial states in code units; the merge applies
+    the V scale)."""
+    log(f"fp8 verification attention k=4 split part={part}")
+    wl = make_spec_verify(batch=24, k=4, vocab=8).attn
+    pool = fp8_pool_for(wl)
+    got = gpu_prefill_fp8(wl, pool, max_q_len=5, partition_size=part)
+    assert_close(got, oracle_prefill_fp8(wl, pool), "bf16", "fp8 verification split")
 
 
 def test_prefill_last_row_matches_decode_over_the_same_codes():

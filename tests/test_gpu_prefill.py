@@ -169,3 +169,49 @@ def test_config5_mixed_step_one_pool():
     torch.cuda.synchronize()
     assert np.array_equal(raw_bits(seq.dout), d_conc)
     assert np.array_equal(raw_bits(seq.pout), p_conc)
+
+
+# ---- split-K over the keys: parts of a tile's keys leave partial states,
+# merged by a second kernel with the online-softmax rescale
+
+SPLIT_SHAPES = [
+    # D, Hq, Hkv, prior, chunk, partition_size
+    (128, 32, 8, (0, 5, 40, 700), (7, 16, 33, 3), 64),      # narrow; parts inside the chunk
+    (128, 32, 8, (300, 0, 1000), (5, 5, 5), 128),           # narrow, k + 1 rows
+    (128, 32, 8, (0, 90, 300), (200, 64, 97), 64),          # wide; causal diagonal across parts
+    (128, 8, 1, (33, 1500), (40, 1), 256),                  # G 8, ragged
+    (64, 16, 4, (2000, 17), (3, 70), 192),                  # D 64
+]
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,prior,chunk,part", SPLIT_SHAPES)
+def test_prefill_split_matches_oracle(D, Hq, Hkv, prior, chunk, part):
+    from gpu_util import prefill_splits
+
+    log(f"prefill split D={D} {Hq}/{Hkv} prior={prior} chunk={chunk} part={part}")
+    wl = make_tiny_prefill(seed=40 + part, prior=prior, chunk=chunk, Hq=Hq, Hkv=Hkv, D=D)
+    assert prefill_splits(wl, wl.max_q_len, part) > 1
+    pool = gpu_pool_for(wl)
+    ref = _oracle_prefill(wl)
+    got = to_f64(gpu_prefill(wl, pool, partition_size=part, workspace_fill=float("nan")))
+    err = assert_close(got, ref, "bf16", "split prefill")
+    log(f"  max abs err {err:.3g}")
+    whole = to_f64(gpu_prefill(wl, pool, partition_size=-1))
+    assert_close(whole, ref, "bf16", "unsplit prefill")
+
+
+def test_prefill_split_last_row_still_matches_decode():
+    wl = make_tiny_prefill(seed=9, prior=(3000, 1200), chunk=(5, 5), Hq=32, Hkv=8, D=128)
+    pool = gpu_pool_for(wl)
+    pre = to_f64(gpu_prefill(wl, pool, partition_size=512))
+    last = wl.query_start_loc[1:] - 1
+
+    class _Dec:
+        pass
+
+    d = _Dec()
+    d.q = wl.q[last]
+    d.dtype, d.num_kv_heads, d.scale = wl.dtype, wl.num_kv_heads, wl.scale
+    d.block_tables, d.context_lens = wl.block_tables, wl.context_lens
+    dec = to_f64(gpu_decode(d, pool))
+    assert_close(pre[last], dec, "bf16", "split last row vs decode")

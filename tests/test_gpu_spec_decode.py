@@ -185,6 +185,25 @@ def test_verification_attention_batch64(k):
     log(f"  max abs err {err:.3g}")
 
 
+@pytest.mark.parametrize("batch,k,part", [(16, 4, 0), (64, 4, 512), (8, 8, 0), (64, 1, 1024)])
+def test_verification_attention_split(batch, k, part):
+    """The same verification attention split over the keys (automatic on
+    batches too small to fill the chip, or parts of 512 / 1024 keys), with a
+    NaN-filled workspace: every request, row and head against the oracle."""
+    from gpu_util import prefill_splits
+
+    log(f"verification attention split batch={batch} k={k} part={part}")
+    wl = make_spec_verify(batch=batch, k=k, vocab=8).attn
+    assert prefill_splits(wl, k + 1, part) > 1, "expected a split call"
+    out = to_f64(gpu_prefill(wl, gpu_pool_for(wl), max_q_len=k + 1, partition_size=part,
+                             workspace_fill=float("nan")))
+    pk, pv = oracle_pools(wl, oracle)
+    ref = oracle.prefill_chunk(wl.q, pk, pv, wl.block_tables, wl.query_start_loc, wl.context_lens,
+                               wl.scale, wl.dtype)
+    err = assert_close(out, ref, "bf16", f"split k={k} part={part}")
+    log(f"  max abs err {err:.3g}")
+
+
 def test_verification_last_row_equals_decode():
     """The last of the k + 1 rows sees the whole context: it matches the
     oracle's decode attention of the same sequences."""
