@@ -917,26 +917,47 @@ void decode_balanced_kernel(DecodeParams p) {
 
   WaveDecoder<EB, D, G> wd;
   wd.init(lds.pbuf[w], p.scale_log2);
-  for (int s = lo; s < S; ++s) {
+  // The segments of the range, in sequence order.  A segment's block ids
+  // and q are requested before the previous segment's wave merge, so their
+  // memory round trip overlaps it.
+  auto next_segment = [&](int s) {  // first sequence >= s with blocks in the range, or S
+    for (; s < S; ++s) {
+      const int cs = __builtin_amdgcn_readfirstlane(cum[s]);
+      if (cs >= B1) return S;
+      const int ce = __builtin_amdgcn_readfirstlane(cum[s + 1]);
+      if (max(B0, cs) < min(B1, ce)) return s;  // else a sequence with no blocks
+    }
+    return S;
+  };
+  auto fetch = [&](int s) {  // ids of this wave's blocks of segment s; its q into wd.qv
     const int cs = __builtin_amdgcn_readfirstlane(cum[s]);
     const int ce = __builtin_amdgcn_readfirstlane(cum[s + 1]);
-    if (cs >= B1) break;
+    const int jb = max(B0, cs) - cs + w + NW * lane;
+    const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+    const int ids = jb < min(B1, ce) - cs ? bt[jb] : 0;
+    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::QRB, wd.qv);
+    return ids;
+  };
+  int s = next_segment(lo);
+  int my_ids = s < S ? fetch(s) : 0;
+  while (s < S) {
+    const int cs = __builtin_amdgcn_readfirstlane(cum[s]);
+    const int ce = __builtin_amdgcn_readfirstlane(cum[s + 1]);
     const int sb = max(B0, cs), se = min(B1, ce);
-    if (sb >= se) continue;  // a sequence with no blocks
     const int ctx = __builtin_amdgcn_readfirstlane(sctx[s]);
     const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-    const int b0 = sb - cs, b1 = se - cs;
-    const int jb = b0 + w + NW * lane;
-    const int my_ids = jb < b1 ? bt[jb] : 0;
-    wd.load_q((const char*)p.q + ((int64_t)s * p.num_q_heads + (int64_t)g * G) * C::QRB, wd.qv);
     wd.reset();
     const bool append = p.new_k != nullptr && se == ce && ctx > 0;
-    stream_blocks(wd, lds, p, bt, g, w, b0, b1, ctx, my_ids, append ? s : -1);
+    stream_blocks(wd, lds, p, bt, g, w, sb - cs, se - cs, ctx, my_ids, append ? s : -1);
+    const int s_next = next_segment(s + 1);
+    const int ids_next = s_next < S ? fetch(s_next) : 0;
     const bool whole = cs >= B0 && ce <= B1;
     const int slot = sb == B0 ? 0 : 1;
     finish_waves(wd, lds, p, w, s, g, whole,
                  ((int64_t)(g * p.num_ranges + range) * 2 + slot) * G, 1);
     __syncthreads();
+    s = s_next;
+    my_ids = ids_next;
   }
 }
 
