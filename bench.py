@@ -548,26 +548,39 @@ def prefill_flops(wl):
 
 
 def bench_bulk_write(wl, timer, steps):
-    """pa_reshape_and_cache of the 70B layer's whole history in one call:
-    524,288 tokens, each sequence's tokens in order into its shuffled blocks
-    (the shape of a prefill's cache fill)."""
+    """pa_reshape_and_cache of the 70B layer's KV in one call (the shape of a
+    prefill's cache fill), twice: every sequence's 2048 tokens (524,288 in
+    all; each sequence's run starts at a block boundary) and the 2047-token
+    histories alone (524,032; from the second sequence on, every run starts
+    mid-block in the input's groups of 16)."""
     import torch
 
     import paged_kv_cache_396_amd as pa
     from gpu_util import GpuPool, to_dev
 
     pool = GpuPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
-    k, v = to_dev(wl.hist_k, wl.dtype), to_dev(wl.hist_v, wl.dtype)
-    slots = torch.from_numpy(wl.hist_slots).cuda()
+    S, Hkv, D = wl.num_seqs, wl.num_kv_heads, wl.head_dim
+    n = int(wl.context_lens[0])
+    whole_k = np.concatenate([wl.hist_k.reshape(S, n - 1, Hkv, D), wl.new_k.reshape(S, 1, Hkv, D)], 1)
+    whole_v = np.concatenate([wl.hist_v.reshape(S, n - 1, Hkv, D), wl.new_v.reshape(S, 1, Hkv, D)], 1)
+    whole_s = np.concatenate([wl.hist_slots.reshape(S, n - 1), wl.new_slots.reshape(S, 1)], 1)
+    out = {}
+    for name, (kr, vr, sr) in (("whole_contexts", (whole_k.reshape(-1, Hkv, D), whole_v.reshape(-1, Hkv, D),
+                                                   whole_s.reshape(-1))),
+                               ("histories_2047", (wl.hist_k, wl.hist_v, wl.hist_slots))):
+        k, v = to_dev(kr, wl.dtype), to_dev(vr, wl.dtype)
+        slots = torch.from_numpy(np.ascontiguousarray(sr)).cuda()
 
-    def call():
-        pa.pa_reshape_and_cache(k, v, slots, pool.k, pool.v, pool.desc)
+        def call():
+            pa.pa_reshape_and_cache(k, v, slots, pool.k, pool.v, pool.desc)
 
-    call()
-    T = int(len(wl.hist_slots))
-    moved = 4 * T * wl.num_kv_heads * wl.head_dim * 2  # K and V read once and written once
-    cold = timer.calls(call, steps, cold=True)
-    return {"tokens": T, "bytes_moved": moved, "cold": dist(cold, moved)}
+        call()
+        T = int(len(sr))
+        moved = 4 * T * Hkv * D * 2  # K and V read once and written once
+        out[name] = {"tokens": T, "bytes_moved": moved,
+                     "cold": dist(timer.calls(call, steps, cold=True), moved)}
+        del k, v, slots
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -6,13 +6,17 @@
 // raw bits (no conversion), so the result is bit-exact by construction.
 //
 // One workgroup takes 16 consecutive input tokens of one kv head.
-//  * When they fill one whole block in order (slots s0, s0+1, .., s0+15 with
-//    s0 a multiple of 16: the shape of a bulk fill or of a prefill chunk),
-//    the K tile is written row by row and the V tile, which is dim-major in
-//    the pool, is transposed through LDS, so every store is a full 16 bytes.
-//  * Otherwise (a decode step's scattered tokens, padding, partial blocks)
-//    every token is scattered on its own: its K row as 16-byte stores, its V
-//    elements one by one, 16 elements apart.
+//  * When their slots are consecutive (s0, s0+1, .., s0+15: the tokens of a
+//    bulk fill or of a prefill chunk, wherever the run starts in the input
+//    and in its block) they fill the tail of block s0 / 16 from offset
+//    s0 % 16 and, unless s0 % 16 is 0, the head of the next block.  K rows
+//    are written row by row; V, dim-major in the pool, is transposed through
+//    LDS and written as 16-byte chunks of dim rows, with the one partial
+//    chunk per dim row and block at a run's edge written element by element.
+//  * Otherwise (a decode step's scattered tokens, padding, a group holding
+//    the end of one run and the start of another) every token is scattered
+//    on its own: its K row as 16-byte stores, its V elements one by one, 16
+//    elements apart.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -51,50 +55,74 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
       vr[u] = v[row_of(i0 + j) + x];
     }
   }
-  // The group fills one whole block in order when slot j is s0 + j for all
-  // 16 tokens, s0 a multiple of 16 inside the pool.
-  bool in_order = true;
+  // The group is one run when slot j is s0 + j for all 16 tokens, inside
+  // the pool.
+  bool in_run = true;
   if (tid < kBlock) {
     const bool real = i0 + tid < num_tokens;
     const int64_t s0 = slots[i0];
     const int64_t mine = real ? slots[i0 + tid] : -1;
     sl[tid] = mine;
-    in_order = real && s0 >= 0 && s0 % kBlock == 0 && s0 + kBlock <= pool_slots && mine == s0 + tid;
+    in_run = real && s0 >= 0 && s0 + kBlock <= pool_slots && mine == s0 + tid;
   }
-  const bool full = __syncthreads_and(in_order);
+  const bool run = __syncthreads_and(in_run);
 
-  if (full) {
-    const int64_t base = tile_base(sl[0] / kBlock, g, num_kv_heads, head_dim) * EB;  // bytes
+  if (run) {
+    // token j sits in block b0 at offset o0 + j, or (past the block) in
+    // block b0 + 1 at offset o0 + j - 16
+    const int64_t b0 = sl[0] / kBlock;
+    const int o0 = (int)(sl[0] - b0 * kBlock);
     const int stage_rb = RB + 16;
-    // K: the tile is the 16 rows one after another
+    auto tile_bytes = [&](int blk) { return tile_base(b0 + blk, g, num_kv_heads, head_dim) * EB; };
 #pragma unroll
     for (int u = 0; u < kCwMaxChunks; ++u) {
       const int c = tid + u * kCwThreads;
       if (c < nch) {
-        const int o = c / RC, x = c - o * RC;
-        k_cache[base / 16 + c] = kr[u];
-        *(uint4*)(vstage + o * stage_rb + x * 16) = vr[u];
+        const int j = c / RC, x = c - j * RC;
+        const int blk = o0 + j >= kBlock ? 1 : 0;
+        const int o = o0 + j - blk * kBlock;
+        k_cache[(tile_bytes(blk) + (int64_t)o * RB) / 16 + x] = kr[u];
+        *(uint4*)(vstage + j * stage_rb + x * 16) = vr[u];
       }
     }
     __syncthreads();
-    // V: chunk c of the tile is dim c / CPD, tokens TPC * (c % CPD) ..
+    // V: chunk c of a tile is dim c / CPD, offsets TPC * (c % CPD) ..; the
+    // run covers offsets o0 .. 15 of the first block and 0 .. o0 - 1 of the
+    // second
     constexpr int TPC = 16 / EB;       // tokens per 16-byte chunk
     constexpr int CPD = kBlock / TPC;  // chunks per dim row
-    for (int c = tid; c < head_dim * CPD; c += kCwThreads) {
-      const int x = c / CPD, t0 = (c - x * CPD) * TPC;
-      uint32_t w[4];
-      if constexpr (EB == 2) {
+    const int nblk = o0 > 0 ? 2 : 1;
+    for (int c = tid; c < nblk * head_dim * CPD; c += kCwThreads) {
+      const int blk = c / (head_dim * CPD);
+      const int cc = c - blk * head_dim * CPD;
+      const int x = cc / CPD, of = (cc - x * CPD) * TPC;
+      const int j0 = of - o0 + blk * kBlock;  // token at offset `of`
+      char* dst = v_cache + tile_bytes(blk) + (int64_t)cc * 16;
+      auto elem = [&](int j) -> uint32_t {
+        if constexpr (EB == 2) return *(const uint16_t*)(vstage + j * stage_rb + x * 2);
+        else return *(const uint32_t*)(vstage + j * stage_rb + x * 4);
+      };
+      if (j0 >= 0 && j0 + TPC <= kBlock) {
+        uint32_t w[4];
+        if constexpr (EB == 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = *(const uint16_t*)(vstage + (t0 + 2 * e) * stage_rb + x * 2);
-          const uint32_t hi = *(const uint16_t*)(vstage + (t0 + 2 * e + 1) * stage_rb + x * 2);
-          w[e] = lo | (hi << 16);
+          for (int e = 0; e < 4; ++e) w[e] = elem(j0 + 2 * e) | (elem(j0 + 2 * e + 1) << 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = elem(j0 + e);
         }
+        *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = *(const uint32_t*)(vstage + (t0 + e) * stage_rb + x * 4);
+        for (int e = 0; e < TPC; ++e) {
+          const int j = j0 + e;
+          if (j < 0 || j >= kBlock) continue;  // another run's slot: left alone
+          if constexpr (EB == 2)
+            *(uint16_t*)(dst + e * 2) = (uint16_t)elem(j);
+          else
+            *(uint32_t*)(dst + e * 4) = elem(j);
+        }
       }
-      *(uint4*)(v_cache + base + (int64_t)c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     return;
   }
@@ -144,7 +172,8 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
 // becomes 0x7F with x's sign bit (quantize4).
 
 // One workgroup takes 16 consecutive input tokens of one kv head, as the
-// bf16/fp32 kernel does.  Input chunk c (8 bf16 of one token) becomes 8 codes.
+// bf16/fp32 kernel does, with the same run and scatter paths.  Input chunk c
+// (8 bf16 of one token) becomes 8 codes.
 __global__ __launch_bounds__(kCwThreads) void cache_write_fp8_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slots,
     int num_tokens, int num_kv_heads, int head_dim, int64_t pool_slots, float k_scale,
@@ -167,26 +196,47 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_fp8_kernel(
     kq = make_uint2(quantize4(kr.x, kr.y, k_scale), quantize4(kr.z, kr.w, k_scale));
     vq = make_uint2(quantize4(vr.x, vr.y, v_scale), quantize4(vr.z, vr.w, v_scale));
   }
-  bool in_order = true;
+  bool in_run = true;
   if (tid < kBlock) {
     const bool real = i0 + tid < num_tokens;
     const int64_t s0 = slots[i0];
     const int64_t s = real ? slots[i0 + tid] : -1;
     sl[tid] = s;
-    in_order = real && s0 >= 0 && s0 % kBlock == 0 && s0 + kBlock <= pool_slots && s == s0 + tid;
+    in_run = real && s0 >= 0 && s0 + kBlock <= pool_slots && s == s0 + tid;
   }
-  const bool full = __syncthreads_and(in_order);
+  const bool run = __syncthreads_and(in_run);
   const uint8_t* vb = (const uint8_t*)&vq;
 
-  if (full) {
-    const int64_t base = tile_base(sl[0] / kBlock, g, num_kv_heads, head_dim);  // bytes
+  if (run) {
+    // token j sits in block b0 at offset o0 + j, or in block b0 + 1 at
+    // offset o0 + j - 16; vt holds the group's codes by token (x * 16 + j)
+    const int64_t b0 = sl[0] / kBlock;
+    const int o0 = (int)(sl[0] - b0 * kBlock);
     if (tid < nch) {
-      *(uint2*)(k_cache + base + j * head_dim + x * 8) = kq;
+      const int blk = o0 + j >= kBlock ? 1 : 0;
+      const int64_t base = tile_base(b0 + blk, g, num_kv_heads, head_dim);  // bytes
+      *(uint2*)(k_cache + base + (o0 + j - blk * kBlock) * head_dim + x * 8) = kq;
 #pragma unroll
       for (int e = 0; e < 8; ++e) vt[(x * 8 + e) * kBlock + j] = vb[e];
     }
     __syncthreads();
-    if (tid < head_dim) *(uint4*)(v_cache + base + tid * kBlock) = *(const uint4*)&vt[tid * kBlock];
+    if (o0 == 0) {
+      const int64_t base = tile_base(b0, g, num_kv_heads, head_dim);
+      if (tid < head_dim) *(uint4*)(v_cache + base + tid * kBlock) = *(const uint4*)&vt[tid * kBlock];
+      return;
+    }
+    // dim row x of the first block takes offsets o0 .. 15 (tokens 0 ..),
+    // of the second offsets 0 .. o0 - 1 (tokens 16 - o0 ..): byte stores,
+    // neighbouring threads on neighbouring bytes
+    for (int c = tid; c < 2 * head_dim * kBlock; c += kCwThreads) {
+      const int blk = c / (head_dim * kBlock);
+      const int cc = c - blk * head_dim * kBlock;
+      const int xx = cc / kBlock, o = cc - xx * kBlock;
+      const int jj = blk == 0 ? o - o0 : o + kBlock - o0;
+      if (jj < 0 || jj >= kBlock) continue;  // another run's slot: left alone
+      const int64_t base = tile_base(b0 + blk, g, num_kv_heads, head_dim);
+      v_cache[base + xx * kBlock + o] = (char)vt[xx * kBlock + jj];
+    }
     return;
   }
 

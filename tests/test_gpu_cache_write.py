@@ -103,3 +103,65 @@ def test_cache_write_bulk_fill_config3_pool_full():
         vb = pool.v[b0 * per_block: b1 * per_block].cpu().numpy().view(np.uint16)
         assert np.array_equal(kb, oracle.k_pool_bytes(pk[b0:b1])), f"K blocks {b0}..{b1 - 1}"
         assert np.array_equal(vb, oracle.v_pool_bytes(pv[b0:b1])), f"V blocks {b0}..{b1 - 1}"
+
+def _run_slots(rng, nb, lengths, offsets):
+    """Slots of consecutive runs (one per request), each starting at the given
+    offset inside a fresh random block and continuing through the next
+    blocks; concatenated in request order, so most input groups of 16 start
+    mid-block and some hold the end of one run and the start of the next."""
+    blocks = list(rng.permutation(nb))
+    out = []
+    for n, o in zip(lengths, offsets):
+        nbk = (o + n + 15) // 16
+        mine = [blocks.pop() for _ in range(nbk)]
+        pos = o + np.arange(n)
+        out.append(np.asarray(mine, dtype=np.int64)[pos // 16] * 16 + pos % 16)
+    return np.concatenate(out).astype(np.int64)
+
+
+@pytest.mark.parametrize("dtype,D,Hkv", [("bf16", 128, 8), ("f32", 64, 2), ("bf16", 64, 3)])
+def test_cache_write_runs_starting_mid_block(dtype, D, Hkv):
+    """Consecutive slots that start anywhere in a block (a prefill chunk's or
+    a ragged history's tokens): whole pools byte-exact, untouched slots keep
+    their poison; adjacent runs fill complementary halves of shared blocks."""
+    from gpu_util import GpuPool
+
+    log(f"cache write runs starting mid-block {dtype} D={D} Hkv={Hkv}")
+    rng = np.random.default_rng(D * 7 + Hkv)
+    nb = 200
+    lengths = [2047 % 300 + 1, 16, 17, 31, 1, 64, 100, 15, 33, 250]
+    offsets = [3, 0, 15, 8, 7, 1, 12, 0, 5, 9]
+    slots = _run_slots(rng, nb, lengths, offsets)
+    T = slots.shape[0]
+    raw = np.uint16 if dtype == "bf16" else np.uint32
+    k = rng.integers(0, 2 ** 15 if dtype == "bf16" else 2 ** 30, (T, Hkv, D)).astype(raw)
+    v = rng.integers(0, 2 ** 15 if dtype == "bf16" else 2 ** 30, (T, Hkv, D)).astype(raw)
+    pool = GpuPool(nb, Hkv, D, dtype)
+    pool.write(k, v, slots)
+    pk = oracle.new_pool(nb, Hkv, D, dtype, poison_bits(dtype))
+    pv = oracle.new_pool(nb, Hkv, D, dtype, poison_bits(dtype))
+    oracle.reshape_and_cache(pk, pv, k, v, slots)
+    assert np.array_equal(pool.k_bits(), oracle.k_pool_bytes(pk)), "K pool"
+    assert np.array_equal(pool.v_bits(), oracle.v_pool_bytes(pv)), "V pool"
+
+
+def test_cache_write_run_halves_of_one_block_in_two_calls():
+    """One block filled by two runs, offsets 0..6 in the first call and 7..15
+    (continuing into the next block) in the second: the first call's
+    elements survive the second's partial chunk writes."""
+    from gpu_util import GpuPool
+
+    log("cache write two runs into one block")
+    rng = np.random.default_rng(3)
+    nb, Hkv, D = 8, 2, 128
+    pool = GpuPool(nb, Hkv, D, "bf16")
+    pk = oracle.new_pool(nb, Hkv, D, "bf16", poison_bits("bf16"))
+    pv = oracle.new_pool(nb, Hkv, D, "bf16", poison_bits("bf16"))
+    for sl in (np.arange(3 * 16, 3 * 16 + 7), np.arange(3 * 16 + 7, 3 * 16 + 7 + 20)):
+        sl = sl.astype(np.int64)
+        k = rng.integers(0, 2 ** 15, (len(sl), Hkv, D)).astype(np.uint16)
+        v = rng.integers(0, 2 ** 15, (len(sl), Hkv, D)).astype(np.uint16)
+        pool.write(k, v, sl)
+        oracle.reshape_and_cache(pk, pv, k, v, sl)
+    assert np.array_equal(pool.k_bits(), oracle.k_pool_bytes(pk))
+    assert np.array_equal(pool.v_bits(), oracle.v_pool_bytes(pv))

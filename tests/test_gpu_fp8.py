@@ -149,6 +149,28 @@ def test_cache_write_ragged_batches(D, Hkv):
         pool.assert_codes_equal(f"T={T}")
 
 
+@pytest.mark.parametrize("D,Hkv", [(128, 8), (64, 2)])
+def test_cache_write_runs_starting_mid_block(D, Hkv):
+    """Runs of consecutive slots starting anywhere in a block, concatenated
+    request after request (most input groups of 16 start mid-block, some
+    hold the end of one run and the start of the next): every code of both
+    pools against the oracle's quantization."""
+    log(f"fp8 cache write runs starting mid-block D={D} Hkv={Hkv}")
+    rng = np.random.default_rng(11 + D)
+    nb = 120
+    pool = Fp8Pool(nb, Hkv, D, 0.05, 0.02)
+    blocks = list(rng.permutation(nb))
+    slots = []
+    for n, o in zip([47, 16, 17, 1, 64, 90, 15, 33], [3, 0, 15, 7, 1, 12, 0, 9]):
+        mine = [blocks.pop() for _ in range((o + n + 15) // 16)]
+        pos = o + np.arange(n)
+        slots.append(np.asarray(mine, dtype=np.int64)[pos // 16] * 16 + pos % 16)
+    slots = np.concatenate(slots).astype(np.int64)
+    x = rng.standard_normal((2, len(slots), Hkv, D)).astype(np.float32)
+    pool.write(bf16_bits_from_f32(x[0]), bf16_bits_from_f32(x[1]), slots)
+    pool.assert_codes_equal("runs")
+
+
 # ----------------------------------------------------------------------------
 # decode
 
