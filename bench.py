@@ -849,6 +849,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--configs", default="c1,c2,c3,c4,c5",
                     help="comma list of c1..c5 (c2, the headline, always runs)")
+    ap.add_argument("--no-headline", action="store_true",
+                    help="skip the headline workload (profiling one configuration alone); "
+                         "prints the configuration sections only")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip fp8 pools, speculative verification, block pool and the read probe")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -893,6 +896,18 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.no_headline:
+        sections = {"c1": bench_c1, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5}
+        out = {}
+        for c in want:
+            if c in sections:
+                log(f"{c} {CONFIGS[c]}")
+                out[f"{c}_{CONFIGS[c]}"] = sections[c](timer, args.steps, args.warmup, budget / 2)
+        if "c5" in want:
+            out["prefill_chunk"] = bench_prefill(timer, min(args.steps, 30), 3)
+        print(json.dumps({"configs": out}), flush=True)
+        return
 
     log("c2 llama3_8b_b64")
     c2, db2 = bench_c2(timer, args.steps, args.warmup, budget)

@@ -5,34 +5,74 @@
 // negative slot marking a padding token that writes nothing.  The copy moves
 // raw bits (no conversion), so the result is bit-exact by construction.
 //
-// One workgroup takes 16 consecutive input tokens of one kv head.
-//  * When their slots are consecutive (s0, s0+1, .., s0+15: the tokens of a
-//    bulk fill or of a prefill chunk, wherever the run starts in the input
-//    and in its block) they fill the tail of block s0 / 16 from offset
-//    s0 % 16 and, unless s0 % 16 is 0, the head of the next block.  K rows
-//    are written row by row; V, dim-major in the pool, is transposed through
-//    LDS and written as 16-byte chunks of dim rows, with the one partial
-//    chunk per dim row and block at a run's edge written element by element.
-//  * Otherwise (a decode step's scattered tokens, padding, a group holding
-//    the end of one run and the start of another) every token is scattered
-//    on its own: its K row as 16-byte stores, its V elements one by one, 16
-//    elements apart.
+// Tokens are written by "segments": a segment is a run of tokens whose
+// slots are consecutive inside one block.  It starts at a token whose slot
+// opens a block or does not continue the previous token's slot, and takes
+// the following tokens while their slots continue it, up to the block's
+// end.  One workgroup takes the segments that start among 16 consecutive
+// input tokens of one kv head (reading up to 15 tokens of the next 16), so
+// the tokens of a bulk fill or of a prefill chunk fill each block from one
+// workgroup wherever their run starts, and every V store is a whole 16-byte
+// chunk of a dim row except at the two ends of a run.  (With groups cut at
+// input boundaries instead, a run starting mid-block split every dim row of
+// every block between two workgroups, and those partial-sector writes made
+// a 70B-layer history fill 1.8x slower than the same fill starting at block
+// boundaries.)  Scattered tokens (a decode step's) are segments of one.
+//  * K: each owned token's row goes straight to its slot (16-byte stores).
+//  * V: the owned rows are staged in LDS by token and written as chunks of
+//    the dim-major tile; a chunk only partly inside the segment is written
+//    element by element.
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
 constexpr int kCwThreads = 256;
-constexpr int kCwMaxChunks = 2;  // 16 tokens x (D * eb / 16) chunks <= 512 for D <= 128, eb <= 4
+constexpr int kCwWin = 2 * kBlock;  // input tokens a workgroup may read
+
+// Slots of input tokens i0 - 1 .. i0 + 31 (-1: none, negative or outside the
+// pool) and the segments that start at tokens i0 .. i0 + 15.
+struct CwSegments {
+  int64_t sw[kCwWin + 1];  // slot of input i0 - 1 + t
+  int t0[kBlock];          // first token of segment k (window index: input i0 + t0)
+  int n[kBlock];           // its length
+  int owner[kCwWin];       // segment of window token t, or -1
+  int count;
+};
+
+__device__ inline void cw_find_segments(CwSegments& sg, const int64_t* slots, int64_t i0,
+                                        int num_tokens, int64_t pool_slots) {
+  const int tid = threadIdx.x;
+  if (tid <= kCwWin) {
+    const int64_t idx = i0 - 1 + tid;
+    int64_t sv = idx >= 0 && idx < num_tokens ? slots[idx] : -1;
+    sg.sw[tid] = sv >= 0 && sv < pool_slots ? sv : -1;
+  }
+  if (tid < kCwWin) sg.owner[tid] = -1;
+  if (tid == 0) sg.count = 0;
+  __syncthreads();
+  if (tid < kBlock) {
+    const int64_t sv = sg.sw[tid + 1];
+    if (sv >= 0 && (sv % kBlock == 0 || sg.sw[tid] != sv - 1)) {
+      const int lim = kBlock - (int)(sv % kBlock);
+      int len = 1;
+      while (len < lim && tid + len < kCwWin && sg.sw[tid + 1 + len] == sv + len) ++len;
+      const int k = atomicAdd(&sg.count, 1);  // segment order does not matter
+      sg.t0[k] = tid;
+      sg.n[k] = len;
+      for (int e = 0; e < len; ++e) sg.owner[tid + e] = k;
+    }
+  }
+  __syncthreads();
+}
 
 template <int EB>
 __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slots,
     int num_tokens, int num_kv_heads, int head_dim, int64_t pool_slots, uint4* __restrict__ k_cache,
     char* __restrict__ v_cache) {
-  // row = one token's D values of one kv head; RC 16-byte chunks per row
-  __shared__ int64_t sl[kBlock];
-  // V rows of the group, token-major, padded by 16 bytes per row
+  __shared__ CwSegments sg;
+  // V rows of the window's tokens, token-major, padded by 16 bytes per row
   extern __shared__ __attribute__((aligned(16))) char vstage[];
 
   const int tid = threadIdx.x;
@@ -40,121 +80,65 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
   const int64_t i0 = (int64_t)blockIdx.x * kBlock;
   const int RB = head_dim * EB;  // bytes of one row
   const int RC = RB / 16;        // 16-byte chunks per row
-  const int nch = kBlock * RC;   // chunks of the group
-  auto row_of = [&](int64_t tok) { return (tok * num_kv_heads + g) * RC; };  // in 16-byte chunks
+  const int stage_rb = RB + 16;
+  cw_find_segments(sg, slots, i0, num_tokens, pool_slots);
+  const int nseg = sg.count;
+  if (nseg == 0) return;  // uniform
 
-  // The rows do not depend on the slots: load them together with the slots,
-  // so that the group waits on one memory round trip.
-  uint4 kr[kCwMaxChunks], vr[kCwMaxChunks];
-#pragma unroll
-  for (int u = 0; u < kCwMaxChunks; ++u) {
-    const int c = tid + u * kCwThreads;
-    const int j = c / RC, x = c - j * RC;
-    if (c < nch && i0 + j < num_tokens) {
-      kr[u] = k[row_of(i0 + j) + x];
-      vr[u] = v[row_of(i0 + j) + x];
-    }
+  // rows of the owned tokens: K to its slot, V into LDS
+  for (int c = tid; c < kCwWin * RC; c += kCwThreads) {
+    const int t = c / RC, x = c - t * RC;
+    if (sg.owner[t] < 0) continue;
+    const int64_t row = ((i0 + t) * num_kv_heads + g) * RC + x;
+    const uint4 kr = k[row];
+    const uint4 vr = v[row];
+    const int64_t sv = sg.sw[t + 1];
+    const int64_t b = sv / kBlock;
+    k_cache[(tile_base(b, g, num_kv_heads, head_dim) * EB + (sv - b * kBlock) * RB) / 16 + x] = kr;
+    *(uint4*)(vstage + t * stage_rb + x * 16) = vr;
   }
-  // The group is one run when slot j is s0 + j for all 16 tokens, inside
-  // the pool.
-  bool in_run = true;
-  if (tid < kBlock) {
-    const bool real = i0 + tid < num_tokens;
-    const int64_t s0 = slots[i0];
-    const int64_t mine = real ? slots[i0 + tid] : -1;
-    sl[tid] = mine;
-    in_run = real && s0 >= 0 && s0 + kBlock <= pool_slots && mine == s0 + tid;
-  }
-  const bool run = __syncthreads_and(in_run);
+  __syncthreads();
 
-  if (run) {
-    // token j sits in block b0 at offset o0 + j, or (past the block) in
-    // block b0 + 1 at offset o0 + j - 16
-    const int64_t b0 = sl[0] / kBlock;
-    const int o0 = (int)(sl[0] - b0 * kBlock);
-    const int stage_rb = RB + 16;
-    auto tile_bytes = [&](int blk) { return tile_base(b0 + blk, g, num_kv_heads, head_dim) * EB; };
-#pragma unroll
-    for (int u = 0; u < kCwMaxChunks; ++u) {
-      const int c = tid + u * kCwThreads;
-      if (c < nch) {
-        const int j = c / RC, x = c - j * RC;
-        const int blk = o0 + j >= kBlock ? 1 : 0;
-        const int o = o0 + j - blk * kBlock;
-        k_cache[(tile_bytes(blk) + (int64_t)o * RB) / 16 + x] = kr[u];
-        *(uint4*)(vstage + j * stage_rb + x * 16) = vr[u];
-      }
-    }
-    __syncthreads();
-    // V: chunk c of a tile is dim c / CPD, offsets TPC * (c % CPD) ..; the
-    // run covers offsets o0 .. 15 of the first block and 0 .. o0 - 1 of the
-    // second
-    constexpr int TPC = 16 / EB;       // tokens per 16-byte chunk
-    constexpr int CPD = kBlock / TPC;  // chunks per dim row
-    const int nblk = o0 > 0 ? 2 : 1;
-    for (int c = tid; c < nblk * head_dim * CPD; c += kCwThreads) {
-      const int blk = c / (head_dim * CPD);
-      const int cc = c - blk * head_dim * CPD;
-      const int x = cc / CPD, of = (cc - x * CPD) * TPC;
-      const int j0 = of - o0 + blk * kBlock;  // token at offset `of`
-      char* dst = v_cache + tile_bytes(blk) + (int64_t)cc * 16;
-      auto elem = [&](int j) -> uint32_t {
-        if constexpr (EB == 2) return *(const uint16_t*)(vstage + j * stage_rb + x * 2);
-        else return *(const uint32_t*)(vstage + j * stage_rb + x * 4);
+  // V: chunk (x, kc) of a tile holds dim x, offsets TPC * kc .. TPC * kc + TPC - 1
+  constexpr int TPC = 16 / EB;       // offsets per 16-byte chunk
+  constexpr int CPD = kBlock / TPC;  // chunks per dim row
+  for (int sgi = 0; sgi < nseg; ++sgi) {
+    const int t0 = sg.t0[sgi], len = sg.n[sgi];
+    const int64_t sv = sg.sw[t0 + 1];
+    const int64_t b = sv / kBlock;
+    const int o = (int)(sv - b * kBlock);
+    const int kc0 = o / TPC, nk = (o + len - 1) / TPC - kc0 + 1;
+    char* tile = v_cache + tile_base(b, g, num_kv_heads, head_dim) * EB;
+    for (int it = tid; it < head_dim * nk; it += kCwThreads) {
+      const int x = it / nk, kc = kc0 + (it - x * nk);
+      const int of = kc * TPC;  // offset of the chunk's first element
+      auto elem = [&](int off) -> uint32_t {  // element of offset `off` (inside the segment)
+        const char* r = vstage + (t0 + off - o) * stage_rb;
+        if constexpr (EB == 2) return *(const uint16_t*)(r + x * 2);
+        else return *(const uint32_t*)(r + x * 4);
       };
-      if (j0 >= 0 && j0 + TPC <= kBlock) {
+      char* dst = tile + (int64_t)(x * CPD + kc) * 16;
+      if (of >= o && of + TPC <= o + len) {
         uint32_t w[4];
         if constexpr (EB == 2) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = elem(j0 + 2 * e) | (elem(j0 + 2 * e + 1) << 16);
+          for (int e = 0; e < 4; ++e) w[e] = elem(of + 2 * e) | (elem(of + 2 * e + 1) << 16);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = elem(j0 + e);
+          for (int e = 0; e < 4; ++e) w[e] = elem(of + e);
         }
         *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
       } else {
 #pragma unroll
         for (int e = 0; e < TPC; ++e) {
-          const int j = j0 + e;
-          if (j < 0 || j >= kBlock) continue;  // another run's slot: left alone
+          const int off = of + e;
+          if (off < o || off >= o + len) continue;  // another segment's slot: left alone
           if constexpr (EB == 2)
-            *(uint16_t*)(dst + e * 2) = (uint16_t)elem(j);
+            *(uint16_t*)(dst + e * 2) = (uint16_t)elem(off);
           else
-            *(uint32_t*)(dst + e * 4) = elem(j);
+            *(uint32_t*)(dst + e * 4) = elem(off);
         }
       }
-    }
-    return;
-  }
-
-  // scattered tokens: each token on its own
-#pragma unroll
-  for (int u = 0; u < kCwMaxChunks; ++u) {
-    const int c = tid + u * kCwThreads;
-    if (c >= nch) continue;
-    const int j = c / RC, chunk = c - j * RC;
-    const int64_t slot = sl[j];  // -1 for tokens past the end
-    if (slot < 0 || slot >= pool_slots) continue;
-    const int64_t b = slot / kBlock;
-    const int o = (int)(slot - b * kBlock);
-    const int64_t base = tile_base(b, g, num_kv_heads, head_dim);  // elements
-    // K: element (b, g, o, x) at base + o * D + x
-    k_cache[(base + (int64_t)o * head_dim) * EB / 16 + chunk] = kr[u];
-    // V: element (b, g, o, x) at base + x * 16 + o
-    constexpr int E = 16 / EB;  // elements in this chunk
-    const int64_t vrow = base + (int64_t)(chunk * E) * kBlock + o;
-    const uint32_t w[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
-    if constexpr (EB == 2) {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(v_cache) + vrow;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const uint32_t word = w[e >> 1];
-        dst[e * kBlock] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
-      }
-    } else {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(v_cache) + vrow;
-#pragma unroll
-      for (int e = 0; e < E; ++e) dst[e * kBlock] = w[e];
     }
   }
 }
@@ -171,85 +155,62 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
 // division), ties to the even code, magnitudes beyond 448 saturating; a NaN
 // becomes 0x7F with x's sign bit (quantize4).
 
-// One workgroup takes 16 consecutive input tokens of one kv head, as the
-// bf16/fp32 kernel does, with the same run and scatter paths.  Input chunk c
-// (8 bf16 of one token) becomes 8 codes.
+// The same segments as the bf16 / fp32 kernel.  Input chunk c (8 bf16 of
+// one token) becomes 8 codes.
 __global__ __launch_bounds__(kCwThreads) void cache_write_fp8_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slots,
     int num_tokens, int num_kv_heads, int head_dim, int64_t pool_slots, float k_scale,
     float v_scale, char* __restrict__ k_cache, char* __restrict__ v_cache) {
-  __shared__ int64_t sl[kBlock];
-  // codes of the V tile, dim-major: byte (x, o) at x * 16 + o
-  __shared__ __attribute__((aligned(16))) uint8_t vt[128 * kBlock];
+  __shared__ CwSegments sg;
+  // V codes of the window's tokens, token-major: byte (t, x) at t * 128 + x
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kCwWin * 128];
 
   const int tid = threadIdx.x;
   const int g = blockIdx.y;
   const int64_t i0 = (int64_t)blockIdx.x * kBlock;
-  const int RC = head_dim / 8;   // 16-byte input chunks per row
-  const int nch = kBlock * RC;   // <= kCwThreads
-  const int j = tid / RC, x = tid - j * RC;
-  const bool mine = tid < nch && i0 + j < num_tokens;
-  uint2 kq = make_uint2(0, 0), vq = make_uint2(0, 0);
-  if (mine) {
-    const int64_t row = ((i0 + j) * num_kv_heads + g) * RC + x;
+  const int RC = head_dim / 8;  // 16-byte input chunks per row
+  cw_find_segments(sg, slots, i0, num_tokens, pool_slots);
+  const int nseg = sg.count;
+  if (nseg == 0) return;  // uniform
+
+  for (int c = tid; c < kCwWin * RC; c += kCwThreads) {
+    const int t = c / RC, x = c - t * RC;
+    if (sg.owner[t] < 0) continue;
+    const int64_t row = ((i0 + t) * num_kv_heads + g) * RC + x;
     const uint4 kr = k[row], vr = v[row];
-    kq = make_uint2(quantize4(kr.x, kr.y, k_scale), quantize4(kr.z, kr.w, k_scale));
-    vq = make_uint2(quantize4(vr.x, vr.y, v_scale), quantize4(vr.z, vr.w, v_scale));
+    const uint2 kq = make_uint2(quantize4(kr.x, kr.y, k_scale), quantize4(kr.z, kr.w, k_scale));
+    const uint2 vq = make_uint2(quantize4(vr.x, vr.y, v_scale), quantize4(vr.z, vr.w, v_scale));
+    const int64_t sv = sg.sw[t + 1];
+    const int64_t b = sv / kBlock;
+    *(uint2*)(k_cache + tile_base(b, g, num_kv_heads, head_dim) + (sv - b * kBlock) * head_dim + x * 8) = kq;
+    *(uint2*)(vt + t * 128 + x * 8) = vq;
   }
-  bool in_run = true;
-  if (tid < kBlock) {
-    const bool real = i0 + tid < num_tokens;
-    const int64_t s0 = slots[i0];
-    const int64_t s = real ? slots[i0 + tid] : -1;
-    sl[tid] = s;
-    in_run = real && s0 >= 0 && s0 + kBlock <= pool_slots && s == s0 + tid;
-  }
-  const bool run = __syncthreads_and(in_run);
-  const uint8_t* vb = (const uint8_t*)&vq;
+  __syncthreads();
 
-  if (run) {
-    // token j sits in block b0 at offset o0 + j, or in block b0 + 1 at
-    // offset o0 + j - 16; vt holds the group's codes by token (x * 16 + j)
-    const int64_t b0 = sl[0] / kBlock;
-    const int o0 = (int)(sl[0] - b0 * kBlock);
-    if (tid < nch) {
-      const int blk = o0 + j >= kBlock ? 1 : 0;
-      const int64_t base = tile_base(b0 + blk, g, num_kv_heads, head_dim);  // bytes
-      *(uint2*)(k_cache + base + (o0 + j - blk * kBlock) * head_dim + x * 8) = kq;
+  // V: dim row x of a tile is 16 codes (offsets 0 .. 15), one 16-byte chunk
+  for (int sgi = 0; sgi < nseg; ++sgi) {
+    const int t0 = sg.t0[sgi], len = sg.n[sgi];
+    const int64_t sv = sg.sw[t0 + 1];
+    const int64_t b = sv / kBlock;
+    const int o = (int)(sv - b * kBlock);
+    char* tile = v_cache + tile_base(b, g, num_kv_heads, head_dim);
+    if (len == kBlock) {  // the whole tile
+      for (int x = tid; x < head_dim; x += kCwThreads) {
+        uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(x * 8 + e) * kBlock + j] = vb[e];
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)vt[(t0 + 4 * e) * 128 + x] | ((uint32_t)vt[(t0 + 4 * e + 1) * 128 + x] << 8) |
+                 ((uint32_t)vt[(t0 + 4 * e + 2) * 128 + x] << 16) |
+                 ((uint32_t)vt[(t0 + 4 * e + 3) * 128 + x] << 24);
+        *(uint4*)(tile + x * kBlock) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {  // codes at offsets o .. o + len - 1 of every dim row
+      for (int it = tid; it < head_dim * len; it += kCwThreads) {
+        const int x = it / len, e = it - x * len;
+        tile[x * kBlock + o + e] = (char)vt[(t0 + e) * 128 + x];
+      }
     }
-    __syncthreads();
-    if (o0 == 0) {
-      const int64_t base = tile_base(b0, g, num_kv_heads, head_dim);
-      if (tid < head_dim) *(uint4*)(v_cache + base + tid * kBlock) = *(const uint4*)&vt[tid * kBlock];
-      return;
-    }
-    // dim row x of the first block takes offsets o0 .. 15 (tokens 0 ..),
-    // of the second offsets 0 .. o0 - 1 (tokens 16 - o0 ..): byte stores,
-    // neighbouring threads on neighbouring bytes
-    for (int c = tid; c < 2 * head_dim * kBlock; c += kCwThreads) {
-      const int blk = c / (head_dim * kBlock);
-      const int cc = c - blk * head_dim * kBlock;
-      const int xx = cc / kBlock, o = cc - xx * kBlock;
-      const int jj = blk == 0 ? o - o0 : o + kBlock - o0;
-      if (jj < 0 || jj >= kBlock) continue;  // another run's slot: left alone
-      const int64_t base = tile_base(b0 + blk, g, num_kv_heads, head_dim);
-      v_cache[base + xx * kBlock + o] = (char)vt[xx * kBlock + jj];
-    }
-    return;
   }
-
-  // scattered tokens: each token on its own
-  if (!mine) return;
-  const int64_t slot = sl[j];
-  if (slot < 0 || slot >= pool_slots) return;
-  const int64_t b = slot / kBlock;
-  const int o = (int)(slot - b * kBlock);
-  const int64_t base = tile_base(b, g, num_kv_heads, head_dim);
-  *(uint2*)(k_cache + base + o * head_dim + x * 8) = kq;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v_cache[base + (x * 8 + e) * kBlock + o] = (char)vb[e];
 }
 
 hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slots, int num_tokens,
@@ -267,9 +228,8 @@ hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slots
                        (char*)v_cache);
     return hipGetLastError();
   }
-  if ((int64_t)kBlock * g.head_dim * g.elem_bytes / 16 > (int64_t)kCwMaxChunks * kCwThreads)
-    return hipErrorInvalidValue;
-  const size_t lds = (size_t)kBlock * (g.head_dim * g.elem_bytes + 16);
+  if (g.head_dim > 128) return hipErrorInvalidValue;
+  const size_t lds = (size_t)kCwWin * (g.head_dim * g.elem_bytes + 16);
   const int64_t pool_slots = (int64_t)g.num_blocks * kBlock;
   if (g.elem_bytes == 2) {
     hipLaunchKernelGGL(cache_write_kernel<2>, grid, dim3(kCwThreads), lds, stream,
