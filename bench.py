@@ -842,6 +842,17 @@ def read_ceiling(timer, steps=10):
 # ----------------------------------------------------------------------------
 
 
+def extras(timer, n):
+    """The sections beside the five configurations: the read ceiling, fp8 pools
+    (prefill and decode step), a speculative verification round and the host
+    block pool."""
+    return {"hbm_read_ceiling": read_ceiling(timer),
+            "fp8_prefill_chunk": bench_prefill(timer, n, 3, fp8=True),
+            "fp8_kv_step": bench_fp8_decode(timer, n, 5),
+            "spec_verify_round": bench_spec_verify(timer, n, 3),
+            "block_pool": bench_block_pool(timer)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -859,6 +870,9 @@ def main():
                     help="seconds of oracle time for the headline workload (others get less)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only pa_prefill_chunk on the long-context batch (for profiling)")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="time only the extra sections (fp8 pools, speculative verification, "
+                         "block pool, read probe; for profiling)")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of the bench, run N plain 1 GiB device copies (counter calibration)")
     args = ap.parse_args()
@@ -889,6 +903,10 @@ def main():
         print(json.dumps({"prefill_chunk": bench_prefill(timer, args.steps, args.warmup),
                           "fp8_prefill_chunk": bench_prefill(timer, args.steps, args.warmup, fp8=True)}),
               flush=True)
+        return
+
+    if args.extras_only:
+        print(json.dumps(extras(timer, min(args.steps, 30))), flush=True)
         return
 
     want = [c.strip() for c in args.configs.split(",") if c.strip()]
@@ -977,15 +995,10 @@ def main():
         line["prefill_chunk"] = bench_prefill(timer, min(args.steps, 30), 3)
     if not args.no_extras:
         log("extras")
-        line["hbm_read_ceiling"] = read_ceiling(timer)
+        line.update(extras(timer, min(args.steps, 30)))
         line["roofline"]["frac_of_read_ceiling"] = round(value / line["hbm_read_ceiling"]["gbs"], 4)
-        n = min(args.steps, 30)
-        line["fp8_prefill_chunk"] = bench_prefill(timer, n, 3, fp8=True)
-        line["fp8_kv_step"] = bench_fp8_decode(timer, n, 5)
         line["fp8_kv_step"]["speedup_vs_bf16_step_cold"] = round(
             ms_step / line["fp8_kv_step"]["step_cold"]["median_ms"], 3)
-        line["spec_verify_round"] = bench_spec_verify(timer, n, 3)
-        line["block_pool"] = bench_block_pool(timer)
     print(json.dumps(line), flush=True)
 
 

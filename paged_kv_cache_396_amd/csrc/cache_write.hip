@@ -38,6 +38,8 @@ struct CwSegments {
   int n[kBlock];           // its length
   int owner[kCwWin];       // segment of window token t, or -1
   int count;
+  int multi;  // some segment is longer than one token (its V goes through LDS)
+  int tail;   // some segment reaches into tokens i0 + 16 ..
 };
 
 __device__ inline void cw_find_segments(CwSegments& sg, const int64_t* slots, int64_t i0,
@@ -49,7 +51,11 @@ __device__ inline void cw_find_segments(CwSegments& sg, const int64_t* slots, in
     sg.sw[tid] = sv >= 0 && sv < pool_slots ? sv : -1;
   }
   if (tid < kCwWin) sg.owner[tid] = -1;
-  if (tid == 0) sg.count = 0;
+  if (tid == 0) {
+    sg.count = 0;
+    sg.multi = 0;
+    sg.tail = 0;
+  }
   __syncthreads();
   if (tid < kBlock) {
     const int64_t sv = sg.sw[tid + 1];
@@ -61,9 +67,48 @@ __device__ inline void cw_find_segments(CwSegments& sg, const int64_t* slots, in
       sg.t0[k] = tid;
       sg.n[k] = len;
       for (int e = 0; e < len; ++e) sg.owner[tid + e] = k;
+      if (len > 1) sg.multi = 1;
+      if (tid + len > kBlock) sg.tail = 1;
     }
   }
   __syncthreads();
+}
+
+// Rows are read in two rounds.  The group's own 16 tokens are read at once,
+// together with the slots, so a scattered step's tokens wait on one memory
+// round trip; the window's next 16 tokens are read after the segments are
+// known, and only when a run continues into them.  A token that is a
+// segment of its own (a decode step's) writes its V elements straight from
+// registers, one element per dim row; longer segments go through LDS.
+
+// One 16-byte chunk x of token t's K and V rows, t owned: K to its slot, V
+// into the stage, or (a one-token segment) V element by element.
+template <int EB>
+__device__ inline void cw_place(const CwSegments& sg, int t, int x, uint4 kr, uint4 vr, int g,
+                                int num_kv_heads, int head_dim, uint4* k_cache, char* v_cache,
+                                char* vstage, int stage_rb) {
+  const int RB = head_dim * EB;
+  const int64_t sv = sg.sw[t + 1];
+  const int64_t b = sv / kBlock;
+  const int o = (int)(sv - b * kBlock);
+  const int64_t base = tile_base(b, g, num_kv_heads, head_dim);  // elements
+  k_cache[(base * EB + o * RB) / 16 + x] = kr;
+  if (sg.n[sg.owner[t]] > 1) {
+    *(uint4*)(vstage + t * stage_rb + x * 16) = vr;
+    return;
+  }
+  // V: element (b, g, o, d) at base + d * 16 + o; this chunk holds dims E x ..
+  constexpr int E = 16 / EB;
+  const uint32_t w[4] = {vr.x, vr.y, vr.z, vr.w};
+  if constexpr (EB == 2) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(v_cache) + base + (int64_t)(x * E) * kBlock + o;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e * kBlock] = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+  } else {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(v_cache) + base + (int64_t)(x * E) * kBlock + o;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e * kBlock] = w[e];
+  }
 }
 
 template <int EB>
@@ -78,32 +123,53 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
   const int tid = threadIdx.x;
   const int g = blockIdx.y;
   const int64_t i0 = (int64_t)blockIdx.x * kBlock;
-  const int RB = head_dim * EB;  // bytes of one row
-  const int RC = RB / 16;        // 16-byte chunks per row
-  const int stage_rb = RB + 16;
-  cw_find_segments(sg, slots, i0, num_tokens, pool_slots);
-  const int nseg = sg.count;
-  if (nseg == 0) return;  // uniform
+  const int RC = head_dim * EB / 16;  // 16-byte chunks per row
+  const int stage_rb = head_dim * EB + 16;
+  const int own = kBlock * RC;        // chunks of one round (16 tokens): <= 2 per thread
 
-  // rows of the owned tokens: K to its slot, V into LDS
-  for (int c = tid; c < kCwWin * RC; c += kCwThreads) {
-    const int t = c / RC, x = c - t * RC;
-    if (sg.owner[t] < 0) continue;
-    const int64_t row = ((i0 + t) * num_kv_heads + g) * RC + x;
-    const uint4 kr = k[row];
-    const uint4 vr = v[row];
-    const int64_t sv = sg.sw[t + 1];
-    const int64_t b = sv / kBlock;
-    k_cache[(tile_base(b, g, num_kv_heads, head_dim) * EB + (sv - b * kBlock) * RB) / 16 + x] = kr;
-    *(uint4*)(vstage + t * stage_rb + x * 16) = vr;
+  // round 1: chunks tid and tid + 256 of the group's own rows
+  const int c0 = tid, c1 = tid + kCwThreads;
+  const int t0r = c0 / RC, t1r = c1 / RC;
+  const bool h0 = c0 < own && i0 + t0r < num_tokens;
+  const bool h1 = EB == 4 && c1 < own && i0 + t1r < num_tokens;
+  uint4 k0 = make_uint4(0, 0, 0, 0), v0 = k0, k1 = k0, v1 = k0;
+  if (h0) {
+    const int64_t row = ((i0 + t0r) * num_kv_heads + g) * RC + (c0 - t0r * RC);
+    k0 = k[row];
+    v0 = v[row];
+  }
+  if (h1) {
+    const int64_t row = ((i0 + t1r) * num_kv_heads + g) * RC + (c1 - t1r * RC);
+    k1 = k[row];
+    v1 = v[row];
+  }
+  cw_find_segments(sg, slots, i0, num_tokens, pool_slots);
+  if (sg.count == 0) return;  // uniform
+
+  if (h0 && sg.owner[t0r] >= 0)
+    cw_place<EB>(sg, t0r, c0 - t0r * RC, k0, v0, g, num_kv_heads, head_dim, k_cache, v_cache, vstage, stage_rb);
+  if (h1 && sg.owner[t1r] >= 0)
+    cw_place<EB>(sg, t1r, c1 - t1r * RC, k1, v1, g, num_kv_heads, head_dim, k_cache, v_cache, vstage, stage_rb);
+  if (!sg.multi) return;  // uniform: every segment was one token
+  // round 2: tokens i0 + 16 .. that continue a run
+  if (sg.tail) {  // uniform
+    for (int c = tid; c < own; c += kCwThreads) {
+      const int t = kBlock + c / RC, x = c % RC;
+      if (sg.owner[t] < 0) continue;
+      const int64_t row = ((i0 + t) * num_kv_heads + g) * RC + x;
+      cw_place<EB>(sg, t, x, k[row], v[row], g, num_kv_heads, head_dim, k_cache, v_cache, vstage, stage_rb);
+    }
   }
   __syncthreads();
 
-  // V: chunk (x, kc) of a tile holds dim x, offsets TPC * kc .. TPC * kc + TPC - 1
+  // V of the longer segments: chunk (x, kc) of a tile holds dim x, offsets
+  // TPC * kc .. TPC * kc + TPC - 1; a chunk only partly inside the segment
+  // is written element by element
   constexpr int TPC = 16 / EB;       // offsets per 16-byte chunk
   constexpr int CPD = kBlock / TPC;  // chunks per dim row
-  for (int sgi = 0; sgi < nseg; ++sgi) {
+  for (int sgi = 0; sgi < sg.count; ++sgi) {
     const int t0 = sg.t0[sgi], len = sg.n[sgi];
+    if (len == 1) continue;  // uniform: written from registers
     const int64_t sv = sg.sw[t0 + 1];
     const int64_t b = sv / kBlock;
     const int o = (int)(sv - b * kBlock);
@@ -112,10 +178,11 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
     for (int it = tid; it < head_dim * nk; it += kCwThreads) {
       const int x = it / nk, kc = kc0 + (it - x * nk);
       const int of = kc * TPC;  // offset of the chunk's first element
-      auto elem = [&](int off) -> uint32_t {  // element of offset `off` (inside the segment)
-        const char* r = vstage + (t0 + off - o) * stage_rb;
-        if constexpr (EB == 2) return *(const uint16_t*)(r + x * 2);
-        else return *(const uint32_t*)(r + x * 4);
+      // staged element of offset off (o <= off < o + len): token t0 + off - o
+      auto elem = [&](int off) -> uint32_t {
+        const char* r = vstage + (t0 + off - o) * stage_rb + x * EB;
+        if constexpr (EB == 2) return *(const uint16_t*)r;
+        else return *(const uint32_t*)r;
       };
       char* dst = tile + (int64_t)(x * CPD + kc) * 16;
       if (of >= o && of + TPC <= o + len) {
@@ -155,8 +222,8 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
 // division), ties to the even code, magnitudes beyond 448 saturating; a NaN
 // becomes 0x7F with x's sign bit (quantize4).
 
-// The same segments as the bf16 / fp32 kernel.  Input chunk c (8 bf16 of
-// one token) becomes 8 codes.
+// The same segments and read rounds as the bf16 / fp32 kernel.  Input chunk
+// c (8 bf16 of one token) becomes 8 codes.
 __global__ __launch_bounds__(kCwThreads) void cache_write_fp8_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slots,
     int num_tokens, int num_kv_heads, int head_dim, int64_t pool_slots, float k_scale,
@@ -169,27 +236,54 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_fp8_kernel(
   const int g = blockIdx.y;
   const int64_t i0 = (int64_t)blockIdx.x * kBlock;
   const int RC = head_dim / 8;  // 16-byte input chunks per row
-  cw_find_segments(sg, slots, i0, num_tokens, pool_slots);
-  const int nseg = sg.count;
-  if (nseg == 0) return;  // uniform
+  const int own = kBlock * RC;  // <= 256: one chunk per thread per round
 
-  for (int c = tid; c < kCwWin * RC; c += kCwThreads) {
-    const int t = c / RC, x = c - t * RC;
-    if (sg.owner[t] < 0) continue;
-    const int64_t row = ((i0 + t) * num_kv_heads + g) * RC + x;
-    const uint4 kr = k[row], vr = v[row];
+  // chunk x of token t's rows, t owned: K codes to the slot; V codes into
+  // LDS, or (a one-token segment) byte by byte into its 8 dim rows
+  auto place = [&](int t, int x, uint4 kr, uint4 vr) {
     const uint2 kq = make_uint2(quantize4(kr.x, kr.y, k_scale), quantize4(kr.z, kr.w, k_scale));
     const uint2 vq = make_uint2(quantize4(vr.x, vr.y, v_scale), quantize4(vr.z, vr.w, v_scale));
     const int64_t sv = sg.sw[t + 1];
     const int64_t b = sv / kBlock;
-    *(uint2*)(k_cache + tile_base(b, g, num_kv_heads, head_dim) + (sv - b * kBlock) * head_dim + x * 8) = kq;
-    *(uint2*)(vt + t * 128 + x * 8) = vq;
+    const int o = (int)(sv - b * kBlock);
+    const int64_t base = tile_base(b, g, num_kv_heads, head_dim);
+    *(uint2*)(k_cache + base + o * head_dim + x * 8) = kq;
+    if (sg.n[sg.owner[t]] > 1) {
+      *(uint2*)(vt + t * 128 + x * 8) = vq;
+      return;
+    }
+    char* dst = v_cache + base + (int64_t)(x * 8) * kBlock + o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e * kBlock] = (char)(((e < 4 ? vq.x : vq.y) >> (8 * (e & 3))) & 0xffu);
+  };
+
+  const int tr = tid / RC;
+  const bool have = tid < own && i0 + tr < num_tokens;
+  uint4 kr = make_uint4(0, 0, 0, 0), vr = kr;
+  if (have) {
+    const int64_t row = ((i0 + tr) * num_kv_heads + g) * RC + (tid - tr * RC);
+    kr = k[row];
+    vr = v[row];
+  }
+  cw_find_segments(sg, slots, i0, num_tokens, pool_slots);
+  if (sg.count == 0) return;  // uniform
+
+  if (have && sg.owner[tr] >= 0) place(tr, tid - tr * RC, kr, vr);
+  if (!sg.multi) return;  // uniform
+  if (sg.tail && tid < own) {
+    const int t = kBlock + tr, x = tid - tr * RC;
+    if (sg.owner[t] >= 0) {
+      const int64_t row = ((i0 + t) * num_kv_heads + g) * RC + x;
+      place(t, x, k[row], v[row]);
+    }
   }
   __syncthreads();
 
-  // V: dim row x of a tile is 16 codes (offsets 0 .. 15), one 16-byte chunk
-  for (int sgi = 0; sgi < nseg; ++sgi) {
+  // V of the longer segments: dim row x of a tile is 16 codes (offsets
+  // 0 .. 15), one 16-byte chunk
+  for (int sgi = 0; sgi < sg.count; ++sgi) {
     const int t0 = sg.t0[sgi], len = sg.n[sgi];
+    if (len == 1) continue;  // uniform: written from registers
     const int64_t sv = sg.sw[t0 + 1];
     const int64_t b = sv / kBlock;
     const int o = (int)(sv - b * kBlock);
