@@ -247,6 +247,43 @@ def test_balanced_nan_workspace():
     assert_close(out[keep], ref[keep], "bf16", "balanced NaN workspace")
 
 
+def test_balanced_all_contexts_empty():
+    """No sequence has a block: the merge writes every row as zeros."""
+    log("decode balanced all contexts empty")
+    wl = make_tiny_decode(seed=89, ctx=(3000, 5, 700, 16), Hq=32, Hkv=8, D=128, dtype="bf16")
+    assert pa.pa_decode_partition_size(4, 8, 4096, 0) == 0, "expected the balanced schedule"
+    ws = decode_workspace(4, 32, 8, 128, 4096)
+    ws.fill_(float("nan"))
+    out = to_f64(gpu_decode(wl, gpu_pool_for(wl), context_lens=np.zeros(4, np.int32), max_ctx=4096,
+                            workspace=ws))
+    assert (out == 0).all()
+
+
+def test_balanced_repeated_calls_share_one_workspace():
+    """Calls that reuse one workspace with different context mixes (so the
+    pieces of a sequence and the ranges holding them change from call to
+    call): the merge reads only what the current call wrote.  The first call
+    starts from a zeroed workspace, the others from what the call before
+    left."""
+    log("decode balanced repeated calls, one workspace")
+    full = (3000, 1, 700, 16, 4096, 33, 2)
+    wl = make_tiny_decode(seed=90, ctx=full, Hq=32, Hkv=8, D=128, dtype="bf16")
+    pool = gpu_pool_for(wl)
+    pk, pv = oracle_pools(wl, oracle)
+    ws = decode_workspace(7, 32, 8, 128, 4096)
+    ws.zero_()
+    rng = np.random.default_rng(90)
+    mixes = [np.array(full, np.int32)]
+    for _ in range(5):
+        mixes.append(np.array([int(rng.integers(0, c + 1)) for c in full], np.int32))
+    mixes.append(np.array(full, np.int32))
+    for it, cl in enumerate(mixes):
+        out = to_f64(gpu_decode(wl, pool, context_lens=cl, max_ctx=4096, workspace=ws))
+        ref = oracle.decode(wl.q, pk, pv, wl.block_tables, cl, wl.scale, wl.dtype)
+        assert (out[cl == 0] == 0).all(), f"call {it}"
+        assert_close(out[cl > 0], ref[cl > 0], "bf16", f"call {it} ({cl.tolist()})")
+
+
 @pytest.mark.parametrize("S", [1000, 1023])
 def test_balanced_many_sequences(S):
     """Every workgroup scans all S block counts in LDS (up to four per

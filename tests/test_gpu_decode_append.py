@@ -13,8 +13,9 @@ import pytest
 import oracle
 from workloads import make_decode, make_tiny_decode
 
+import paged_kv_cache_396_amd as pa
 from gpu_util import (assert_close, decode_workspace, gpu_decode, gpu_decode_append, gpu_pool_for,
-                      log, oracle_pools, raw_bits, to_f64, torch)
+                      log, oracle_pools, raw_bits, to_dev, to_f64, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +82,39 @@ def test_append_negative_slot_writes_nothing():
     out = to_f64(gpu_decode_append(wl, pool, slots=slots))
     _assert_pools_equal(pool, gpu_pool_for(wl), "negative slot")
     assert_close(out, _oracle_decode(wl), "bf16", "negative slot")
+
+
+def test_append_balanced_with_empty_sequences():
+    """One step of the balanced schedule where some rows have context 0:
+    those rows are not written and their outputs are zero; the others are
+    written and attended."""
+    log("decode append balanced with empty sequences")
+    t = torch()
+    wl = make_tiny_decode(seed=18, ctx=(3000, 1, 700, 16, 4096, 33), Hq=32, Hkv=8, D=128,
+                          dtype="bf16")
+    cl = wl.context_lens.copy()
+    cl[[1, 3]] = 0
+    assert pa.pa_decode_partition_size(6, 8, 4096, 0) == 0, "expected the balanced schedule"
+    pool = gpu_pool_for(wl, with_new=False)
+    q = to_dev(wl.q, "bf16")
+    out = t.empty_like(q)
+    sl = t.from_numpy(np.ascontiguousarray(wl.new_slots, dtype=np.int64)).cuda()
+    ws = decode_workspace(6, 32, 8, 128, 4096)
+    ws.fill_(float("nan"))
+    pa.pa_decode_append(out, q, to_dev(wl.new_k, "bf16"), to_dev(wl.new_v, "bf16"), sl, pool.k,
+                        pool.v, t.from_numpy(np.ascontiguousarray(wl.block_tables)).cuda(),
+                        t.from_numpy(cl).cuda(), 4096, float(wl.scale), pool.desc, workspace=ws)
+    t.cuda.synchronize()
+    got = to_f64(out)
+    assert (got[[1, 3]] == 0).all()
+    # the pool gains the rows of the sequences with a context only
+    keep = [s for s in range(6) if cl[s] > 0]
+    want = gpu_pool_for(wl, with_new=False)
+    want.write(wl.new_k[keep], wl.new_v[keep], wl.new_slots[keep])
+    _assert_pools_equal(pool, want, "empty sequences")
+    pk, pv = oracle_pools(wl, oracle)
+    ref = oracle.decode(wl.q, pk, pv, wl.block_tables, cl, wl.scale, wl.dtype)
+    assert_close(got[keep], ref[keep], "bf16", "balanced append, empty sequences")
 
 
 def test_append_nan_workspace_and_repeat():
