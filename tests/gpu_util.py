@@ -312,3 +312,36 @@ class MixedStep:
         e2.record(self.s2)
         main.wait_event(e1)
         main.wait_event(e2)
+
+
+def mixed_slots(rng, nb, n_pieces):
+    """One call's slots mixing every shape the segment logic meets: runs of
+    random length starting at random offsets (some reaching over several
+    blocks and over several groups of 16 inputs), single scattered tokens,
+    runs broken by one skipped slot, padding (-1) inside and between runs,
+    and slots past the pool.  No slot appears twice."""
+    free = [int(b) for b in rng.permutation(nb)]
+    pieces = []
+    for _ in range(n_pieces):
+        kind = rng.integers(0, 4)
+        if kind == 0 and len(free) >= 1:          # a single token anywhere
+            pieces.append(np.array([free.pop() * 16 + int(rng.integers(0, 16))]))
+        elif kind == 3:                          # padding or past the pool
+            pieces.append(np.array([-1 if rng.integers(0, 2) else nb * 16 + int(rng.integers(0, 64))]))
+        else:                                    # a run, maybe with a gap
+            o = int(rng.integers(0, 16))
+            n = int(rng.integers(1, 70))
+            nbk = (o + n + 15) // 16
+            if len(free) < nbk:
+                continue
+            mine = np.asarray([free.pop() for _ in range(nbk)], dtype=np.int64)
+            pos = o + np.arange(n)
+            run = mine[pos // 16] * 16 + pos % 16
+            if kind == 2 and n > 4:              # skip one slot mid-run
+                cut = int(rng.integers(1, n - 1))
+                run = np.concatenate([run[:cut], run[cut + 1:]])
+            if rng.integers(0, 3) == 0 and len(run) > 2:  # a padding token inside
+                at = int(rng.integers(1, len(run)))
+                run = np.concatenate([run[:at], [-1], run[at:]])
+            pieces.append(run)
+    return np.concatenate(pieces).astype(np.int64)

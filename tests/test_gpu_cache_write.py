@@ -7,7 +7,7 @@ import pytest
 import oracle
 from workloads import make_decode, make_tiny_decode, poison_bits
 
-from gpu_util import gpu_pool_for, log, oracle_pools
+from gpu_util import gpu_pool_for, log, mixed_slots, oracle_pools
 
 pytestmark = pytest.mark.gpu
 
@@ -141,6 +141,31 @@ def test_cache_write_runs_starting_mid_block(dtype, D, Hkv):
     pk = oracle.new_pool(nb, Hkv, D, dtype, poison_bits(dtype))
     pv = oracle.new_pool(nb, Hkv, D, dtype, poison_bits(dtype))
     oracle.reshape_and_cache(pk, pv, k, v, slots)
+    assert np.array_equal(pool.k_bits(), oracle.k_pool_bytes(pk)), "K pool"
+    assert np.array_equal(pool.v_bits(), oracle.v_pool_bytes(pv)), "V pool"
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("dtype,D,Hkv", [("bf16", 128, 8), ("f32", 64, 2), ("bf16", 64, 3)])
+def test_cache_write_random_segments(dtype, D, Hkv, seed):
+    """Random mixtures of runs, scattered tokens, padding and out-of-range
+    slots in one call: whole pools byte-exact against the oracle."""
+    from gpu_util import GpuPool
+
+    log(f"cache write random segments {dtype} D={D} Hkv={Hkv} seed={seed}")
+    rng = np.random.default_rng(1000 * seed + D + Hkv)
+    nb = 400
+    slots = mixed_slots(rng, nb, 120)
+    T = slots.shape[0]
+    raw = np.uint16 if dtype == "bf16" else np.uint32
+    k = rng.integers(0, 2 ** 15 if dtype == "bf16" else 2 ** 30, (T, Hkv, D)).astype(raw)
+    v = rng.integers(0, 2 ** 15 if dtype == "bf16" else 2 ** 30, (T, Hkv, D)).astype(raw)
+    pool = GpuPool(nb, Hkv, D, dtype)
+    pool.write(k, v, slots)
+    pk = oracle.new_pool(nb, Hkv, D, dtype, poison_bits(dtype))
+    pv = oracle.new_pool(nb, Hkv, D, dtype, poison_bits(dtype))
+    # slots past the pool are ignored (the oracle skips negative ones)
+    oracle.reshape_and_cache(pk, pv, k, v, np.where(slots >= nb * 16, -1, slots))
     assert np.array_equal(pool.k_bits(), oracle.k_pool_bytes(pk)), "K pool"
     assert np.array_equal(pool.v_bits(), oracle.v_pool_bytes(pv)), "V pool"
 

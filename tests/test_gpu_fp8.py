@@ -45,7 +45,9 @@ class Fp8Pool:
         s = t.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).cuda()
         pa.pa_reshape_and_cache(to_dev(k_raw, "bf16"), to_dev(v_raw, "bf16"), s, self.k, self.v,
                                 self.desc)
-        f8.reshape_and_cache(self.ok, self.ov, k_raw, v_raw, slots, self.k_scale, self.v_scale)
+        # slots past the pool are ignored (the oracle skips negative ones)
+        inpool = np.where(np.asarray(slots) >= self.shape[0] * 16, -1, slots)
+        f8.reshape_and_cache(self.ok, self.ov, k_raw, v_raw, inpool, self.k_scale, self.v_scale)
 
     def assert_codes_equal(self, what=""):
         torch().cuda.synchronize()
@@ -169,6 +171,23 @@ def test_cache_write_runs_starting_mid_block(D, Hkv):
     x = rng.standard_normal((2, len(slots), Hkv, D)).astype(np.float32)
     pool.write(bf16_bits_from_f32(x[0]), bf16_bits_from_f32(x[1]), slots)
     pool.assert_codes_equal("runs")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_cache_write_random_segments(seed):
+    """Random mixtures of runs, scattered tokens, padding and out-of-range
+    slots in one call: every code of both pools against the oracle's
+    quantization."""
+    from gpu_util import mixed_slots
+
+    log(f"fp8 cache write random segments seed={seed}")
+    rng = np.random.default_rng(77 + seed)
+    nb, Hkv, D = 300, 4, 128
+    pool = Fp8Pool(nb, Hkv, D, 0.05, 0.02)
+    slots = mixed_slots(rng, nb, 100)
+    x = rng.standard_normal((2, len(slots), Hkv, D)).astype(np.float32)
+    pool.write(bf16_bits_from_f32(x[0]), bf16_bits_from_f32(x[1]), slots)
+    pool.assert_codes_equal("random segments")
 
 
 # ----------------------------------------------------------------------------
