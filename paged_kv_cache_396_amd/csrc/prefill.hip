@@ -209,16 +209,15 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   static_assert(S == 2 || S == 4, "stage count: even, and a power of two");
   static_assert(COLS % G == 0, "group must divide the column tile");
 
-  // One array per ring stage: the K tile, then the V tile.
-  __shared__ __attribute__((aligned(1024))) char st0[2 * C::TILE], st1[2 * C::TILE];
-  __shared__ __attribute__((aligned(1024))) char st2[S > 2 ? 2 * C::TILE : 16];
-  __shared__ __attribute__((aligned(1024))) char st3[S > 2 ? 2 * C::TILE : 16];
+  // The ring: each stage holds the K tile, then the V tile.  A stage is
+  // named by a compile-time index (inside the unrolled rounds) or by the
+  // tile number (the single iterations around them: one body for all
+  // stages, so the compiler keeps one register assignment for O instead of
+  // one per stage joined by copies of the whole accumulator).
+  __shared__ __attribute__((aligned(1024))) char ring[S][2 * C::TILE];
   auto stage = [&](auto J) -> char* {
-    constexpr int j = decltype(J)::value % S;
-    if constexpr (j == 0) return st0;
-    else if constexpr (j == 1) return st1;
-    else if constexpr (j == 2) return st2;
-    else return st3;
+    if constexpr (std::is_same_v<decltype(J), int>) return ring[J & (S - 1)];
+    else return ring[decltype(J)::value % S];
   };
   auto kstage = [&](auto J) -> char* { return stage(J); };
   auto vstage = [&](auto J) -> char* { return stage(J) + C::TILE; };
@@ -626,9 +625,11 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // iteration the waves issue them at different times: 1.5% faster.)
   // Every wave runs every iteration.
   auto iteration = [&](auto J, int t, auto mask_c, auto last_c) __attribute__((always_inline)) {
-    constexpr int j = decltype(J)::value;
     constexpr bool LAST = decltype(last_c)::value;
-    using JN = std::integral_constant<int, j + S - 1>;
+    const auto JN = [&] {
+      if constexpr (std::is_same_v<decltype(J), int>) return J + S - 1;
+      else return std::integral_constant<int, decltype(J)::value + S - 1>{};
+    }();
     stage_barrier(std::integral_constant<int, S - 2>{});  // batch t has landed
     // fresh copies of the fragment bases each iteration: the compiler would
     // otherwise keep every stage's derived addresses live across the loop
@@ -643,22 +644,17 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       pin_probs(0);
       rescale(a0);
       pv(vstage(J), vf, k0, 0, mask_c);
-      if constexpr (!LAST) copy_tile(JN{}, t + S - 1);
+      if constexpr (!LAST) copy_tile(JN, t + S - 1);
       softmax(s1, k0, 1, mask_c, a1);
       pin_probs(1);
       rescale(a1);
       pv(vstage(J), vf, k0, 1, mask_c);
     } else if constexpr (!LAST) {
-      copy_tile(JN{}, t + S - 1);
+      copy_tile(JN, t + S - 1);
     }
   };
-  auto dispatch = [&](int t, auto mask_c, auto last_c) __attribute__((always_inline)) {
-    switch (t & (S - 1)) {
-      case 0: iteration(std::integral_constant<int, 0>{}, t, mask_c, last_c); break;
-      case 1: iteration(std::integral_constant<int, 1>{}, t, mask_c, last_c); break;
-      case 2: if constexpr (S > 2) iteration(std::integral_constant<int, 2>{}, t, mask_c, last_c); break;
-      default: if constexpr (S > 3) iteration(std::integral_constant<int, 3>{}, t, mask_c, last_c); break;
-    }
+  auto single = [&](int t, auto mask_c, auto last_c) __attribute__((always_inline)) {
+    iteration(t, t, mask_c, last_c);
   };
   // Tiles that end before the workgroup's first query position need no
   // mask for any column; the rest (the causal diagonal, the context end and
@@ -671,7 +667,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   auto run = [&](int from, int to, auto mask_c) __attribute__((always_inline)) {
     using F = std::false_type;
     int t = from;
-    while (t < to && (t & (S - 1)) != 0) dispatch(t++, mask_c, F{});
+    while (t < to && (t & (S - 1)) != 0) single(t++, mask_c, F{});
     for (; t + S <= to; t += S) {
       iteration(std::integral_constant<int, 0>{}, t, mask_c, F{});
       iteration(std::integral_constant<int, 1>{}, t + 1, mask_c, F{});
@@ -680,16 +676,16 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
         iteration(std::integral_constant<int, 3>{}, t + 3, mask_c, F{});
       }
     }
-    while (t < to) dispatch(t++, mask_c, F{});
+    while (t < to) single(t++, mask_c, F{});
   };
   if (iters > 0) {
     const int split = min(n_plain, iters - 1);
     run(0, split, std::false_type{});
     run(split, iters - 1, std::true_type{});
     if (n_plain >= iters)
-      dispatch(iters - 1, std::false_type{}, std::true_type{});
+      single(iters - 1, std::false_type{}, std::true_type{});
     else
-      dispatch(iters - 1, std::true_type{}, std::true_type{});
+      single(iters - 1, std::true_type{}, std::true_type{});
   }
   // copies of tiles past the end may still be in flight: let them land
   // before the workgroup's LDS is released
