@@ -34,7 +34,10 @@
 //    they are directly the B operand of the P V product.
 //  * each 64-key tile is taken as two 32-key blocks, each a full online
 //    softmax step, so that one block's vector work can overlap the other
-//    block's matrix products.
+//    block's matrix products.  When a request's rows fill at most half of a
+//    narrow workgroup's columns (speculative verification), two waves share
+//    each column block and take one 32-key block each; their states are
+//    merged with the online-softmax rescale at the end.
 //  * O^T = V^T P accumulates in fp32 (32 dims x 32 columns per instruction);
 //    the V tiles are dim-major in the pool and in LDS, so each A fragment is
 //    one 16-byte read.
@@ -79,6 +82,7 @@ constexpr int kPfDma = 1024;             // bytes one LDS-writing load instructi
 // Narrow shape for chunks of a few query rows (speculative verification,
 // shared-prefix groups): with 4 waves and 2 stages a workgroup needs half
 // the LDS, so two share a compute unit and twice as many waves compute.
+// With at most 64 columns it runs paired (two waves per column block).
 constexpr int kPfNarrowWaves = 4;
 constexpr int kPfNarrowStages = 2;
 
@@ -200,11 +204,16 @@ __device__ inline void pf_copy_to_lds(const pf_rsrc& rs, unsigned lds, int voff)
 // query sees every key of the partition (they all sit past the prefix), and
 // the result is a partial state (running max in log2 units, sum, unscaled
 // output) for the decode merge instead of a normalised row.
-template <int D, int G, int NCB, bool PFX = false, int W = kPfWaves, int S = kPfStages, int KB = 2>
+template <int D, int G, int NCB, bool PFX = false, int W = kPfWaves, int S = kPfStages, int KB = 2,
+          bool KS = false>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kernel(PrefillParams p) {
   using C = PrefillCfg<D, W, KB>;
-  constexpr int COLS = W * 32 * NCB;  // columns per workgroup
+  // KS (paired waves): waves 2 i and 2 i + 1 share column block i and take
+  // the first and the second 32-key block of every tile, each with its own
+  // online-softmax state; the two states are merged at the end.
+  constexpr int CW = KS ? W / 2 : W;  // waves with distinct columns
+  constexpr int COLS = CW * 32 * NCB;  // columns per workgroup
   constexpr int QT = COLS / G;        // queries per workgroup
   static_assert(S == 2 || S == 4, "stage count: even, and a power of two");
   static_assert(COLS % G == 0, "group must divide the column tile");
@@ -283,6 +292,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   __builtin_assume(tid < W * kWave);
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wc = KS ? w >> 1 : w;  // column block of this wave
+  const int kbw = KS ? w & 1 : 0;  // its key block (paired waves)
   const int half = lane >> 5;
   const int cw = lane & 31;
   // block ids are read through the scalar cache (uniform addresses)
@@ -299,7 +310,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   uint4 qf[NCB][C::DS];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    const int c = 32 * (w * NCB + cb) + cw;
+    const int c = 32 * (wc * NCB + cb) + cw;
     const int qi = q0 + c / G;
     const int hh = c % G;
     const bool valid = qi < n_r;
@@ -600,7 +611,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // It is issued at iteration n - S + 1, after the barrier that ends every
   // read of that stage (tile n - S, read at iteration n - S).
   f32x16_t s0[NCB], s1[NCB];  // scores of the two key blocks
-  const bool wave_active = q0 + 32 * w * NCB / G < n_r;  // its first column is a real query
+  const bool wave_active = q0 + 32 * wc * NCB / G < n_r;  // its first column is a real query
   int id_next = -1;  // id of this wave's block of the next tile to copy
   auto copy_tile = [&](auto J, int n) __attribute__((always_inline)) {
     copy_k(kstage(J), id_next, n);
@@ -636,7 +647,26 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     int kf = kfb, vf = vfb;
     __asm__ volatile("" : "+v"(kf), "+v"(vf));
     const int k0 = kbeg + t * kPfKT;
-    if (wave_active) {  // uniform: a wave with no real column only copies
+    if constexpr (KS) {
+      // paired waves: the copies first (two stages leave one iteration for
+      // them to land), then this wave's key block of the tile
+      if constexpr (!LAST) copy_tile(JN, t + S - 1);
+      if (wave_active) {
+        auto block = [&](auto KBc) __attribute__((always_inline)) {
+          constexpr int kb = decltype(KBc)::value;
+          float a[NCB];
+          scores(kstage(J), kf, kb, s0);
+          softmax(s0, k0, kb, mask_c, a);
+          pin_probs(kb);
+          rescale(a);
+          pv(vstage(J), vf, k0, kb, mask_c);
+        };
+        if (kbw)
+          block(std::integral_constant<int, 1>{});
+        else
+          block(std::integral_constant<int, 0>{});
+      }
+    } else if (wave_active) {  // uniform: a wave with no real column only copies
       float a0[NCB], a1[NCB];
       scores(kstage(J), kf, 0, s0);
       scores(kstage(J), kf, 1, s1);
@@ -691,13 +721,54 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(pf_vmcnt(0));
 
+  if constexpr (KS) {
+    // Merge of paired waves through LDS (the ring is free once every wave
+    // has left the loop and every copy has landed): the second wave of a
+    // pair leaves m, l and O; the first rescales both to the larger max,
+    //   m = max(m0, m1),  l = l0 2^(m0 - m) + l1 2^(m1 - m),  O likewise,
+    // and goes on as if it had seen every key.
+    static_assert(sizeof(ring) >= (size_t)CW * NCB * C::DB * 16 * kWave * 4, "merge area");
+    __shared__ float xml[CW][NCB][2][kWave];
+    float* xo = (float*)&ring[0][0] + (int64_t)wc * NCB * C::DB * 16 * kWave;
+    __syncthreads();
+    if (wave_active && kbw == 1) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        xml[wc][cb][0][lane] = m_run[cb];
+        xml[wc][cb][1][lane] = l_run[cb];
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xo[((cb * C::DB + db) * 16 + i) * kWave + lane] = acco[cb][db][i];
+      }
+    }
+    __syncthreads();
+    if (kbw == 1) return;  // uniform
+    if (wave_active) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const float m1 = xml[wc][cb][0][lane];
+        const float mx = fmaxf(m_run[cb], m1);
+        const float f0 = __builtin_amdgcn_exp2f(m_run[cb] - mx);
+        const float f1 = __builtin_amdgcn_exp2f(m1 - mx);
+        m_run[cb] = mx;
+        l_run[cb] = l_run[cb] * f0 + xml[wc][cb][1][lane] * f1;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            acco[cb][db][i] = acco[cb][db][i] * f0 + xo[((cb * C::DB + db) * 16 + i) * kWave + lane] * f1;
+      }
+    }
+  }
+
   // ---- normalise and store (or, in shared-prefix mode, leave the partial
   // state): register i of dim block db is dim 32 db + 8 (i / 4) + 4 half +
   // i % 4 of this lane's column
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const float lt = l_run[cb] + xor_lane<32>(l_run[cb]);
-    const int c = 32 * (w * NCB + cb) + cw;
+    const int c = 32 * (wc * NCB + cb) + cw;
     const int qi = q0 + c / G;
     if (qi >= n_r) continue;
     if (partial) {  // uniform
@@ -810,15 +881,23 @@ constexpr int pf_queries(int W, int G) { return W * 32 * PA_PF_NCB / G; }
 // The narrow shape when every request's rows (or a group's sequences) fit
 // one narrow workgroup: its other waves would have no column to compute.
 inline bool pf_narrow(int rows, int G) { return rows <= pf_queries(kPfNarrowWaves, G); }
+// Paired waves when the rows fit half of it: two waves per column block,
+// each taking one 32-key half of every tile.
+inline bool pf_paired(int rows, int G) { return rows <= pf_queries(kPfNarrowWaves / 2, G); }
 
 template <int D, int G, int KB>
 static hipError_t launch_prefill_t(PrefillParams prm, int max_q_len, hipStream_t stream) {
   constexpr int NCB = PA_PF_NCB;
   const bool narrow = pf_narrow(max_q_len, G);
-  prm.qt = narrow ? pf_queries(kPfNarrowWaves, G) : pf_queries(kPfWaves, G);
+  const bool paired = pf_paired(max_q_len, G);
+  prm.qt = paired ? pf_queries(kPfNarrowWaves / 2, G)
+                  : narrow ? pf_queries(kPfNarrowWaves, G) : pf_queries(kPfWaves, G);
   prm.num_qtiles = (max_q_len + prm.qt - 1) / prm.qt;
   const int64_t grid = (int64_t)prm.num_qtiles * prm.num_reqs * prm.num_kv_heads * prm.max_parts;
-  if (narrow) {
+  if (paired) {
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, false, kPfNarrowWaves, kPfNarrowStages, KB, true>),
+                       dim3((unsigned)grid), dim3(kPfNarrowWaves * kWave), 0, stream, prm);
+  } else if (narrow) {
     hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, false, kPfNarrowWaves, kPfNarrowStages, KB>),
                        dim3((unsigned)grid), dim3(kPfNarrowWaves * kWave), 0, stream, prm);
   } else {
@@ -837,7 +916,10 @@ template <int D, int G, int KB>
 static hipError_t launch_prefix_t(const PrefillParams& prm, int num_groups, hipStream_t stream) {
   constexpr int NCB = PA_PF_NCB;
   const int64_t grid = (int64_t)prm.prefix_parts * num_groups * prm.num_kv_heads;
-  if (pf_narrow(prm.group_size, G)) {
+  if (pf_paired(prm.group_size, G)) {
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true, kPfNarrowWaves, kPfNarrowStages, KB, true>),
+                       dim3((unsigned)grid), dim3(kPfNarrowWaves * kWave), 0, stream, prm);
+  } else if (pf_narrow(prm.group_size, G)) {
     hipLaunchKernelGGL((prefill_chunk_kernel<D, G, NCB, true, kPfNarrowWaves, kPfNarrowStages, KB>),
                        dim3((unsigned)grid), dim3(kPfNarrowWaves * kWave), 0, stream, prm);
   } else {
@@ -852,7 +934,9 @@ int prefill_queries_per_tile(int group) { return pf_queries(kPfWaves, group); }
 bool prefill_narrow(int max_q_len, int group) { return pf_narrow(max_q_len, group); }
 
 int prefill_tile_queries(int max_q_len, int group) {
-  return pf_narrow(max_q_len, group) ? pf_queries(kPfNarrowWaves, group) : pf_queries(kPfWaves, group);
+  return pf_paired(max_q_len, group)   ? pf_queries(kPfNarrowWaves / 2, group)
+         : pf_narrow(max_q_len, group) ? pf_queries(kPfNarrowWaves, group)
+                                       : pf_queries(kPfWaves, group);
 }
 
 
