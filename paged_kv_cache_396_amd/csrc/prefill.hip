@@ -175,7 +175,6 @@ __host__ __device__ constexpr int pf_vmcnt(int n) {
 }
 
 typedef int pf_rsrc __attribute__((ext_vector_type(4)));
-typedef unsigned pf_u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline unsigned pf_lds_addr(const char* p) {
   return __builtin_amdgcn_readfirstlane(
@@ -539,19 +538,6 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       l_run[cb] = fmaf(l_run[cb], alpha[cb], lsum0 + lsum1);
     }
   };
-  // Keeps a block's probabilities computed before the rescale branch that
-  // follows them (the compiler would otherwise sink the exponentials past it,
-  // away from the matrix products they are meant to overlap).
-  auto pin_probs = [&](int kb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        pf_u32x4 u = __builtin_bit_cast(pf_u32x4, pf[cb][kb][t]);
-        __asm__ volatile("" : "+v"(u));
-        pf[cb][kb][t] = __builtin_bit_cast(bf16x8_t, u);
-      }
-  };
   // O *= alpha before a block's P V products (rare: only when the max rose)
   auto rescale = [&](const float (&alpha)[NCB]) __attribute__((always_inline)) {
     bool any = false;
@@ -657,7 +643,6 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
           float a[NCB];
           scores(kstage(J), kf, kb, s0);
           softmax(s0, k0, kb, mask_c, a);
-          pin_probs(kb);
           rescale(a);
           pv(vstage(J), vf, k0, kb, mask_c);
         };
@@ -671,12 +656,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       scores(kstage(J), kf, 0, s0);
       scores(kstage(J), kf, 1, s1);
       softmax(s0, k0, 0, mask_c, a0);
-      pin_probs(0);
       rescale(a0);
       pv(vstage(J), vf, k0, 0, mask_c);
       if constexpr (!LAST) copy_tile(JN, t + S - 1);
       softmax(s1, k0, 1, mask_c, a1);
-      pin_probs(1);
       rescale(a1);
       pv(vstage(J), vf, k0, 1, mask_c);
     } else if constexpr (!LAST) {
