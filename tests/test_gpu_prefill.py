@@ -37,6 +37,7 @@ SHAPES = [
     (64, 16, 2, (9, 0), (20, 65)),
     (64, 8, 8, (130,), (33,)),
     (64, 32, 4, (0, 1), (64, 129)),
+    (128, 32, 8, (0, 50, 2000), (16, 9, 12)),  # both column blocks of the paired shape
 ]
 
 
