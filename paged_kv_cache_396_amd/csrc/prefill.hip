@@ -496,16 +496,21 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       float v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = (MASK && !visible(i)) ? -INFINITY : sacc[cb][i];
-      // max as a tree (short dependency chain)
+      // max as a tree (short dependency chain).  The NaN-propagating
+      // maximum needs no quieting of its inputs (three-input v_maximum3);
+      // no NaN reaches it that would not reach the row anyway.
+      auto mx3 = [](float a, float b, float c) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+      };
       float t5[6];
 #pragma unroll
-      for (int i = 0; i < 5; ++i) t5[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+      for (int i = 0; i < 5; ++i) t5[i] = mx3(v[3 * i], v[3 * i + 1], v[3 * i + 2]);
       t5[5] = v[15];
-      float mraw = fmaxf(fmaxf(fmaxf(t5[0], t5[1]), t5[2]), fmaxf(fmaxf(t5[3], t5[4]), t5[5]));
+      float mraw = __builtin_elementwise_maximum(mx3(t5[0], t5[1], t5[2]), mx3(t5[3], t5[4], t5[5]));
       // the two lane halves hold the two 8-key halves of every 16 keys
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw), __float_as_uint(mraw),
                                                         false, false);
-      mraw = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mraw = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       const float mx = mraw == -INFINITY ? -INFINITY : mraw * sl;
       const bool up = mx > m_run[cb] + kPfGap;
       const float m_new = up ? mx : m_run[cb];
