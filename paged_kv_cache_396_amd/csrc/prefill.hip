@@ -417,6 +417,14 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // 32 db + cw of 16-key step st, keys 8 half ..
   const int ksw = pf_ksw<C::RB>(cw & 15);
   const int kfb = (cw >> 4) * C::BLK + (cw & 15) * C::RB + 16 * (half ^ (ksw & 1)) + 32 * (ksw >> 1);
+  // the K fragment address of every k-step, kept in registers for the
+  // whole loop (an XOR cannot go into the read's offset field)
+  int kfs[C::DS];
+#pragma unroll
+  for (int st = 0; st < C::DS; ++st) {
+    kfs[st] = kfb ^ (st * 32);
+    __asm__ volatile("" : "+v"(kfs[st]));
+  }
   // fp8 V: dim 32 db + cw, keys 8 half .. of a block are 8 bytes at
   // (32 db + cw) * 16 + 8 half
   const int vfb = KB == 2 ? cw * 32 + 16 * (half ^ ((cw >> 3) & 1)) : cw * 16 + 8 * half;
@@ -432,8 +440,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
 #define PA_PF_AHEAD 2
 #endif
   constexpr int kPfAhead = PA_PF_AHEAD;
-  auto scores = [&](const char* st, int kf, int kb, f32x16_t (&sacc)[NCB]) __attribute__((always_inline)) {
-    auto kfrag = [&](int s) { return *(const uint4*)(st + kb * 2 * C::BLK + (kf ^ (s * 32))); };
+  auto scores = [&](const char* st, int kb, f32x16_t (&sacc)[NCB]) __attribute__((always_inline)) {
+    auto kfrag = [&](int s) { return *(const uint4*)(st + kb * 2 * C::BLK + kfs[s]); };
     if constexpr (KB == 1) {
       // one 16-code chunk per lane feeds two k-steps once widened to bf16
       constexpr int NP = C::DS / 2;
@@ -517,7 +525,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       alpha[cb] = up ? __builtin_amdgcn_exp2f(m_run[cb] - m_new) : 1.f;
       m_run[cb] = m_new;
       const float nm = -m_new;
-      float lsum0 = 0.f, lsum1 = 0.f;
+      // two sum chains; the first starts from the earlier sum brought to
+      // the new max
+      float lsum0 = l_run[cb] * alpha[cb], lsum1 = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         uint32_t wds[4];
@@ -540,7 +550,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
         }
         pf[cb][kb][t] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
       }
-      l_run[cb] = fmaf(l_run[cb], alpha[cb], lsum0 + lsum1);
+      l_run[cb] = lsum0 + lsum1;
     }
   };
   // O *= alpha before a block's P V products (rare: only when the max rose)
@@ -633,10 +643,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       else return std::integral_constant<int, decltype(J)::value + S - 1>{};
     }();
     stage_barrier(std::integral_constant<int, S - 2>{});  // batch t has landed
-    // fresh copies of the fragment bases each iteration: the compiler would
+    // a fresh copy of the V fragment base each iteration: the compiler would
     // otherwise keep every stage's derived addresses live across the loop
-    int kf = kfb, vf = vfb;
-    __asm__ volatile("" : "+v"(kf), "+v"(vf));
+    int vf = vfb;
+    __asm__ volatile("" : "+v"(vf));
     const int k0 = kbeg + t * kPfKT;
     if constexpr (KS) {
       // paired waves: the copies first (two stages leave one iteration for
@@ -646,7 +656,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
         auto block = [&](auto KBc) __attribute__((always_inline)) {
           constexpr int kb = decltype(KBc)::value;
           float a[NCB];
-          scores(kstage(J), kf, kb, s0);
+          scores(kstage(J), kb, s0);
           softmax(s0, k0, kb, mask_c, a);
           rescale(a);
           pv(vstage(J), vf, k0, kb, mask_c);
@@ -658,8 +668,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       }
     } else if (wave_active) {  // uniform: a wave with no real column only copies
       float a0[NCB], a1[NCB];
-      scores(kstage(J), kf, 0, s0);
-      scores(kstage(J), kf, 1, s1);
+      scores(kstage(J), 0, s0);
+      scores(kstage(J), 1, s1);
       softmax(s0, k0, 0, mask_c, a0);
       rescale(a0);
       pv(vstage(J), vf, k0, 0, mask_c);
