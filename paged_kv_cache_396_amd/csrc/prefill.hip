@@ -301,7 +301,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
 
   // Scores are scaled by |scale|; a negative scale is applied by flipping the
   // sign of q, which is exact in bf16.
-  const float sl = fabsf(p.scale_log2);
+  // A zero scale becomes the smallest normal one: every scaled score and
+  // max then rounds away in the exponent and the softmax stays uniform,
+  // and -inf times the scale stays -inf, so the max needs no guard.
+  const float sl = fmaxf(fabsf(p.scale_log2), FLT_MIN);
   const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // ---- this lane's columns and their query positions
@@ -495,7 +498,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // to zero, which also discards any NaN from a poisoned slot past the
   // context.
   bf16x8_t pf[NCB][2][2];
-  auto softmax = [&](const f32x16_t (&sacc)[NCB], int k0, int kb, auto mask_c, float (&alpha)[NCB])
+  auto softmax = [&](const f32x16_t (&sacc)[NCB], int k0, int kb, auto mask_c, float (&alpha)[NCB],
+                     bool (&raised)[NCB])
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
@@ -519,8 +523,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw), __float_as_uint(mraw),
                                                         false, false);
       mraw = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const float mx = mraw == -INFINITY ? -INFINITY : mraw * sl;
+      const float mx = mraw * sl;
       const bool up = mx > m_run[cb] + kPfGap;
+      raised[cb] = up;
       const float m_new = up ? mx : m_run[cb];
       alpha[cb] = up ? __builtin_amdgcn_exp2f(m_run[cb] - m_new) : 1.f;
       m_run[cb] = m_new;
@@ -554,10 +559,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     }
   };
   // O *= alpha before a block's P V products (rare: only when the max rose)
-  auto rescale = [&](const float (&alpha)[NCB]) __attribute__((always_inline)) {
+  auto rescale = [&](const float (&alpha)[NCB], const bool (&raised)[NCB]) __attribute__((always_inline)) {
     bool any = false;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) any = any || alpha[cb] != 1.f;
+    for (int cb = 0; cb < NCB; ++cb) any = any || raised[cb];
     if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
@@ -612,7 +617,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // It is issued at iteration n - S + 1, after the barrier that ends every
   // read of that stage (tile n - S, read at iteration n - S).
   f32x16_t s0[NCB], s1[NCB];  // scores of the two key blocks
-  const bool wave_active = q0 + 32 * wc * NCB / G < n_r;  // its first column is a real query
+  // its first column is a real query (uniform: kept in a scalar register)
+  const bool wave_active = __builtin_amdgcn_readfirstlane(q0 + 32 * wc * NCB / G < n_r ? 1 : 0) != 0;
   int id_next = -1;  // id of this wave's block of the next tile to copy
   auto copy_tile = [&](auto J, int n) __attribute__((always_inline)) {
     copy_k(kstage(J), id_next, n);
@@ -656,9 +662,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
         auto block = [&](auto KBc) __attribute__((always_inline)) {
           constexpr int kb = decltype(KBc)::value;
           float a[NCB];
+          bool up[NCB];
           scores(kstage(J), kb, s0);
-          softmax(s0, k0, kb, mask_c, a);
-          rescale(a);
+          softmax(s0, k0, kb, mask_c, a, up);
+          rescale(a, up);
           pv(vstage(J), vf, k0, kb, mask_c);
         };
         if (kbw)
@@ -668,14 +675,15 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       }
     } else if (wave_active) {  // uniform: a wave with no real column only copies
       float a0[NCB], a1[NCB];
+      bool u0[NCB], u1[NCB];
       scores(kstage(J), 0, s0);
       scores(kstage(J), 1, s1);
-      softmax(s0, k0, 0, mask_c, a0);
-      rescale(a0);
+      softmax(s0, k0, 0, mask_c, a0, u0);
+      rescale(a0, u0);
       pv(vstage(J), vf, k0, 0, mask_c);
       if constexpr (!LAST) copy_tile(JN, t + S - 1);
-      softmax(s1, k0, 1, mask_c, a1);
-      rescale(a1);
+      softmax(s1, k0, 1, mask_c, a1, u1);
+      rescale(a1, u1);
       pv(vstage(J), vf, k0, 1, mask_c);
     } else if constexpr (!LAST) {
       copy_tile(JN, t + S - 1);

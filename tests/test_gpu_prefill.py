@@ -201,6 +201,22 @@ def test_prefill_split_matches_oracle(D, Hq, Hkv, prior, chunk, part):
     assert_close(whole, ref, "bf16", "unsplit prefill")
 
 
+@pytest.mark.parametrize("prior,chunk", [((0, 90), (130, 64)), ((5, 40), (20, 33)), ((0, 300), (5, 3))])
+@pytest.mark.parametrize("factor", [0.0, -1.0, 8.0])
+def test_prefill_scale_edge_cases(prior, chunk, factor):
+    """Zero, negative and large softmax scales on the wide, narrow and
+    paired shapes: a zero scale is uniform attention over the visible keys,
+    a negative one flips the sign of every score."""
+    import dataclasses
+
+    wl = make_tiny_prefill(seed=77, prior=prior, chunk=chunk, Hq=32, Hkv=8, D=128)
+    wl = dataclasses.replace(wl, scale=float(wl.scale) * factor)
+    log(f"prefill scale x{factor} prior={prior} chunk={chunk}")
+    got = to_f64(gpu_prefill(wl, gpu_pool_for(wl)))
+    err = assert_close(got, _oracle_prefill(wl), "bf16", f"scale x{factor}")
+    log(f"  max abs err {err:.3g}")
+
+
 def test_prefill_split_last_row_still_matches_decode():
     wl = make_tiny_prefill(seed=9, prior=(3000, 1200), chunk=(5, 5), Hq=32, Hkv=8, D=128)
     pool = gpu_pool_for(wl)
