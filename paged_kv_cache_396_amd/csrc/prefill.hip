@@ -208,6 +208,13 @@ template <int D, int G, int NCB, bool PFX = false, int W = kPfWaves, int S = kPf
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kernel(PrefillParams p) {
   using C = PrefillCfg<D, W, KB>;
+  // CVT (fp8 pools, wide shape): each tile is widened to bf16 once, by all
+  // waves together, into an LDS buffer laid out as a bf16 tile; the
+  // fragment reads then follow the bf16 path.  CR and KBR describe what the
+  // fragment reads see.
+  constexpr bool CVT = KB == 1 && W == 8 && !KS;
+  constexpr int KBR = CVT ? 2 : KB;
+  using CR = PrefillCfg<D, W, KBR>;
   // KS (paired waves): waves 2 i and 2 i + 1 share column block i and take
   // the first and the second 32-key block of every tile, each with its own
   // online-softmax state; the two states are merged at the end.
@@ -229,6 +236,16 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   };
   auto kstage = [&](auto J) -> char* { return stage(J); };
   auto vstage = [&](auto J) -> char* { return stage(J) + C::TILE; };
+  // widened tiles (CVT): tile t in buffer t % 2, K then V
+  __shared__ __attribute__((aligned(1024))) char cvb[CVT ? 2 : 1][CVT ? 2 * CR::TILE : 16];
+  auto rkstage = [&](auto J, int t) -> const char* {
+    if constexpr (CVT) return cvb[t & 1];
+    else return kstage(J);
+  };
+  auto rvstage = [&](auto J, int t) -> const char* {
+    if constexpr (CVT) return cvb[t & 1] + CR::TILE;
+    else return vstage(J);
+  };
 
   // ---- which queries and which keys.  Chunk mode: (request, kv head, query
   // tile); tiles of one (request, kv head) are consecutive in the "logical"
@@ -323,7 +340,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       // k-step s, lane half h: dims 16 s + 8 h .. (bf16 pools); with fp8
       // pools the dims follow the 16-code chunks a lane reads, 32 (s / 2) +
       // 16 h + 8 (s % 2) .. (the same order on both sides of the product)
-      const int qoff = KB == 2 ? (2 * s + half) * 16 : 64 * (s >> 1) + 32 * half + 16 * (s & 1);
+      const int qoff = KBR == 2 ? (2 * s + half) * 16 : 64 * (s >> 1) + 32 * half + 16 * (s & 1);
       uint4 v = valid ? *(const uint4*)(qrow + qoff) : make_uint4(0, 0, 0, 0);
       v.x ^= qsign; v.y ^= qsign; v.z ^= qsign; v.w ^= qsign;
       qf[cb][s] = v;
@@ -409,7 +426,10 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   auto stage_barrier = [&](auto n_c) __attribute__((always_inline)) {
     constexpr int n = decltype(n_c)::value;
     __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(pf_vmcnt(n * kLoadsPerBatch));
+    if constexpr (CVT)
+      __builtin_amdgcn_s_waitcnt(pf_vmcnt(n * kLoadsPerBatch) & ~(15 << 8));  // and LDS writes done
+    else
+      __builtin_amdgcn_s_waitcnt(pf_vmcnt(n * kLoadsPerBatch));
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
   };
@@ -418,8 +438,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // LDS block 2 kb + cw / 16; its chunk 2 s + half sits at slot
   // (2 s + half) ^ sw, so the address of step s is kfb ^ (32 s).  V: dim
   // 32 db + cw of 16-key step st, keys 8 half ..
-  const int ksw = pf_ksw<C::RB>(cw & 15);
-  const int kfb = (cw >> 4) * C::BLK + (cw & 15) * C::RB + 16 * (half ^ (ksw & 1)) + 32 * (ksw >> 1);
+  const int ksw = pf_ksw<CR::RB>(cw & 15);
+  const int kfb = (cw >> 4) * CR::BLK + (cw & 15) * CR::RB + 16 * (half ^ (ksw & 1)) + 32 * (ksw >> 1);
   // the K fragment address of every k-step, kept in registers for the
   // whole loop (an XOR cannot go into the read's offset field)
   int kfs[C::DS];
@@ -430,7 +450,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   }
   // fp8 V: dim 32 db + cw, keys 8 half .. of a block are 8 bytes at
   // (32 db + cw) * 16 + 8 half
-  const int vfb = KB == 2 ? cw * 32 + 16 * (half ^ ((cw >> 3) & 1)) : cw * 16 + 8 * half;
+  const int vfb = KBR == 2 ? cw * 32 + 16 * (half ^ ((cw >> 3) & 1)) : cw * 16 + 8 * half;
 
   // The tile is processed as two 32-key blocks, each a full online-softmax
   // step, so that the vector work of one block overlaps the matrix products
@@ -444,8 +464,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
 #endif
   constexpr int kPfAhead = PA_PF_AHEAD;
   auto scores = [&](const char* st, int kb, f32x16_t (&sacc)[NCB]) __attribute__((always_inline)) {
-    auto kfrag = [&](int s) { return *(const uint4*)(st + kb * 2 * C::BLK + kfs[s]); };
-    if constexpr (KB == 1) {
+    auto kfrag = [&](int s) { return *(const uint4*)(st + kb * 2 * CR::BLK + kfs[s]); };
+    if constexpr (KBR == 1) {
       // one 16-code chunk per lane feeds two k-steps once widened to bf16
       constexpr int NP = C::DS / 2;
       uint4 ka[2];
@@ -582,8 +602,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     constexpr int NJ = 2 * C::DB;  // product j: 16-key step 2 kb + j / DB, dim block j % DB
     auto vfrag = [&](int j) {
       const int step = 2 * kb + j / C::DB, db = j % C::DB;
-      if constexpr (KB == 2) return *(const uint4*)(st + step * C::BLK + db * 32 * 32 + vf);
-      const uint2 raw = *(const uint2*)(st + step * C::BLK + db * 32 * 16 + vf);
+      if constexpr (KBR == 2) return *(const uint4*)(st + step * CR::BLK + db * 32 * 32 + vf);
+      const uint2 raw = *(const uint2*)(st + step * CR::BLK + db * 32 * 16 + vf);
       return make_uint4(fp8x2_to_bf16x2<false>(raw.x), fp8x2_to_bf16x2<true>(raw.x),
                         fp8x2_to_bf16x2<false>(raw.y), fp8x2_to_bf16x2<true>(raw.y));
     };
@@ -613,6 +633,40 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     }
   };
 
+  // CVT: widen the codes of the fp8 tile in stage st8 into the bf16 buffer
+  // dst.  Lane (w, l) takes K chunk 64 w + l (16 codes of one key row) and
+  // V row 64 w + l (16 keys of one dim), and writes them where the bf16
+  // tile's copies would have put them (same row order and swizzles).
+  auto convert = [&](const char* st8, char* dst) __attribute__((always_inline)) {
+    static_assert(!CVT || (D == 128 && W * kWave == 512), "one K chunk and one V row per lane");
+    const int id = w * kWave + lane;
+    const int b = id >> 7;  // block of the tile
+    {
+      const int m = (id >> 3) & 15, c = id & 7;  // K row, 16-code chunk
+      const uint4 raw = *(const uint4*)(st8 + b * C::BLK + m * C::RB + 16 * (c ^ pf_ksw<C::RB>(m)));
+      const uint4 w0 = make_uint4(fp8x2_to_bf16x2<false>(raw.x), fp8x2_to_bf16x2<true>(raw.x),
+                                  fp8x2_to_bf16x2<false>(raw.y), fp8x2_to_bf16x2<true>(raw.y));
+      const uint4 w1 = make_uint4(fp8x2_to_bf16x2<false>(raw.z), fp8x2_to_bf16x2<true>(raw.z),
+                                  fp8x2_to_bf16x2<false>(raw.w), fp8x2_to_bf16x2<true>(raw.w));
+      const int sw = pf_ksw<CR::RB>(m);
+      char* row = dst + b * CR::BLK + m * CR::RB;
+      *(uint4*)(row + 16 * ((2 * c) ^ sw)) = w0;
+      *(uint4*)(row + 16 * ((2 * c + 1) ^ sw)) = w1;
+    }
+    {
+      const int x = id & 127;  // dim
+      const uint4 raw = *(const uint4*)(st8 + C::TILE + b * C::BLK + x * 16);
+      const uint4 w0 = make_uint4(fp8x2_to_bf16x2<false>(raw.x), fp8x2_to_bf16x2<true>(raw.x),
+                                  fp8x2_to_bf16x2<false>(raw.y), fp8x2_to_bf16x2<true>(raw.y));
+      const uint4 w1 = make_uint4(fp8x2_to_bf16x2<false>(raw.z), fp8x2_to_bf16x2<true>(raw.z),
+                                  fp8x2_to_bf16x2<false>(raw.w), fp8x2_to_bf16x2<true>(raw.w));
+      const int xs = (x >> 3) & 1;
+      char* row = dst + CR::TILE + b * CR::BLK + x * 32;
+      *(uint4*)(row + 16 * xs) = w0;
+      *(uint4*)(row + 16 * (1 ^ xs)) = w1;
+    }
+  };
+
   // ---- the ring.  Batch n is K and V of tile n, copied into stage n % S.
   // It is issued at iteration n - S + 1, after the barrier that ends every
   // read of that stage (tile n - S, read at iteration n - S).
@@ -633,6 +687,13 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       copy_tile(std::integral_constant<int, 1>{}, 1);
       copy_tile(std::integral_constant<int, 2>{}, 2);
     }
+    if constexpr (CVT) {
+      // tile 0 widened before the loop; the loop widens tile t + 1 at t
+      __builtin_amdgcn_s_waitcnt(pf_vmcnt((S - 2) * kLoadsPerBatch));
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      convert(kstage(std::integral_constant<int, 0>{}), cvb[0]);
+    }
   }
 
   // One iteration: wait for tile t in LDS, then S^T = K Q^T, online
@@ -648,7 +709,15 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
       if constexpr (std::is_same_v<decltype(J), int>) return J + S - 1;
       else return std::integral_constant<int, decltype(J)::value + S - 1>{};
     }();
-    stage_barrier(std::integral_constant<int, S - 2>{});  // batch t has landed
+    // batch t has landed (CVT: batch t + 1, and the widening of tile t)
+    stage_barrier(std::integral_constant<int, CVT ? S - 3 : S - 2>{});
+    if constexpr (CVT && !LAST) {
+      const auto J1 = [&] {
+        if constexpr (std::is_same_v<decltype(J), int>) return J + 1;
+        else return std::integral_constant<int, decltype(J)::value + 1>{};
+      }();
+      convert(kstage(J1), cvb[(t + 1) & 1]);
+    }
     // a fresh copy of the V fragment base each iteration: the compiler would
     // otherwise keep every stage's derived addresses live across the loop
     int vf = vfb;
@@ -676,15 +745,15 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     } else if (wave_active) {  // uniform: a wave with no real column only copies
       float a0[NCB], a1[NCB];
       bool u0[NCB], u1[NCB];
-      scores(kstage(J), 0, s0);
-      scores(kstage(J), 1, s1);
+      scores(rkstage(J, t), 0, s0);
+      scores(rkstage(J, t), 1, s1);
       softmax(s0, k0, 0, mask_c, a0, u0);
       rescale(a0, u0);
-      pv(vstage(J), vf, k0, 0, mask_c);
+      pv(rvstage(J, t), vf, k0, 0, mask_c);
       if constexpr (!LAST) copy_tile(JN, t + S - 1);
       softmax(s1, k0, 1, mask_c, a1, u1);
       rescale(a1, u1);
-      pv(vstage(J), vf, k0, 1, mask_c);
+      pv(rvstage(J, t), vf, k0, 1, mask_c);
     } else if constexpr (!LAST) {
       copy_tile(JN, t + S - 1);
     }
