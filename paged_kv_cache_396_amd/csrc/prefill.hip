@@ -458,9 +458,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
   // evaluated, and block 0's P V products run while block 1's are.
 
   // S^T = K Q^T for key block kb (a chain of DS products); each K fragment
-  // is read two products ahead of its use.
+  // is read three products ahead of its use.
 #ifndef PA_PF_AHEAD
-#define PA_PF_AHEAD 2
+#define PA_PF_AHEAD 3
 #endif
   constexpr int kPfAhead = PA_PF_AHEAD;
   auto scores = [&](const char* st, int kb, f32x16_t (&sacc)[NCB]) __attribute__((always_inline)) {
@@ -593,7 +593,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PF_WAVES_PER_EU))) void prefill_chunk_kern
     }
   };
   // O^T += V^T P for key block kb: the DB output chains alternate; each V
-  // fragment is read two products ahead of its use.  In the tile holding the
+  // fragment is read three products ahead of its use.  In the tile holding the
   // context end the V values of keys past it (whatever the pool holds there,
   // possibly NaN) are cleared in the fragment: a zero probability must meet
   // a finite value.
