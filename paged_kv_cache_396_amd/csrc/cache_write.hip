@@ -74,7 +74,7 @@ __device__ inline void cw_find_segments(CwSegments& sg, const int64_t* slots, in
   __syncthreads();
 }
 
-// Rows are read in two rounds.  The group's own 16 tokens are read at once,
+// Rows are read in two passes.  The group's own 16 tokens are read at once,
 // together with the slots, so a scattered step's tokens wait on one memory
 // round trip; the window's next 16 tokens are read after the segments are
 // known, and only when a run continues into them.  A token that is a
@@ -125,9 +125,9 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
   const int64_t i0 = (int64_t)blockIdx.x * kBlock;
   const int RC = head_dim * EB / 16;  // 16-byte chunks per row
   const int stage_rb = head_dim * EB + 16;
-  const int own = kBlock * RC;        // chunks of one round (16 tokens): <= 2 per thread
+  const int own = kBlock * RC;        // chunks of one read pass (16 tokens): <= 2 per thread
 
-  // round 1: chunks tid and tid + 256 of the group's own rows
+  // first read pass: chunks tid and tid + 256 of the group's own rows
   const int c0 = tid, c1 = tid + kCwThreads;
   const int t0r = c0 / RC, t1r = c1 / RC;
   const bool h0 = c0 < own && i0 + t0r < num_tokens;
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
   if (h1 && sg.owner[t1r] >= 0)
     cw_place<EB>(sg, t1r, c1 - t1r * RC, k1, v1, g, num_kv_heads, head_dim, k_cache, v_cache, vstage, stage_rb);
   if (!sg.multi) return;  // uniform: every segment was one token
-  // round 2: tokens i0 + 16 .. that continue a run
+  // second read pass: tokens i0 + 16 .. that continue a run
   if (sg.tail) {  // uniform
     for (int c = tid; c < own; c += kCwThreads) {
       const int t = kBlock + c / RC, x = c % RC;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
 // division), ties to the even code, magnitudes beyond 448 saturating; a NaN
 // becomes 0x7F with x's sign bit (quantize4).
 
-// The same segments and read rounds as the bf16 / fp32 kernel.  Input chunk
+// The same segments and read passes as the bf16 / fp32 kernel.  Input chunk
 // c (8 bf16 of one token) becomes 8 codes.
 __global__ __launch_bounds__(kCwThreads) void cache_write_fp8_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slots,
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_fp8_kernel(
   const int g = blockIdx.y;
   const int64_t i0 = (int64_t)blockIdx.x * kBlock;
   const int RC = head_dim / 8;  // 16-byte input chunks per row
-  const int own = kBlock * RC;  // <= 256: one chunk per thread per round
+  const int own = kBlock * RC;  // <= 256: one chunk per thread per read pass
 
   // chunk x of token t's rows, t owned: K codes to the slot; V codes into
   // LDS, or (a one-token segment) byte by byte into its 8 dim rows
